@@ -1,0 +1,92 @@
+"""Seeded synthetic inputs for the MoE layer and the DenseFA baseline.
+
+Both the HIP path and the CPU oracle are fed from here; this module holds none
+of the method's arithmetic, only the input distributions:
+
+* x ~ N(0, 1), router logits ~ N(0, 1) (fp32);
+* "zipf" routing adds a log-Zipf expert prior: l[t, e] = n[t, e] - s * ln(e + 1),
+  so expert 0 is the hottest (the normaliser of the Zipf law is dropped: a
+  constant shift of all logits of a token does not change softmax);
+* every weight W ~ N(0, std = 1/sqrt(fan_in)), fan_in = H for the gate/up
+  matrices and the intermediate width for the down matrix;
+* values are rounded once to the storage dtype (bf16 round-to-nearest-even).
+
+Each tensor draws from its own generator seeded from (seed, tensor name), so
+adding a tensor never shifts another.  Generation happens on `device`; tests
+that need the same values on the host copy the device tensors back.
+"""
+import math
+import zlib
+
+import torch
+
+_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _gen(seed: int, name: str, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1000003 + zlib.crc32(name.encode())) & 0x7FFFFFFFFFFFFFFF)
+    return g
+
+
+def _normal(shape, std, dtype, seed, name, device, chunk_dim0=None):
+    """N(0, std^2) rounded to dtype; generated in slices of dim 0 to bound the fp32 temporary."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    g = _gen(seed, name, device)
+    n0 = shape[0]
+    step = chunk_dim0 or n0
+    for a in range(0, n0, step):
+        b = min(n0, a + step)
+        t = torch.randn((b - a,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        out[a:b].copy_(t)
+        del t
+    return out
+
+
+def router_logits(T, E, routing="uniform", zipf_s=1.2, seed=0, device="cpu", name="logits"):
+    l = _normal((T, E), 1.0, torch.float32, seed, name, device)
+    if routing == "zipf":
+        prior = torch.log(torch.arange(1, E + 1, dtype=torch.float64, device=device)) * zipf_s
+        l = (l.double() - prior[None, :]).float()
+    elif routing != "uniform":
+        raise ValueError(f"unknown routing {routing!r}")
+    return l.contiguous()
+
+
+def tokens(T, H, dtype="bf16", seed=0, device="cpu", name="x"):
+    return _normal((T, H), 1.0, _DT[dtype], seed, name, device)
+
+
+def swiglu_weights(n_out_inter, H, dtype="bf16", seed=0, device="cpu", prefix="w", experts=None):
+    """Gate/up matrix [.., 2*I, H] (rows 0..I-1 gate, I..2I-1 up) and down matrix [.., H, I]."""
+    I = n_out_inter
+    dt = _DT[dtype]
+    if experts is None:
+        w13 = _normal((2 * I, H), 1.0 / math.sqrt(H), dt, seed, prefix + "13", device, chunk_dim0=4096)
+        w2 = _normal((H, I), 1.0 / math.sqrt(I), dt, seed, prefix + "2", device, chunk_dim0=4096)
+    else:
+        w13 = _normal((experts, 2 * I, H), 1.0 / math.sqrt(H), dt, seed, prefix + "13", device, chunk_dim0=1)
+        w2 = _normal((experts, H, I), 1.0 / math.sqrt(I), dt, seed, prefix + "2", device, chunk_dim0=1)
+    return w13, w2
+
+
+def layer_inputs(shape, T, routing=None, seed=0, device="cpu", dense=True, moe=True):
+    """All inputs of one MoE layer pass (and its DenseFA baseline) for a LayerShape."""
+    routing = routing or shape.routing[0]
+    d = {"T": T, "routing": routing}
+    d["x"] = tokens(T, shape.hidden, shape.dtype, seed, device)
+    d["logits"] = router_logits(T, shape.experts, routing, shape.zipf_s, seed, device)
+    if moe:
+        d["w13"], d["w2"] = swiglu_weights(shape.inter, shape.hidden, shape.dtype, seed, device,
+                                           "expert_w", experts=shape.experts)
+        if shape.shared_inter:
+            d["ws13"], d["ws2"] = swiglu_weights(shape.shared_inter, shape.hidden, shape.dtype, seed,
+                                                 device, "shared_w")
+        else:
+            d["ws13"] = d["ws2"] = None
+    if dense:
+        d["wfa13"], d["wfa2"] = swiglu_weights(shape.dense_fa_inter, shape.hidden, shape.dtype, seed,
+                                               device, "densefa_w")
+    return d

@@ -1,0 +1,171 @@
+"""CPU oracle of one MoE feed-forward layer pass -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The library's compute path never calls it; it shares no
+code with the HIP kernels (the C source is compiled with gcc on its own).
+
+Thin ctypes marshalling around ``moe_oracle.c``; every step of the arithmetic
+is in that file.  Inputs are torch CPU tensors or numpy arrays, fp32 or bf16;
+results are float64 numpy arrays (routing ids and alignment arrays int32).
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "moe_oracle.c")
+LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
+
+F32, BF16 = 0, 1
+_lib = None
+
+
+def build(force=True):
+    """Compile the oracle with gcc (plain -O2, no fast-math, OpenMP)."""
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                           "-Wextra", "-Wno-unused-parameter", SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        vp, i64, i32, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.orc_route.argtypes = [vp, i64, i32, i32, vp, vp]
+        L.orc_route.restype = i32
+        L.orc_align.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
+        L.orc_align.restype = i32
+        L.orc_swiglu.argtypes = [vp, i32, i64, i32, i32, vp, vp, i32, dp]
+        L.orc_swiglu.restype = None
+        L.orc_combine.argtypes = [dp, dp, dp, i64, i32, i32, dp]
+        L.orc_combine.restype = None
+        L.orc_moe_layer.argtypes = [vp, i32, vp, i64, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp,
+                                    vp, dp, dp]
+        L.orc_moe_layer.restype = i32
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_max_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _arr(t):
+    """(contiguous numpy array, dtype code) for fp32/bf16 torch tensors or numpy arrays."""
+    if t is None:
+        return None, F32
+    if isinstance(t, np.ndarray):
+        a = np.ascontiguousarray(t)
+        if a.dtype == np.float32:
+            return a, F32
+        if a.dtype == np.uint16:
+            return a, BF16
+        raise TypeError(f"unsupported numpy dtype {a.dtype}")
+    import torch
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy(), F32
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16), BF16
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n):
+    lib().orc_set_threads(int(n))
+
+
+def max_threads():
+    return lib().orc_max_threads()
+
+
+def route(logits, K):
+    """Softmax top-K routing; returns (ids int32 [T,K], w float64 [T,K])."""
+    l, dt = _arr(logits)
+    assert dt == F32, "router logits are fp32"
+    T, E = l.shape
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float64)
+    rc = lib().orc_route(_p(l), T, E, K, _p(ids), _p(w))
+    if rc:
+        raise ValueError(f"orc_route: bad arguments (E={E}, K={K})")
+    return ids, w
+
+
+def align(ids, E, B, cap):
+    """Block-padded alignment of the T*K pairs; returns a dict of int32 arrays."""
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    T, K = ids.shape
+    out = dict(expert_counts=np.empty(E, np.int32), expert_offsets=np.empty(E + 1, np.int32),
+               sorted_ids=np.empty(cap, np.int32), block_expert=np.empty(cap // B, np.int32),
+               inv_pos=np.empty(T * K, np.int32))
+    rc = lib().orc_align(_p(ids), T, K, E, B, cap, _p(out["expert_counts"]),
+                         _p(out["expert_offsets"]), _p(out["sorted_ids"]),
+                         _p(out["block_expert"]), _p(out["inv_pos"]))
+    if rc == -2:
+        raise ValueError("orc_align: padded total exceeds capacity")
+    if rc:
+        raise ValueError("orc_align: bad arguments")
+    return out
+
+
+def swiglu(x, w13, w2):
+    """y = W2 (silu(W1 x) * (W3 x)) per row; w13 [2I,H], w2 [H,I]."""
+    xa, xdt = _arr(x)
+    a13, wdt = _arr(w13)
+    a2, wdt2 = _arr(w2)
+    assert wdt == wdt2
+    n, H = xa.shape
+    I = a13.shape[0] // 2
+    assert a13.shape == (2 * I, H) and a2.shape == (H, I)
+    y = np.empty((n, H), np.float64)
+    lib().orc_swiglu(_p(xa), xdt, n, H, I, _p(a13), _p(a2), wdt, _p(y))
+    return y
+
+
+dense_ffn = swiglu
+
+
+def combine(y, w, s=None):
+    """out[t] = sum_k w[t,k] y[t*K+k] (+ s[t])."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    T, K = w.shape
+    y = np.ascontiguousarray(y, dtype=np.float64).reshape(T * K, -1)
+    H = y.shape[1]
+    s = None if s is None else np.ascontiguousarray(s, dtype=np.float64)
+    out = np.empty((T, H), np.float64)
+    lib().orc_combine(_p(y), _p(w), _p(s), T, K, H, _p(out))
+    return out
+
+
+def moe_layer(x, logits, w13, w2, K, ws13=None, ws2=None):
+    """Whole layer; returns (out float64 [T,H], ids int32 [T,K], w float64 [T,K])."""
+    xa, xdt = _arr(x)
+    la, _ = _arr(logits)
+    a13, wdt = _arr(w13)
+    a2, _ = _arr(w2)
+    T, H = xa.shape
+    E = a13.shape[0]
+    I = a13.shape[1] // 2
+    assert a13.shape == (E, 2 * I, H) and a2.shape == (E, H, I) and la.shape == (T, E)
+    s13, _ = _arr(ws13)
+    s2, _ = _arr(ws2)
+    Is = 0 if s13 is None else s13.shape[0] // 2
+    out = np.empty((T, H), np.float64)
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float64)
+    rc = lib().orc_moe_layer(_p(xa), xdt, _p(la), T, H, I, E, K, _p(a13), _p(a2), wdt, Is,
+                             _p(s13), _p(s2), _p(ids), _p(w), _p(out))
+    if rc:
+        raise ValueError("orc_moe_layer: bad arguments")
+    return out, ids, w

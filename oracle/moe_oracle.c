@@ -1,0 +1,301 @@
+/*
+ * moe_oracle.c -- CPU oracle of one MoE feed-forward layer pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the CPU
+ * baseline leg of the benchmark call it; the library's compute path never
+ * does, and this file shares no code, header or table with the HIP kernels.
+ *
+ * Plain loops, one token and one expert at a time, float64 accumulation.
+ * Inputs are fp32 or bf16 bit patterns; bf16 is decoded exactly (its 16 bits
+ * are the top half of an fp32).  Where the pages leave a step open the reading
+ * taken is stated at the function.
+ *
+ * What it computes, and where the pages define it:
+ *  - routing and top-K selection: named as auxiliary kernels in the talk notes
+ *    on "Demystifying the Mixture of Experts Serving Tax" (Table 1, auxiliary
+ *    kernels row; finding 5, Fig. 5).  The gating function is not given there;
+ *    the reading is softmax over all E logits, the K largest, renormalised to
+ *    sum to one.
+ *  - alignment with block-wise padding: same notes, "Padding model (Section
+ *    5.1)": each expert's token count N_i is rounded up to a multiple of the
+ *    block B, P = sum_i ceil(N_i / B) * B.
+ *  - expert FFN: the notes give only the "MoE intermediate size" (Table 2);
+ *    the reading is a bias-free SwiGLU, y = W2 (silu(W1 x) * (W3 x)).
+ *  - combine ("local sum", finding 5): out_t = sum_k w[t,k] y[t,k] (+ shared).
+ *  - DenseFA (section "定義"): the same SwiGLU with the intermediate size
+ *    scaled by top-K (plus the shared width), applied to every token.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* Element i of an fp32 or bf16 array, as a double (exact in both cases). */
+static double elem(const void *p, int dt, int64_t i)
+{
+    if (dt == ORC_F32)
+        return (double)((const float *)p)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Row `row` (length n) of a row-major matrix, decoded to doubles. */
+static void decode_row(const void *m, int dt, int64_t row, int64_t n, double *dst)
+{
+    for (int64_t c = 0; c < n; ++c)
+        dst[c] = elem(m, dt, row * n + c);
+}
+
+/* out[j] = sum_c M[row0 + j][c] * v[c] over c ascending, for j < nrows. */
+static void matvec(const void *m, int dt, int64_t row0, int64_t nrows, int64_t ncols,
+                   const double *v, double *rowbuf, double *out)
+{
+    for (int64_t j = 0; j < nrows; ++j) {
+        decode_row(m, dt, row0 + j, ncols, rowbuf);
+        double s = 0.0;
+        for (int64_t c = 0; c < ncols; ++c)
+            s += rowbuf[c] * v[c];
+        out[j] = s;
+    }
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * One SwiGLU expert applied to one token vector xv[H]:
+ *   g_i = sum_h W1[i][h] x[h],  u_i = sum_h W3[i][h] x[h]   (W1 = rows 0..I-1
+ *   of w13, W3 = rows I..2I-1), a_i = silu(g_i) * u_i,
+ *   y_h = sum_i W2[h][i] a_i   (w2 is [H][I], out x in, row-major).
+ * w13/w2 point at this expert's matrices.  scratch holds 3*I + max(H,I) doubles.
+ */
+static void swiglu_token(const double *xv, int H, int I, const void *w13, const void *w2, int wdt,
+                         double *scratch, double *y)
+{
+    double *g = scratch, *u = scratch + I, *a = scratch + 2 * (int64_t)I;
+    double *rowbuf = scratch + 3 * (int64_t)I;
+    matvec(w13, wdt, 0, I, H, xv, rowbuf, g);
+    matvec(w13, wdt, I, I, H, xv, rowbuf, u);
+    for (int i = 0; i < I; ++i)
+        a[i] = silu(g[i]) * u[i];
+    matvec(w2, wdt, 0, H, I, a, rowbuf, y);
+}
+
+static size_t swiglu_scratch(int H, int I) { return 3 * (size_t)I + (size_t)(H > I ? H : I); }
+
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Routing of T tokens over E experts, K per token.
+ *   p_e = exp(l_e - max l) / sum_e exp(l_e - max l)        (softmax, e ascending)
+ *   the K selected experts are the K largest by the key (l_e descending, e
+ *   ascending); slot j holds the j-th of them in that order;
+ *   w_j = p_{e_j} / sum_{i<K} p_{e_i}                       (renormalised)
+ * The selection compares the fp32 logits themselves: softmax is increasing,
+ * so the K largest logits are the K largest probabilities, and ties between
+ * equal logits go to the lower expert id (IEEE comparison, -0 == +0).
+ * Returns 0, or -1 if K is outside [1, E].
+ */
+int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double *w)
+{
+    if (E < 1 || K < 1 || K > E || T < 0)
+        return -1;
+    double *p = malloc(sizeof(double) * (size_t)E);
+    unsigned char *taken = malloc((size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m)
+                m = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - m);
+            z += p[e];
+        }
+        for (int e = 0; e < E; ++e)
+            p[e] /= z;
+
+        memset(taken, 0, (size_t)E);
+        double s = 0.0;
+        for (int j = 0; j < K; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)           /* strict '>' keeps the lowest id among equals */
+                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                    best = e;
+            taken[best] = 1;
+            ids[t * K + j] = best;
+            s += p[best];
+        }
+        for (int j = 0; j < K; ++j)
+            w[t * K + j] = p[ids[t * K + j]] / s;
+    }
+    free(p);
+    free(taken);
+    return 0;
+}
+
+/*
+ * Alignment of the T*K (token, slot) pairs p = t*K + k into expert buckets
+ * with block-wise padding to a multiple of B:
+ *   N_e = #{p : ids[p] = e},  P_e = ceil(N_e / B) * B,
+ *   offsets[0] = 0, offsets[e+1] = offsets[e] + P_e, num_padded = offsets[E];
+ *   bucket e holds its pairs in ascending p at rows offsets[e] ..
+ *   offsets[e] + N_e - 1; every other row below cap holds the sentinel T*K;
+ *   block_expert[b] = e for the blocks of bucket e and -1 past num_padded;
+ *   inv_pos[p] = the row that holds p.
+ * cap must be a multiple of B.  Returns 0, -1 on bad arguments, -2 if the
+ * padded total exceeds cap.
+ */
+int orc_align(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, int32_t *counts,
+              int32_t *offsets, int32_t *sorted_ids, int32_t *block_expert, int32_t *inv_pos)
+{
+    if (T < 0 || K < 1 || E < 1 || B < 1 || cap < 0 || cap % B != 0)
+        return -1;
+    const int64_t TK = T * K;
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t p = 0; p < TK; ++p) {
+        if (ids[p] < 0 || ids[p] >= E)
+            return -1;
+        counts[ids[p]] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t padded = (int64_t)(counts[e] + B - 1) / B * B;
+        offsets[e + 1] = (int32_t)(offsets[e] + padded);
+    }
+    if (offsets[E] > cap)
+        return -2;
+    for (int64_t r = 0; r < cap; ++r)
+        sorted_ids[r] = (int32_t)TK;
+    int32_t *fill = calloc((size_t)E, sizeof(int32_t));
+    for (int64_t p = 0; p < TK; ++p) {
+        int e = ids[p];
+        int64_t r = offsets[e] + fill[e];
+        fill[e] += 1;
+        sorted_ids[r] = (int32_t)p;
+        inv_pos[p] = (int32_t)r;
+    }
+    free(fill);
+    for (int64_t b = 0; b < cap / B; ++b)
+        block_expert[b] = -1;
+    for (int e = 0; e < E; ++e)
+        for (int64_t b = offsets[e] / B; b < offsets[e + 1] / B; ++b)
+            block_expert[b] = e;
+    return 0;
+}
+
+/*
+ * y[r][:] = SwiGLU(x[r][:]) for n rows with one set of weights
+ * (w13 [2I][H] gate rows then up rows, w2 [H][I]).  Serves a single expert,
+ * the shared experts and DenseFA.  Parallel over rows.
+ */
+void orc_swiglu(const void *x, int xdt, int64_t n, int H, int I, const void *w13, const void *w2,
+                int wdt, double *y)
+{
+#pragma omp parallel
+    {
+        double *xv = malloc(sizeof(double) * (size_t)H);
+        double *scratch = malloc(sizeof(double) * swiglu_scratch(H, I));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n; ++r) {
+            decode_row(x, xdt, r, H, xv);
+            swiglu_token(xv, H, I, w13, w2, wdt, scratch, y + r * H);
+        }
+        free(xv);
+        free(scratch);
+    }
+}
+
+/*
+ * out[t][h] = sum_{k ascending} w[t][k] * y[t*K + k][h]  (+ s[t][h] if s).
+ */
+void orc_combine(const double *y, const double *w, const double *s, int64_t T, int K, int H,
+                 double *out)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += w[t * K + k] * y[(t * K + k) * H + h];
+            out[t * H + h] = acc + (s ? s[t * H + h] : 0.0);
+        }
+}
+
+/*
+ * The whole layer for T tokens, one token at a time: route the token, run
+ * each of its K experts on it, add the shared experts (weight 1, width Is;
+ * Is = 0 for none), and combine.  w13 is [E][2I][H], w2 is [E][H][I].
+ * ids_out/w_out (nullable) receive the routing.  Returns 0 or the route error.
+ */
+int orc_moe_layer(const void *x, int xdt, const float *logits, int64_t T, int H, int I, int E,
+                  int K, const void *w13, const void *w2, int wdt, int Is, const void *ws13,
+                  const void *ws2, int32_t *ids_out, double *w_out, double *out)
+{
+    if (E < 1 || K < 1 || K > E || T < 0)
+        return -1;
+    const size_t esize = wdt == ORC_F32 ? 4 : 2;
+    int rc = 0;
+#pragma omp parallel
+    {
+        double *xv = malloc(sizeof(double) * (size_t)H);
+        int Imax = I > Is ? I : Is;
+        double *scratch = malloc(sizeof(double) * swiglu_scratch(H, Imax));
+        double *y = malloc(sizeof(double) * (size_t)H * (size_t)(K + 1));
+        int32_t *ids = malloc(sizeof(int32_t) * (size_t)K);
+        double *w = malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            if (orc_route(logits + t * E, 1, E, K, ids, w) != 0) {
+                rc = -1;
+                continue;
+            }
+            decode_row(x, xdt, t, H, xv);
+            for (int k = 0; k < K; ++k) {
+                const char *e13 = (const char *)w13 + (size_t)ids[k] * 2 * I * H * esize;
+                const char *e2 = (const char *)w2 + (size_t)ids[k] * H * I * esize;
+                swiglu_token(xv, H, I, e13, e2, wdt, scratch, y + (size_t)k * H);
+            }
+            double *s = NULL;
+            if (Is > 0) {
+                s = y + (size_t)K * H;
+                swiglu_token(xv, H, Is, ws13, ws2, wdt, scratch, s);
+            }
+            orc_combine(y, w, s, 1, K, H, out + t * H);
+            if (ids_out)
+                memcpy(ids_out + t * K, ids, sizeof(int32_t) * (size_t)K);
+            if (w_out)
+                memcpy(w_out + t * K, w, sizeof(double) * (size_t)K);
+        }
+        free(xv);
+        free(scratch);
+        free(y);
+        free(ids);
+        free(w);
+    }
+    return rc;
+}
