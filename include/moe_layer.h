@@ -1,0 +1,193 @@
+/*
+ * moe_layer.h -- C ABI of the MI355X (gfx950) forward pass of one
+ * Mixture-of-Experts feed-forward layer, and of its FLOP-matched dense
+ * baseline (DenseFA).
+ *
+ * The layer pass is five stream-ordered calls:
+ *
+ *   moe_route        router logits -> top-K expert ids and combine weights
+ *   moe_align        (token, slot) pairs -> expert buckets padded to the tile
+ *   moe_grouped_ffn  per-expert SwiGLU: gate/up GEMM + SwiGLU, then down GEMM
+ *                    (also callable as its two halves, moe_grouped_gate_up and
+ *                    moe_grouped_down)
+ *   moe_combine      weighted sum of each token's K expert rows (+ shared)
+ *   dense_ffn_fa     one dense SwiGLU FFN over all tokens: the DenseFA
+ *                    baseline, and the shared experts of a layer
+ *
+ * Sources for what each call computes are cited at the call.  "Serving-tax
+ * notes" below means the talk notes on "Demystifying the Mixture of Experts
+ * Serving Tax" (MLSys 2026); "TEMPO page" means the article on TEMPO
+ * (makespan-aware expert-parallel load balancing).
+ *
+ * Conventions (all calls):
+ *  - Every buffer is device memory owned by the caller; the library never
+ *    allocates, frees or keeps state between calls, and is thread-safe.
+ *  - Tensors are dense row-major; base pointers are 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns without waiting; results are valid once the
+ *    stream has reached that point.  No call synchronises with the host.
+ *  - Arguments are checked before anything is launched; on error nothing is
+ *    enqueued and no output is touched.  T = 0 is a successful no-op.
+ *  - A failed launch returns MOE_EHIP.  moe_last_error() returns a message
+ *    for the last failure on the calling thread.
+ *  - Limits: 1 <= K <= E <= 256; H and the intermediate sizes multiples of 64;
+ *    T * K < 2^31; alignment block 1..1024.  Storage dtypes are fp32 or bf16;
+ *    GEMM operands are rounded to bf16 and accumulated in fp32.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,        /* null/misaligned pointer, negative size, K outside [1, E], ... */
+    MOE_EUNSUPPORTED = 2,  /* shape or dtype outside the limits above */
+    MOE_ECAPACITY = 3,     /* plan capacity or workspace smaller than required */
+    MOE_EHIP = 4           /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Schedules of the grouped FFN (and of the dense FFN). */
+typedef enum {
+    MOE_SCHED_AUTO = 0,    /* chosen from the shape */
+    MOE_SCHED_STREAM = 1,  /* weight-streaming: each active expert's weights read once per
+                              pass of up to 128 tokens; for HBM-bound (decode) shapes */
+    MOE_SCHED_TILE = 2     /* MFMA tiles of block_m tokens x 128 weight rows staged through
+                              LDS; for MFMA-bound (prefill) shapes; needs block_m 64 or 128 */
+} moe_schedule;
+
+/*
+ * The alignment produced by moe_align and read by the grouped FFN.  All
+ * arrays are int32 device memory owned by the caller:
+ *   expert_counts  [E]        N_e, pairs routed to expert e
+ *   expert_offsets [E+1]      exclusive prefix sum of P_e = ceil(N_e/B)*B;
+ *                             expert_offsets[E] = num_padded
+ *   sorted_ids     [cap]      pair index p = t*K + k of each row; bucket e is
+ *                             rows expert_offsets[e] .. +N_e-1 in ascending p;
+ *                             every other row holds the sentinel T*K
+ *   block_expert   [cap/B]    expert of each B-row block; -1 past num_padded
+ *   inv_pos        [T*K]      row holding pair p
+ *   block_m        B, the padding block (the GEMM M-tile)
+ *   cap            rows of sorted_ids; a multiple of B and at least
+ *                  moe_align_capacity(T, K, E, B)
+ */
+typedef struct {
+    int32_t *expert_counts;
+    int32_t *expert_offsets;
+    int32_t *sorted_ids;
+    int32_t *block_expert;
+    int32_t *inv_pos;
+    int32_t block_m;
+    int64_t cap;
+} moe_plan;
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *moe_last_error(void);
+const char *moe_status_string(moe_status s);
+
+/*
+ * Rows the alignment may need: the padded total sum_e ceil(N_e/B)*B is at
+ * most T*K + min(E, T*K)*(B-1) (each non-empty bucket adds fewer than B rows
+ * of padding), rounded up to a multiple of B.  Returns -1 on bad arguments.
+ */
+int64_t moe_align_capacity(int64_t T, int K, int E, int block_m);
+
+/* Workspace bytes moe_grouped_ffn needs: the SwiGLU activations, [cap][I] bf16. */
+int64_t moe_ffn_workspace_bytes(int64_t cap, int I);
+
+/* Workspace bytes dense_ffn_fa needs: the activations of T tokens (block-rounded), bf16. */
+int64_t dense_ffn_workspace_bytes(int64_t T, int I_fa);
+
+/*
+ * Routing (Serving-tax notes, Table 1 row "auxiliary kernels": routing and
+ * top-K; finding 5 / Fig. 5).  The pages leave the gating function open; it
+ * is softmax over the E logits, the K largest, renormalised to sum to one:
+ *   selected: the K experts with the largest logits, ties to the lower id;
+ *   slot order: logit descending, then id ascending;
+ *   topk_w[t][j] = p_{e_j} / sum_i p_{e_i},  p = softmax(logits[t]).
+ * logits   [T][E] fp32 (finite)          topk_ids [T][K] int32 (out)
+ * topk_w   [T][K] fp32 (out)
+ * Errors: MOE_EINVAL (null/misaligned, T < 0, K outside [1, E]),
+ *         MOE_EUNSUPPORTED (E > 256).
+ */
+moe_status moe_route(const float *logits, int64_t T, int E, int K, int32_t *topk_ids,
+                     float *topk_w, void *stream);
+
+/*
+ * Alignment with block-wise padding (Serving-tax notes, "Padding model
+ * (Section 5.1)": every expert's token count rounded up to a multiple of the
+ * block B, P = sum_i ceil(N_i/B)*B; the 128-row grouped-GEMM tile of the
+ * TEMPO page is the prefill choice of B).  Fills every array of `plan` (see
+ * moe_plan) over its whole length.  Deterministic: buckets hold their pairs in
+ * ascending p.  topk_ids [T][K] int32 in [0, E).
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (E > 256), MOE_ECAPACITY (cap too small).
+ */
+moe_status moe_align(const int32_t *topk_ids, int64_t T, int K, int E, const moe_plan *plan,
+                     void *stream);
+
+/*
+ * Grouped expert FFN (Serving-tax notes, Table 1 row "GroupGEMM": the batch
+ * is split per expert; Table 2 gives the MoE intermediate size).  The expert
+ * body is a bias-free SwiGLU.  For each valid row r of the plan (pair
+ * p = sorted_ids[r], token t = p / K, expert e):
+ *   a = silu(W1_e x_t) * (W3_e x_t),   y_pairs[p] = W2_e a
+ * x        [T][H]       dtype dt
+ * w13      [E][2I][H]   dtype dt; rows 0..I-1 of each expert are W1 (gate),
+ *                       rows I..2I-1 are W3 (up)
+ * w2       [E][H][I]    dtype dt (down projection, out x in)
+ * workspace            >= moe_ffn_workspace_bytes(plan->cap, I) bytes
+ * y_pairs  [T*K][H]     dtype dt (out), row p = t*K + k
+ * Rows of experts with no tokens are never read: an unused expert's weights
+ * cost no HBM traffic.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY.
+ */
+moe_status moe_grouped_ffn(const void *x, moe_dtype dt, int64_t T, int H, int I, int E, int K,
+                           const void *w13, const void *w2, const moe_plan *plan,
+                           void *workspace, int64_t workspace_bytes, void *y_pairs,
+                           void *stream);
+
+/* First half of moe_grouped_ffn: writes a = silu(W1 x) * (W3 x) as bf16 into
+ * workspace row r, columns 0..I-1, for every valid row r. */
+moe_status moe_grouped_gate_up(const void *x, moe_dtype dt, int64_t T, int H, int I, int E, int K,
+                               const void *w13, const moe_plan *plan, void *workspace,
+                               int64_t workspace_bytes, moe_schedule sched, void *stream);
+
+/* Second half of moe_grouped_ffn: y_pairs[sorted_ids[r]] = W2_e a_r for every valid row r. */
+moe_status moe_grouped_down(const void *w2, moe_dtype dt, int64_t T, int H, int I, int E, int K,
+                            const moe_plan *plan, const void *workspace, int64_t workspace_bytes,
+                            void *y_pairs, moe_schedule sched, void *stream);
+
+/*
+ * Combine, the "local sum" of finding 5 (Serving-tax notes):
+ *   out[t] = sum_{k = 0..K-1, in slot order} topk_w[t][k] * y_pairs[t*K + k]  (+ shared[t])
+ * accumulated in fp32, rounded once to odt.  No atomics: bit-identical on
+ * every run.  shared may be NULL (a layer with no shared experts).
+ * y_pairs [T*K][H] ydt; topk_w [T][K] fp32; shared [T][H] sdt; out [T][H] odt.
+ */
+moe_status moe_combine(const void *y_pairs, moe_dtype ydt, const float *topk_w, const void *shared,
+                       moe_dtype sdt, int64_t T, int K, int H, void *out, moe_dtype odt,
+                       void *stream);
+
+/*
+ * Dense SwiGLU FFN over all T tokens: out = W2 (silu(W1 x) * (W3 x)).
+ * As DenseFA (Serving-tax notes, section "定義", Eq. 1: tau = T(MoE, b) /
+ * T(DenseFA, b)) its width is I_fa = K*I + I_s, the MoE layer's per-token
+ * FLOPs; it also computes a layer's shared experts (width I_s, weight 1).
+ * x [T][H] dt; w13 [2*I_fa][H] dt (gate rows then up rows); w2 [H][I_fa] dt;
+ * workspace >= dense_ffn_workspace_bytes(T, I_fa); out [T][H] odt.
+ */
+moe_status dense_ffn_fa(const void *x, moe_dtype dt, int64_t T, int H, int I_fa, const void *w13,
+                        const void *w2, void *workspace, int64_t workspace_bytes, void *out,
+                        moe_dtype odt, moe_schedule sched, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_H */

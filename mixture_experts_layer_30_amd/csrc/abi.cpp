@@ -1,0 +1,274 @@
+// C ABI of the MoE layer library: argument checks, schedule choice, launches.
+// What each call computes is documented in include/moe_layer.h.
+#include "../../include/moe_layer.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int kMaxExperts = 256;
+
+bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+size_t dt_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+moe_status check_route_shape(int64_t T, int E, int K) {
+  if (T < 0) return fail(MOE_EINVAL, "T = %lld < 0", (long long)T);
+  if (E < 1 || K < 1 || K > E) return fail(MOE_EINVAL, "need 1 <= K <= E (K = %d, E = %d)", K, E);
+  if (E > kMaxExperts) return fail(MOE_EUNSUPPORTED, "E = %d > %d", E, kMaxExperts);
+  if (T * K >= (int64_t)1 << 31) return fail(MOE_EUNSUPPORTED, "T*K must be < 2^31");
+  return MOE_OK;
+}
+
+moe_status check_plan(const moe_plan* plan, int64_t T, int K, int E) {
+  if (!plan) return fail(MOE_EINVAL, "plan is NULL");
+  if (plan->block_m < 1 || plan->block_m > 1024)
+    return fail(MOE_EUNSUPPORTED, "block_m = %d outside 1..1024", plan->block_m);
+  const int32_t* arrs[5] = {plan->expert_counts, plan->expert_offsets, plan->sorted_ids,
+                            plan->block_expert, plan->inv_pos};
+  const char* names[5] = {"expert_counts", "expert_offsets", "sorted_ids", "block_expert",
+                          "inv_pos"};
+  for (int i = 0; i < 5; ++i)
+    if (!arrs[i] || !aligned(arrs[i], 4))
+      return fail(MOE_EINVAL, "plan->%s is NULL or misaligned", names[i]);
+  if (plan->cap % plan->block_m != 0)
+    return fail(MOE_EINVAL, "plan->cap = %lld is not a multiple of block_m = %d",
+                (long long)plan->cap, plan->block_m);
+  const int64_t need = moe_align_capacity(T, K, E, plan->block_m);
+  if (plan->cap < need)
+    return fail(MOE_ECAPACITY, "plan->cap = %lld < %lld required", (long long)plan->cap,
+                (long long)need);
+  if (plan->cap >= (int64_t)1 << 31) return fail(MOE_EUNSUPPORTED, "plan->cap must be < 2^31");
+  return MOE_OK;
+}
+
+moe_status check_ffn_dims(int H, int I) {
+  if (H < 64 || H % 64 != 0) return fail(MOE_EUNSUPPORTED, "H = %d must be a positive multiple of 64", H);
+  if (I < 64 || I % 64 != 0) return fail(MOE_EUNSUPPORTED, "I = %d must be a positive multiple of 64", I);
+  return MOE_OK;
+}
+
+// 16-token MFMA blocks per weight pass of the streaming schedule.  Each
+// expert holds at most T rows (a token's K experts are distinct), so T bounds
+// the largest bucket.
+int stream_tok_blocks(int64_t max_rows) {
+  if (max_rows <= 16) return 1;
+  if (max_rows <= 32) return 2;
+  return 4;
+}
+
+moe_schedule pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m) {
+  (void)T; (void)K; (void)E; (void)block_m;
+  if (req == MOE_SCHED_TILE) return MOE_SCHED_TILE;
+  return MOE_SCHED_STREAM;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ECAPACITY: return "capacity or workspace too small";
+    case MOE_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int64_t moe_align_capacity(int64_t T, int K, int E, int block_m) {
+  if (T < 0 || K < 1 || E < 1 || block_m < 1) return -1;
+  const int64_t TK = T * K;
+  const int64_t active = TK < E ? TK : E;
+  return round_up(TK + active * (block_m - 1), block_m);
+}
+
+int64_t moe_ffn_workspace_bytes(int64_t cap, int I) {
+  if (cap < 0 || I < 0) return -1;
+  return cap * (int64_t)I * 2;
+}
+
+int64_t dense_ffn_workspace_bytes(int64_t T, int I_fa) {
+  if (T < 0 || I_fa < 0) return -1;
+  return round_up(T, 128) * (int64_t)I_fa * 2;
+}
+
+moe_status moe_route(const float* logits, int64_t T, int E, int K, int32_t* topk_ids,
+                     float* topk_w, void* stream) {
+  moe_status st = check_route_shape(T, E, K);
+  if (st) return st;
+  if (T == 0) return ok();
+  if (!logits || !topk_ids || !topk_w || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return fail(MOE_EINVAL, "moe_route: NULL or misaligned pointer");
+  return hip_status(moe::launch_route(logits, T, E, K, topk_ids, topk_w, (hipStream_t)stream),
+                    "moe_route");
+}
+
+moe_status moe_align(const int32_t* topk_ids, int64_t T, int K, int E, const moe_plan* plan,
+                     void* stream) {
+  moe_status st = check_route_shape(T, E, K);
+  if (st) return st;
+  if (T > 0 && (!topk_ids || !aligned(topk_ids, 4)))
+    return fail(MOE_EINVAL, "moe_align: topk_ids NULL or misaligned");
+  st = check_plan(plan, T, K, E);
+  if (st) return st;
+  return hip_status(moe::launch_align(topk_ids, T, K, E, plan->block_m, plan->cap,
+                                      plan->expert_counts, plan->expert_offsets,
+                                      plan->sorted_ids, plan->block_expert, plan->inv_pos,
+                                      (hipStream_t)stream),
+                    "moe_align");
+}
+
+static moe_status check_grouped(const void* x, moe_dtype dt, int64_t T, int H, int I, int E, int K,
+                                const moe_plan* plan, int64_t workspace_bytes) {
+  moe_status st = check_route_shape(T, E, K);
+  if (st) return st;
+  if (!valid_dtype(dt)) return fail(MOE_EUNSUPPORTED, "dtype %d", (int)dt);
+  st = check_ffn_dims(H, I);
+  if (st) return st;
+  st = check_plan(plan, T, K, E);
+  if (st) return st;
+  if (workspace_bytes < moe_ffn_workspace_bytes(plan->cap, I))
+    return fail(MOE_ECAPACITY, "workspace %lld bytes < %lld required", (long long)workspace_bytes,
+                (long long)moe_ffn_workspace_bytes(plan->cap, I));
+  (void)x;
+  return MOE_OK;
+}
+
+static moe::RowMap grouped_rows(const moe_plan* plan, int K) {
+  moe::RowMap rm;
+  rm.counts = plan->expert_counts;
+  rm.offsets = plan->expert_offsets;
+  rm.sorted_ids = plan->sorted_ids;
+  rm.block_expert = plan->block_expert;
+  rm.K = K;
+  rm.dense_rows = 0;
+  rm.block_m = plan->block_m;
+  return rm;
+}
+
+moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, int I, int E, int K,
+                               const void* w13, const moe_plan* plan, void* workspace,
+                               int64_t workspace_bytes, moe_schedule sched, void* stream) {
+  moe_status st = check_grouped(x, dt, T, H, I, E, K, plan, workspace_bytes);
+  if (st) return st;
+  if (T == 0) return ok();
+  if (!x || !w13 || !workspace || !aligned(x, 16) || !aligned(w13, 16) || !aligned(workspace, 16))
+    return fail(MOE_EINVAL, "moe_grouped_gate_up: NULL or misaligned pointer");
+  const moe::RowMap rm = grouped_rows(plan, K);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (pick_schedule(sched, T, K, E, plan->block_m) == MOE_SCHED_TILE)
+    return fail(MOE_EUNSUPPORTED, "tile schedule not available");
+  e = moe::launch_stream_gate_up(x, dt, w13, rm, E, H, I, stream_tok_blocks(T),
+                                 (uint16_t*)workspace, s);
+  return hip_status(e, "moe_grouped_gate_up");
+}
+
+moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int I, int E, int K,
+                            const moe_plan* plan, const void* workspace, int64_t workspace_bytes,
+                            void* y_pairs, moe_schedule sched, void* stream) {
+  moe_status st = check_grouped(w2, dt, T, H, I, E, K, plan, workspace_bytes);
+  if (st) return st;
+  if (T == 0) return ok();
+  if (!w2 || !workspace || !y_pairs || !aligned(w2, 16) || !aligned(workspace, 16) ||
+      !aligned(y_pairs, 16))
+    return fail(MOE_EINVAL, "moe_grouped_down: NULL or misaligned pointer");
+  const moe::RowMap rm = grouped_rows(plan, K);
+  hipStream_t s = (hipStream_t)stream;
+  if (pick_schedule(sched, T, K, E, plan->block_m) == MOE_SCHED_TILE)
+    return fail(MOE_EUNSUPPORTED, "tile schedule not available");
+  hipError_t e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, E, H, I,
+                                         stream_tok_blocks(T), y_pairs, dt, s);
+  return hip_status(e, "moe_grouped_down");
+}
+
+moe_status moe_grouped_ffn(const void* x, moe_dtype dt, int64_t T, int H, int I, int E, int K,
+                           const void* w13, const void* w2, const moe_plan* plan, void* workspace,
+                           int64_t workspace_bytes, void* y_pairs, void* stream) {
+  moe_status st = moe_grouped_gate_up(x, dt, T, H, I, E, K, w13, plan, workspace, workspace_bytes,
+                                      MOE_SCHED_AUTO, stream);
+  if (st) return st;
+  return moe_grouped_down(w2, dt, T, H, I, E, K, plan, workspace, workspace_bytes, y_pairs,
+                          MOE_SCHED_AUTO, stream);
+}
+
+moe_status moe_combine(const void* y_pairs, moe_dtype ydt, const float* topk_w, const void* shared,
+                       moe_dtype sdt, int64_t T, int K, int H, void* out, moe_dtype odt,
+                       void* stream) {
+  if (T < 0 || K < 1) return fail(MOE_EINVAL, "moe_combine: T = %lld, K = %d", (long long)T, K);
+  if (!valid_dtype(ydt) || !valid_dtype(sdt) || !valid_dtype(odt))
+    return fail(MOE_EUNSUPPORTED, "moe_combine: dtype");
+  if (H < 8 || H % 8 != 0) return fail(MOE_EUNSUPPORTED, "moe_combine: H = %d must be a multiple of 8", H);
+  if (T * K >= (int64_t)1 << 31) return fail(MOE_EUNSUPPORTED, "T*K must be < 2^31");
+  if (T == 0) return ok();
+  if (!y_pairs || !topk_w || !out || !aligned(y_pairs, 16) || !aligned(topk_w, 4) ||
+      !aligned(out, 16) || (shared && !aligned(shared, 16)))
+    return fail(MOE_EINVAL, "moe_combine: NULL or misaligned pointer");
+  return hip_status(moe::launch_combine(y_pairs, ydt, topk_w, shared, sdt, T, K, H, out, odt,
+                                        (hipStream_t)stream),
+                    "moe_combine");
+}
+
+moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa, const void* w13,
+                        const void* w2, void* workspace, int64_t workspace_bytes, void* out,
+                        moe_dtype odt, moe_schedule sched, void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "dense_ffn_fa: T < 0");
+  if (T >= (int64_t)1 << 31) return fail(MOE_EUNSUPPORTED, "dense_ffn_fa: T must be < 2^31");
+  if (!valid_dtype(dt) || !valid_dtype(odt)) return fail(MOE_EUNSUPPORTED, "dense_ffn_fa: dtype");
+  moe_status st = check_ffn_dims(H, I_fa);
+  if (st) return st;
+  if (workspace_bytes < dense_ffn_workspace_bytes(T, I_fa))
+    return fail(MOE_ECAPACITY, "dense_ffn_fa: workspace %lld bytes < %lld required",
+                (long long)workspace_bytes, (long long)dense_ffn_workspace_bytes(T, I_fa));
+  if (T == 0) return ok();
+  if (!x || !w13 || !w2 || !workspace || !out || !aligned(x, 16) || !aligned(w13, 16) ||
+      !aligned(w2, 16) || !aligned(workspace, 16) || !aligned(out, 16))
+    return fail(MOE_EINVAL, "dense_ffn_fa: NULL or misaligned pointer");
+  moe::RowMap rm;
+  memset(&rm, 0, sizeof rm);
+  rm.K = 1;
+  rm.dense_rows = T;
+  rm.block_m = 128;
+  hipStream_t s = (hipStream_t)stream;
+  if (sched == MOE_SCHED_TILE) return fail(MOE_EUNSUPPORTED, "tile schedule not available");
+  const int tb = stream_tok_blocks(T);
+  hipError_t e = moe::launch_stream_gate_up(x, dt, w13, rm, 1, H, I_fa, tb, (uint16_t*)workspace, s);
+  if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
+  e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, 1, H, I_fa, tb, out, odt, s);
+  return hip_status(e, "dense_ffn_fa down");
+}
+
+}  // extern "C"

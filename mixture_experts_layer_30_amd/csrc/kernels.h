@@ -1,0 +1,50 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kDtF32 = 0;
+constexpr int kDtBF16 = 1;
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
+                        hipStream_t s);
+
+hipError_t launch_align(const int32_t* ids, int64_t T, int K, int E, int B, int64_t cap,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* inv_pos, hipStream_t s);
+
+hipError_t launch_combine(const void* y, int ydt, const float* w, const void* shared, int sdt,
+                          int64_t T, int K, int H, void* out, int odt, hipStream_t s);
+
+// Token rows of a grouped (or dense) GEMM.  Grouped: expert e owns the rows
+// offsets[e] .. offsets[e] + counts[e] - 1 of the alignment; row r holds pair
+// sorted_ids[r], i.e. token sorted_ids[r] / K.  Dense (counts == nullptr): one
+// "expert" whose row r is token r, for r < dense_rows.
+struct RowMap {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  int K;
+  int64_t dense_rows;
+  int block_m;
+};
+
+// Weight-streaming schedule.  tok_blocks: 16-token MFMA blocks per pass over
+// the weights (1, 2, 4 or 8); E: grid extent over experts (1 for dense).
+hipError_t launch_stream_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm, int E,
+                                 int H, int I, int tok_blocks, uint16_t* act, hipStream_t s);
+hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
+                              int E, int H, int I, int tok_blocks, void* y, int ydt,
+                              hipStream_t s);
+
+// LDS-tiled MFMA schedule: one workgroup per (block_m-row token block, 128 weight rows).
+hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
+                               int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s);
+hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
+                            int64_t nblocks, int H, int I, void* y, int ydt, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status before launching
+anything (every call here returns during argument checking)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_30_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_layer.h")
+
+FAKE = 0x10000  # an aligned, never dereferenced address
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from mixture_experts_layer_30_amd import build
+        build.build()
+    return B.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\([^;{]*\)\s*;", src)))
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.moe_status_string(0) == b"ok"
+    assert L.moe_status_string(3) == b"capacity or workspace too small"
+
+
+def test_align_capacity_bound(L):
+    # T*K + min(E, T*K)*(B-1), rounded up to B
+    assert B.moe_align_capacity(128, 8, 256, 16) == 1024 + 256 * 15
+    assert B.moe_align_capacity(2048, 8, 64, 128) == 16384 + 64 * 127 + 64
+    assert B.moe_align_capacity(1, 2, 8, 128) == 256
+    assert B.moe_align_capacity(0, 2, 8, 16) == 0
+    assert B.moe_align_capacity(-1, 2, 8, 16) == -1
+    assert B.moe_ffn_workspace_bytes(4864, 2048) == 4864 * 2048 * 2
+    assert B.dense_ffn_workspace_bytes(1, 512) == 128 * 512 * 2
+
+
+def st(r):
+    return int(r)
+
+
+def route(L, T=4, E=8, K=2, logits=FAKE, ids=FAKE, w=FAKE):
+    return st(L.moe_route(logits, T, E, K, ids, w, None))
+
+
+def test_route_argument_checks(L):
+    assert route(L, K=9) == B.MOE_EINVAL
+    assert route(L, K=0) == B.MOE_EINVAL
+    assert route(L, T=-1) == B.MOE_EINVAL
+    assert route(L, E=300, K=2) == B.MOE_EUNSUPPORTED
+    assert route(L, logits=NULL) == B.MOE_EINVAL
+    assert route(L, ids=FAKE + 2) == B.MOE_EINVAL
+    assert b"NULL or misaligned" in L.moe_last_error()
+    assert route(L, T=0, logits=NULL, ids=NULL, w=NULL) == B.MOE_OK  # empty batch: no-op
+
+
+def plan(cap=4864, block_m=16, ptr=FAKE):
+    return B.moe_plan(ptr, ptr, ptr, ptr, ptr, block_m, cap)
+
+
+def test_align_argument_checks(L):
+    small = plan(cap=4848)
+    assert st(L.moe_align(FAKE, 128, 8, 256, ctypes.byref(small), None)) == B.MOE_ECAPACITY
+    odd = plan(cap=4865)
+    assert st(L.moe_align(FAKE, 128, 8, 256, ctypes.byref(odd), None)) == B.MOE_EINVAL
+    nullp = plan(ptr=0)
+    assert st(L.moe_align(FAKE, 128, 8, 256, ctypes.byref(nullp), None)) == B.MOE_EINVAL
+    assert st(L.moe_align(FAKE, 128, 8, 256, None, None)) == B.MOE_EINVAL
+    bad_b = plan(block_m=0)
+    assert st(L.moe_align(FAKE, 128, 8, 256, ctypes.byref(bad_b), None)) == B.MOE_EUNSUPPORTED
+
+
+def test_grouped_ffn_argument_checks(L):
+    p = plan(cap=4864)
+    ws = B.moe_ffn_workspace_bytes(4864, 2048)
+    args = lambda **kw: dict(dict(x=FAKE, dt=B.MOE_BF16, T=128, H=7168, I=2048, E=256, K=8,  # noqa: E731
+                                  w13=FAKE, w2=FAKE, ws=ws, y=FAKE), **kw)
+
+    def call(a):
+        return st(L.moe_grouped_ffn(a["x"], a["dt"], a["T"], a["H"], a["I"], a["E"], a["K"],
+                                    a["w13"], a["w2"], ctypes.byref(p), FAKE, a["ws"], a["y"], None))
+    assert call(args(H=7000)) == B.MOE_EUNSUPPORTED
+    assert call(args(I=2050)) == B.MOE_EUNSUPPORTED
+    assert call(args(dt=7)) == B.MOE_EUNSUPPORTED
+    assert call(args(ws=ws - 1)) == B.MOE_ECAPACITY
+    assert call(args(x=NULL)) == B.MOE_EINVAL
+    assert call(args(w13=FAKE + 8)) == B.MOE_EINVAL
+    assert call(args(K=9, E=8)) == B.MOE_EINVAL
+    assert call(args(T=0)) == B.MOE_OK
+
+
+def test_combine_and_dense_argument_checks(L):
+    assert st(L.moe_combine(FAKE, B.MOE_BF16, FAKE, None, B.MOE_F32, 4, 2, 100, FAKE, B.MOE_BF16,
+                            None)) == B.MOE_EUNSUPPORTED
+    assert st(L.moe_combine(FAKE, B.MOE_BF16, NULL, None, B.MOE_F32, 4, 2, 128, FAKE, B.MOE_BF16,
+                            None)) == B.MOE_EINVAL
+    assert st(L.moe_combine(FAKE, B.MOE_BF16, FAKE, FAKE + 4, B.MOE_F32, 4, 2, 128, FAKE,
+                            B.MOE_BF16, None)) == B.MOE_EINVAL
+    ws = B.dense_ffn_workspace_bytes(32, 28672)
+    assert st(L.dense_ffn_fa(FAKE, B.MOE_BF16, 32, 4096, 28672, FAKE, FAKE, FAKE, ws - 2, FAKE,
+                             B.MOE_BF16, 0, None)) == B.MOE_ECAPACITY
+    assert st(L.dense_ffn_fa(FAKE, B.MOE_BF16, 32, 4096, 28600, FAKE, FAKE, FAKE, ws, FAKE,
+                             B.MOE_BF16, 0, None)) == B.MOE_EUNSUPPORTED
+    assert st(L.dense_ffn_fa(FAKE, B.MOE_BF16, -1, 4096, 28672, FAKE, FAKE, FAKE, ws, FAKE,
+                             B.MOE_BF16, 0, None)) == B.MOE_EINVAL
+
+
+def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(ImportError):
+        B.lib()
