@@ -1,0 +1,276 @@
+"""Benchmark of one MoE feed-forward layer pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral] [--T 32]
+                    [--routing uniform] [--all] [--no-cpu]
+
+A step is one whole layer pass over one batch of synthetic tokens: route,
+align, grouped gate/up + SwiGLU, grouped down, shared experts (if any) and
+combine.  W untimed steps, then exactly K timed steps between two device
+synchronisations.  Prints one JSON line with tokens/s (the layer's T tokens
+per step), the roofline of the dominant kernel (the grouped gate/up GEMM,
+timed live with HIP events on the stream it runs on), the tax tau against the
+FLOP-matched dense FFN (DenseFA) timed the same way, and the CPU oracle timed
+on the host's cores on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mixture_experts_layer_30_amd import configs, synth  # noqa: E402
+from mixture_experts_layer_30_amd.layer import MoELayer  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+METRIC = "MoE-layer tokens/s at 1 GPU, % HBM/MFMA roofline, tax τ vs DenseFA"
+
+HEADLINE = [("mixtral", 32, "uniform")]
+ALL = [("tiny", 64, "uniform"), ("mixtral", 32, "uniform"), ("mixtral", 1024, "uniform"),
+       ("qwen2", 1, "zipf"), ("qwen2", 32, "zipf"), ("qwen2", 256, "zipf"), ("qwen2", 2048, "zipf"),
+       ("deepseek_v3", 128, "uniform"), ("deepseek_v3", 128, "zipf")] + \
+      [("mixtral_sweep", T, "uniform") for T in (1, 8, 128, 512, 2048)]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("stream_ffn.hip", "tile_ffn.hip", "common.h"):
+        p = os.path.join(ROOT, "mixture_experts_layer_30_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from committed rocprofv3 counter runs, if the
+    kernel sources are unchanged since they were taken."""
+    p = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(workload)
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def algorithmic(shape, T, e_active):
+    """Unpadded algorithmic bytes and flops (weights of active experts read once)."""
+    H, I, K, Is = shape.hidden, shape.inter, shape.topk, shape.shared_inter
+    eb = 4 if shape.dtype == "f32" else 2
+    gu_bytes = e_active * 2 * I * H * eb + T * H * eb + T * K * I * 2
+    layer_bytes = (e_active * 3 * I * H * eb + 3 * H * Is * eb + T * H * eb * 2
+                   + T * shape.experts * 4)
+    gu_flops = 2 * T * K * H * 2 * I
+    layer_flops = 6 * T * K * H * I + 6 * T * H * Is
+    fa_bytes = 3 * H * shape.dense_fa_inter * eb + 2 * T * H * eb
+    fa_flops = 6 * T * H * shape.dense_fa_inter
+    return dict(gu_bytes=gu_bytes, layer_bytes=layer_bytes, gu_flops=gu_flops,
+                layer_flops=layer_flops, fa_bytes=fa_bytes, fa_flops=fa_flops)
+
+
+def time_steps(fn, steps, warmup, mid=None):
+    """Time exactly `steps` calls of fn between device syncs; with `mid` = (before, after)
+    callables, HIP events on the current stream bracket the dominant kernel live."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [] if mid else None
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        if mid:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fn(a, b, stream)
+            evs.append((a, b))
+        else:
+            fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    kern_ms = None
+    if evs:
+        kern_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    return gpu_ms / steps, wall * 1e3 / steps, kern_ms
+
+
+def breakdown(layer, reps=10):
+    """Per-call device time (HIP events), a Fig. 5-style split of the pass."""
+    names = ["route", "align", "gate_up", "down", "shared", "combine"]
+    out = {}
+    torch.cuda.synchronize()
+    for n in names:
+        fn = getattr(layer, n)
+        tot = 0.0
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        out[n] = round(tot / reps * 1e3, 2)
+    return out
+
+
+def cpu_baseline(shape, dev_inputs, T, budget_s=20.0):
+    """The oracle (as it is) on the host cores, on a bounded sample of the batch."""
+    import oracle
+    x = dev_inputs["x"].cpu()
+    logits = dev_inputs["logits"].cpu()
+    ids, _ = oracle.route(logits, shape.topk)
+    # estimate the cost of one token (expert MACs in fp64) and size the sample
+    macs_tok = 3 * shape.hidden * (shape.topk * shape.inter + shape.shared_inter)
+    threads = oracle.max_threads()
+    n = int(max(1, min(T, budget_s * 0.4e9 * threads / macs_tok)))
+    tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
+    tokens = np.unique(tokens)
+    used = np.unique(ids[tokens])
+    # only the experts the sample routes to are copied; the others are never read
+    E = shape.experts
+    w13 = torch.zeros((E,) + tuple(dev_inputs["w13"].shape[1:]), dtype=dev_inputs["w13"].dtype)
+    w2 = torch.zeros((E,) + tuple(dev_inputs["w2"].shape[1:]), dtype=dev_inputs["w2"].dtype)
+    for e in used:
+        w13[e] = dev_inputs["w13"][e].cpu()
+        w2[e] = dev_inputs["w2"][e].cpu()
+    ws13 = dev_inputs["ws13"].cpu() if dev_inputs.get("ws13") is not None else None
+    ws2 = dev_inputs["ws2"].cpu() if dev_inputs.get("ws2") is not None else None
+    t0 = time.perf_counter()
+    oracle.moe_layer(x[tokens], logits[tokens], w13, w2, shape.topk, ws13, ws2)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(tokens)} of the {T} tokens of the same batch (weights bf16 on host, "
+                      f"fp64 accumulation), {dt:.2f} s wall"}
+
+
+def run_workload(name, T, routing, steps, warmup, do_cpu):
+    shape = configs.CONFIGS[name]
+    torch.manual_seed(0)
+    d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=True)
+    layer = MoELayer(shape, d)
+    layer.forward()
+    torch.cuda.synchronize()
+    ids = layer.topk_ids.cpu().numpy()
+    e_active = int(len(np.unique(ids)))
+    num_padded = int(layer.plan.expert_offsets[-1].item())
+    alg = algorithmic(shape, T, e_active)
+
+    def step(a=None, b=None, stream=None):
+        layer.route()
+        layer.align()
+        if a is not None:
+            a.record(stream)
+        layer.gate_up()
+        if b is not None:
+            b.record(stream)
+        layer.down()
+        layer.shared()
+        layer.combine()
+
+    ms, wall_ms, gu_ms = time_steps(step, steps, warmup, mid=True)
+    fa_ms, _, _ = time_steps(layer.dense_fa, steps, warmup)
+    bd = breakdown(layer)
+
+    dtype = "f32" if shape.dtype == "f32" else "bf16"
+    gu_s = gu_ms * 1e-3
+    ai = alg["gu_flops"] / alg["gu_bytes"]
+    peak_flops = FP32_PEAK_TFLOPS if dtype == "f32" else BF16_PEAK_TFLOPS
+    ridge = peak_flops * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(alg["gu_bytes"] / gu_s / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(alg["gu_flops"] / gu_s / 1e12, 1),
+                "peak": peak_flops, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    workload = f"{name} T={T} {routing}"
+    traffic = measured_traffic(workload)
+    roof["traffic"] = traffic
+    roof["kernel"] = "moe_grouped_gate_up (gate/up GEMM + SwiGLU)"
+    roof["algorithmic_bytes"] = alg["gu_bytes"]
+    roof["algorithmic_flops"] = alg["gu_flops"]
+    roof["avg_launch_us"] = round(gu_ms * 1e3, 2)
+
+    layer_s = ms * 1e-3
+    rec = {
+        "metric": METRIC,
+        "value": round(T * steps / (ms * steps * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": workload, "hidden": shape.hidden, "inter": shape.inter,
+                   "experts": shape.experts, "topk": shape.topk,
+                   "shared_inter": shape.shared_inter, "tokens": T, "routing": routing,
+                   "block_m": layer.block_m, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer": {"achieved_GBps": round(alg["layer_bytes"] / layer_s / 1e9, 1),
+                  "achieved_TFLOPs": round(alg["layer_flops"] / layer_s / 1e12, 2),
+                  "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(alg["layer_flops"] / layer_s / 1e12 / peak_flops, 4),
+                  "e_active": e_active, "padding_eta": round(num_padded / (T * shape.topk), 4),
+                  "breakdown_us": bd, "wall_ms_per_step": round(wall_ms, 4)},
+        "tau": round(ms / fa_ms, 4),
+        "dense_fa": {"ms": round(fa_ms, 4), "inter": shape.dense_fa_inter,
+                     "achieved_GBps": round(alg["fa_bytes"] / (fa_ms * 1e-3) / 1e9, 1),
+                     "achieved_TFLOPs": round(alg["fa_flops"] / (fa_ms * 1e-3) / 1e12, 2)},
+    }
+    if do_cpu:
+        rec["cpu_baseline"] = cpu_baseline(shape, d, T)
+    del d, layer
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=None)
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--routing", default=None)
+    ap.add_argument("--all", action="store_true", help="one line per workload of every config")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
+              "runs on more than one GPU are not part of this library", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.all:
+        work = ALL
+    elif args.config:
+        shape = configs.CONFIGS[args.config]
+        work = [(args.config, args.T or shape.tokens[0], args.routing or shape.routing[0])]
+    else:
+        work = HEADLINE
+    for i, (name, T, routing) in enumerate(work):
+        rec = run_workload(name, T, routing, args.steps, args.warmup,
+                           do_cpu=(not args.no_cpu) and (i == 0))
+        print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

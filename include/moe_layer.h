@@ -101,8 +101,10 @@ int64_t moe_align_capacity(int64_t T, int K, int E, int block_m);
 /* Workspace bytes moe_grouped_ffn needs: the SwiGLU activations, [cap][I] bf16. */
 int64_t moe_ffn_workspace_bytes(int64_t cap, int I);
 
-/* Workspace bytes dense_ffn_fa needs: the activations of T tokens (block-rounded), bf16. */
-int64_t dense_ffn_workspace_bytes(int64_t T, int I_fa);
+/* Workspace bytes dense_ffn_fa needs: the activations of T tokens (bf16) and,
+ * when the contraction is split across workgroups, the fp32 partial sums.
+ * Returns -1 on unsupported sizes. */
+int64_t dense_ffn_workspace_bytes(int64_t T, int H, int I_fa);
 
 /*
  * Routing (Serving-tax notes, Table 1 row "auxiliary kernels": routing and
@@ -180,7 +182,9 @@ moe_status moe_combine(const void *y_pairs, moe_dtype ydt, const float *topk_w, 
  * T(DenseFA, b)) its width is I_fa = K*I + I_s, the MoE layer's per-token
  * FLOPs; it also computes a layer's shared experts (width I_s, weight 1).
  * x [T][H] dt; w13 [2*I_fa][H] dt (gate rows then up rows); w2 [H][I_fa] dt;
- * workspace >= dense_ffn_workspace_bytes(T, I_fa); out [T][H] odt.
+ * workspace >= dense_ffn_workspace_bytes(T, H, I_fa); out [T][H] odt.
+ * Deterministic: when the contraction is split across workgroups the partial
+ * sums are added in a fixed order by a second kernel, never with atomics.
  */
 moe_status dense_ffn_fa(const void *x, moe_dtype dt, int64_t T, int H, int I_fa, const void *w13,
                         const void *w2, void *workspace, int64_t workspace_bytes, void *out,

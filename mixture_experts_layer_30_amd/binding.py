@@ -54,7 +54,7 @@ def lib():
         L.moe_ffn_workspace_bytes.restype = i64
         L.moe_ffn_workspace_bytes.argtypes = [i64, i32]
         L.dense_ffn_workspace_bytes.restype = i64
-        L.dense_ffn_workspace_bytes.argtypes = [i64, i32]
+        L.dense_ffn_workspace_bytes.argtypes = [i64, i32, i32]
         L.moe_route.restype = i32
         L.moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         L.moe_align.restype = i32
@@ -104,8 +104,8 @@ def moe_ffn_workspace_bytes(cap, I):
     return lib().moe_ffn_workspace_bytes(cap, I)
 
 
-def dense_ffn_workspace_bytes(T, I):
-    return lib().dense_ffn_workspace_bytes(T, I)
+def dense_ffn_workspace_bytes(T, H, I):
+    return lib().dense_ffn_workspace_bytes(T, H, I)
 
 
 class Plan:

@@ -84,6 +84,33 @@ int stream_tok_blocks(int64_t max_rows) {
   return 4;
 }
 
+// Dense FFN plan: workgroups per streaming launch are slabs x splits; the
+// contraction is split (deterministically, partial sums added in slice order)
+// until about 1024 workgroups exist, keeping at least 2 chunks per wavefront.
+struct DensePlan {
+  int tok_blocks, split_gu, split_dn;
+  int64_t act_bytes, part_bytes;
+};
+
+int pick_splits(int slabs, int nch) {
+  const int target = 1024;
+  int s = (target + slabs - 1) / slabs;
+  const int most = nch / 8 > 1 ? nch / 8 : 1;
+  return s < 1 ? 1 : (s > most ? most : s);
+}
+
+DensePlan dense_plan(int64_t T, int H, int I) {
+  DensePlan p;
+  p.tok_blocks = stream_tok_blocks(T);
+  p.split_gu = pick_splits(I / 32, H / 64);
+  p.split_dn = pick_splits(H / 64, I / 64);
+  p.act_bytes = round_up(round_up(T, 128) * (int64_t)I * 2, 256);
+  const int64_t gu = p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0;
+  const int64_t dn = p.split_dn > 1 ? (int64_t)p.split_dn * T * H * 4 : 0;
+  p.part_bytes = gu > dn ? gu : dn;
+  return p;
+}
+
 moe_schedule pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m) {
   (void)T; (void)K; (void)E; (void)block_m;
   if (req == MOE_SCHED_TILE) return MOE_SCHED_TILE;
@@ -119,9 +146,10 @@ int64_t moe_ffn_workspace_bytes(int64_t cap, int I) {
   return cap * (int64_t)I * 2;
 }
 
-int64_t dense_ffn_workspace_bytes(int64_t T, int I_fa) {
-  if (T < 0 || I_fa < 0) return -1;
-  return round_up(T, 128) * (int64_t)I_fa * 2;
+int64_t dense_ffn_workspace_bytes(int64_t T, int H, int I_fa) {
+  if (T < 0 || H < 64 || I_fa < 64 || H % 64 || I_fa % 64) return -1;
+  const DensePlan p = dense_plan(T, H, I_fa);
+  return p.act_bytes + p.part_bytes;
 }
 
 moe_status moe_route(const float* logits, int64_t T, int E, int K, int32_t* topk_ids,
@@ -192,8 +220,8 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
   hipError_t e;
   if (pick_schedule(sched, T, K, E, plan->block_m) == MOE_SCHED_TILE)
     return fail(MOE_EUNSUPPORTED, "tile schedule not available");
-  e = moe::launch_stream_gate_up(x, dt, w13, rm, E, H, I, stream_tok_blocks(T),
-                                 (uint16_t*)workspace, s);
+  e = moe::launch_stream_gate_up(x, dt, w13, rm, E, H, I, stream_tok_blocks(T), 1,
+                                 (uint16_t*)workspace, nullptr, s);
   return hip_status(e, "moe_grouped_gate_up");
 }
 
@@ -211,7 +239,7 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   if (pick_schedule(sched, T, K, E, plan->block_m) == MOE_SCHED_TILE)
     return fail(MOE_EUNSUPPORTED, "tile schedule not available");
   hipError_t e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, E, H, I,
-                                         stream_tok_blocks(T), y_pairs, dt, s);
+                                         stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
   return hip_status(e, "moe_grouped_down");
 }
 
@@ -250,9 +278,9 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   if (!valid_dtype(dt) || !valid_dtype(odt)) return fail(MOE_EUNSUPPORTED, "dense_ffn_fa: dtype");
   moe_status st = check_ffn_dims(H, I_fa);
   if (st) return st;
-  if (workspace_bytes < dense_ffn_workspace_bytes(T, I_fa))
+  if (workspace_bytes < dense_ffn_workspace_bytes(T, H, I_fa))
     return fail(MOE_ECAPACITY, "dense_ffn_fa: workspace %lld bytes < %lld required",
-                (long long)workspace_bytes, (long long)dense_ffn_workspace_bytes(T, I_fa));
+                (long long)workspace_bytes, (long long)dense_ffn_workspace_bytes(T, H, I_fa));
   if (T == 0) return ok();
   if (!x || !w13 || !w2 || !workspace || !out || !aligned(x, 16) || !aligned(w13, 16) ||
       !aligned(w2, 16) || !aligned(workspace, 16) || !aligned(out, 16))
@@ -264,10 +292,14 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   rm.block_m = 128;
   hipStream_t s = (hipStream_t)stream;
   if (sched == MOE_SCHED_TILE) return fail(MOE_EUNSUPPORTED, "tile schedule not available");
-  const int tb = stream_tok_blocks(T);
-  hipError_t e = moe::launch_stream_gate_up(x, dt, w13, rm, 1, H, I_fa, tb, (uint16_t*)workspace, s);
+  const DensePlan dp = dense_plan(T, H, I_fa);
+  uint16_t* act = (uint16_t*)workspace;
+  float* part = (float*)((char*)workspace + dp.act_bytes);
+  hipError_t e = moe::launch_stream_gate_up(x, dt, w13, rm, 1, H, I_fa, dp.tok_blocks, dp.split_gu,
+                                            act, part, s);
   if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
-  e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, 1, H, I_fa, tb, out, odt, s);
+  e = moe::launch_stream_down(w2, dt, act, rm, 1, H, I_fa, dp.tok_blocks, dp.split_dn, out, odt,
+                              part, s);
   return hip_status(e, "dense_ffn_fa down");
 }
 

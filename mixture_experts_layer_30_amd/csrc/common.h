@@ -30,19 +30,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-// 8 consecutive elements starting at p, as 8 bf16 in 16 bytes (rounding fp32 storage).
-template <class S>
+// 8 consecutive elements starting at p, as 8 bf16 in 16 bytes (rounding fp32
+// storage).  Streaming (read-once) data uses non-temporal loads, which keep it
+// from displacing reused data in the caches.
+template <class S, bool kStream = false>
 __device__ __forceinline__ u32x4 load8(const typename S::T* p);
 
 template <>
-__device__ __forceinline__ u32x4 load8<BF16>(const uint16_t* p) {
+__device__ __forceinline__ u32x4 load8<BF16, false>(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+template <>
+__device__ __forceinline__ u32x4 load8<BF16, true>(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 template <>
-__device__ __forceinline__ u32x4 load8<F32>(const float* p) {
+__device__ __forceinline__ u32x4 load8<F32, false>(const float* p) {
   const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
   const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+  u32x4 r;
+  r.x = pack_bf16x2(a.x, a.y);
+  r.y = pack_bf16x2(a.z, a.w);
+  r.z = pack_bf16x2(b.x, b.y);
+  r.w = pack_bf16x2(b.z, b.w);
+  return r;
+}
+template <>
+__device__ __forceinline__ u32x4 load8<F32, true>(const float* p) {
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
   u32x4 r;
   r.x = pack_bf16x2(a.x, a.y);
   r.y = pack_bf16x2(a.z, a.w);

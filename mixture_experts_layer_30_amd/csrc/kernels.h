@@ -34,12 +34,16 @@ struct RowMap {
 };
 
 // Weight-streaming schedule.  tok_blocks: 16-token MFMA blocks per pass over
-// the weights (1, 2, 4 or 8); E: grid extent over experts (1 for dense).
+// the weights (1, 2 or 4); E: grid extent over experts (1 for dense).
+// splits > 1 (dense rows only) cuts the contraction into that many slices
+// whose fp32 sums go to `part` ([splits][rows][2I] for gate/up, [splits][rows][H]
+// for down) and are added in slice order by a finish kernel.
 hipError_t launch_stream_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm, int E,
-                                 int H, int I, int tok_blocks, uint16_t* act, hipStream_t s);
+                                 int H, int I, int tok_blocks, int splits, uint16_t* act,
+                                 float* part, hipStream_t s);
 hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
-                              int E, int H, int I, int tok_blocks, void* y, int ydt,
-                              hipStream_t s);
+                              int E, int H, int I, int tok_blocks, int splits, void* y, int ydt,
+                              float* part, hipStream_t s);
 
 // LDS-tiled MFMA schedule: one workgroup per (block_m-row token block, 128 weight rows).
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,

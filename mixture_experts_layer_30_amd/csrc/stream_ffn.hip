@@ -35,57 +35,96 @@ constexpr int kStreamWaves = kStreamThreads / kWave;
 constexpr int kTiles = 4;    // 16-row weight tiles per workgroup
 constexpr int kChunk = 64;   // k per pipeline stage: two 16x16x32 MFMA steps
 
-// acc[q][tb] += W(tile q) * X(token block tb)^T over chunks [c_begin, c_end).
-// Lane l = 16*g + m supplies row m of every tile and of every token block,
-// with k offsets 8g and 32 + 8g inside each chunk (the same for both operands,
-// which is all the contraction needs).
-template <class SW, class SX, int TB, int D>
+// Tuning knobs: waves per SIMD the register budget must allow, and chunks in
+// flight per wavefront for a pass of NB token blocks.
+#ifndef MOE_STREAM_WAVES_PER_SIMD
+#define MOE_STREAM_WAVES_PER_SIMD 2
+#endif
+#ifndef MOE_STREAM_DEPTH_1
+#define MOE_STREAM_DEPTH_1 4
+#endif
+#ifndef MOE_STREAM_DEPTH_2
+#define MOE_STREAM_DEPTH_2 3
+#endif
+#ifndef MOE_STREAM_DEPTH_4
+#define MOE_STREAM_DEPTH_4 2
+#endif
+
+template <class SW, int NB>
+constexpr int stream_depth() {
+  return sizeof(typename SW::T) == 4 ? 1
+         : NB == 1 ? MOE_STREAM_DEPTH_1
+         : NB == 2 ? MOE_STREAM_DEPTH_2
+                   : MOE_STREAM_DEPTH_4;
+}
+
+// acc[q][tb] += W(tile q) * X(token block tb)^T for tb < NB, over chunks
+// [c_begin, c_end).  Lane l = 16*g + m supplies row m of every tile and of
+// every token block, with k offsets 8g and 32 + 8g inside each chunk (the
+// same for both operands, which is all the contraction needs).
+//
+// NB is the exact number of token blocks of the pass (the caller dispatches
+// on it), so every load of the loop is unconditional and the in-order vector
+// memory counter lets D chunks stay in flight.  Prefetches past the wave's
+// last chunk re-read that chunk (an L1/L2 hit) instead of branching.
+template <class SW, class SX, int NB, int TB>
 __device__ __forceinline__ void stream_mainloop(const typename SW::T* const (&wrow)[kTiles],
-                                                const typename SX::T* const (&xrow)[TB], int ntb,
+                                                const typename SX::T* const (&xrow)[TB],
                                                 int c_begin, int c_end, int g,
                                                 f32x4 (&acc)[kTiles][TB]) {
+  constexpr int D = stream_depth<SW, NB>();
+  if (c_begin >= c_end) return;
   u32x4 wr[D][kTiles][2];
-  u32x4 xr[D][TB][2];
+  u32x4 xr[D][NB][2];
   const int kofs = g * 8;
+  const int c_last = c_end - 1;
 
   auto issue = [&](int d, int c) {
-    const int k = c * kChunk + kofs;
+    const int k = min(c, c_last) * kChunk + kofs;
 #pragma unroll
     for (int q = 0; q < kTiles; ++q) {
       wr[d][q][0] = load8<SW>(wrow[q] + k);
       wr[d][q][1] = load8<SW>(wrow[q] + k + 32);
     }
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-      if (tb < ntb) {
-        xr[d][tb][0] = load8<SX>(xrow[tb] + k);
-        xr[d][tb][1] = load8<SX>(xrow[tb] + k + 32);
-      }
+    for (int tb = 0; tb < NB; ++tb) {
+      xr[d][tb][0] = load8<SX>(xrow[tb] + k);
+      xr[d][tb][1] = load8<SX>(xrow[tb] + k + 32);
+    }
   };
   auto compute = [&](int d) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-      if (tb < ntb) {
+    for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-        for (int q = 0; q < kTiles; ++q) {
-          acc[q][tb] = mfma16x16x32(wr[d][q][0], xr[d][tb][0], acc[q][tb]);
-          acc[q][tb] = mfma16x16x32(wr[d][q][1], xr[d][tb][1], acc[q][tb]);
-        }
+      for (int q = 0; q < kTiles; ++q) {
+        acc[q][tb] = mfma16x16x32(wr[d][q][0], xr[d][tb][0], acc[q][tb]);
+        acc[q][tb] = mfma16x16x32(wr[d][q][1], xr[d][tb][1], acc[q][tb]);
       }
   };
 
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (c_begin + d < c_end) issue(d, c_begin + d);
+  for (int d = 0; d < D; ++d) issue(d, c_begin + d);
   for (int c = c_begin; c < c_end; c += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (c + d < c_end) {
-        compute(d);
-        if (c + d + D < c_end) issue(d, c + d + D);
-      }
+      if (c + d < c_end) compute(d);
+      issue(d, c + d + D);
     }
   }
+}
+
+// Runs the main loop specialised for the pass's ntb token blocks (1..TB).
+template <class SW, class SX, int TB>
+__device__ __forceinline__ void stream_pass(const typename SW::T* const (&wrow)[kTiles],
+                                            const typename SX::T* const (&xrow)[TB], int ntb,
+                                            int c_begin, int c_end, int g,
+                                            f32x4 (&acc)[kTiles][TB]) {
+  if (TB >= 4 && ntb > 2)
+    stream_mainloop<SW, SX, (TB >= 4 ? 4 : TB), TB>(wrow, xrow, c_begin, c_end, g, acc);
+  else if (TB >= 2 && ntb == 2)
+    stream_mainloop<SW, SX, (TB >= 2 ? 2 : TB), TB>(wrow, xrow, c_begin, c_end, g, acc);
+  else
+    stream_mainloop<SW, SX, 1, TB>(wrow, xrow, c_begin, c_end, g, acc);
 }
 
 struct Bucket {
@@ -106,13 +145,22 @@ struct StreamSmem {
   int dst[128];   // down: output row of each row of the pass
 };
 
+// Chunks [c_begin, c_end) of wavefront `wave`: the workgroup's slice z =
+// blockIdx.z of the gridDim.z-way split of the contraction, cut four ways.
+__device__ __forceinline__ void split_range(int nch, int wave, int& c_begin, int& c_end) {
+  const int z = blockIdx.z, nz = gridDim.z;
+  const int z0 = z * nch / nz, z1 = (z + 1) * nch / nz;
+  c_begin = z0 + wave * (z1 - z0) / kStreamWaves;
+  c_end = z0 + (wave + 1) * (z1 - z0) / kStreamWaves;
+}
+
 // Gate/up half: act[row][i] = silu(W1_e x_t)_i * (W3_e x_t)_i, bf16.
 // Tiles of the slab: 0 = gate i0..i0+15, 1 = up i0..i0+15, 2 = gate i0+16..i0+31,
 // 3 = up i0+16..i0+31.
-template <class S, int TB, int D>
-__global__ __launch_bounds__(kStreamThreads) void stream_gate_up_kernel(
+template <class S, int TB>
+__global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void stream_gate_up_kernel(
     const typename S::T* __restrict__ x, const typename S::T* __restrict__ w13, RowMap rm, int H,
-    int I, uint16_t* __restrict__ act) {
+    int I, uint16_t* __restrict__ act, float* __restrict__ part) {
   __shared__ StreamSmem sm;
   const int e = blockIdx.y;
   const Bucket bk = bucket_of(rm, e);
@@ -127,9 +175,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gate_up_kernel(
   const typename S::T* const wrow[kTiles] = {
       wexp + (size_t)(i0 + m) * H, wexp + (size_t)(I + i0 + m) * H,
       wexp + (size_t)(i0 + 16 + m) * H, wexp + (size_t)(I + i0 + 16 + m) * H};
-  const int nch = H / kChunk;
-  const int c_begin = wave * nch / kStreamWaves;
-  const int c_end = (wave + 1) * nch / kStreamWaves;
+  int c_begin, c_end;
+  split_range(H / kChunk, wave, c_begin, c_end);
 
   for (int base = 0; base < bk.n; base += 16 * TB) {
     const int n_pass = min(16 * TB, bk.n - base);
@@ -149,7 +196,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gate_up_kernel(
     for (int q = 0; q < kTiles; ++q)
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) acc[q][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_mainloop<S, S, TB, D>(wrow, xrow, ntb, c_begin, c_end, g, acc);
+    stream_pass<S, S, TB>(wrow, xrow, ntb, c_begin, c_end, g, acc);
 
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
@@ -174,7 +221,14 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gate_up_kernel(
             gs += sm.part[w][gate_r][tk];
             us += sm.part[w][up_r][tk];
           }
-          act[(size_t)(bk.row0 + base + j) * I + i0 + il] = f32_to_bf16(silu(gs) * us);
+          const size_t row = (size_t)(bk.row0 + base + j);
+          if (part) {  // split-K: raw sums, the finish kernel applies the SwiGLU
+            float* pr = part + ((size_t)blockIdx.z * rm.dense_rows + row) * (2 * (size_t)I);
+            pr[i0 + il] = gs;
+            pr[I + i0 + il] = us;
+          } else {
+            act[row * I + i0 + il] = f32_to_bf16(silu(gs) * us);
+          }
         }
       }
       __syncthreads();
@@ -184,10 +238,10 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gate_up_kernel(
 
 // Down half: y[p][h] = sum_i W2_e[h][i] act[row][i] for the valid rows of expert e,
 // written to the pair's row p = sorted_ids[row] (dense: row = token = output row).
-template <class SW, class SY, int TB, int D>
-__global__ __launch_bounds__(kStreamThreads) void stream_down_kernel(
+template <class SW, class SY, int TB>
+__global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void stream_down_kernel(
     const typename SW::T* __restrict__ w2, const uint16_t* __restrict__ act, RowMap rm, int H,
-    int I, typename SY::T* __restrict__ y) {
+    int I, typename SY::T* __restrict__ y, float* __restrict__ part) {
   __shared__ StreamSmem sm;
   const int e = blockIdx.y;
   const Bucket bk = bucket_of(rm, e);
@@ -202,9 +256,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_down_kernel(
   const typename SW::T* const wrow[kTiles] = {
       wexp + (size_t)(h0 + m) * I, wexp + (size_t)(h0 + 16 + m) * I,
       wexp + (size_t)(h0 + 32 + m) * I, wexp + (size_t)(h0 + 48 + m) * I};
-  const int nch = I / kChunk;
-  const int c_begin = wave * nch / kStreamWaves;
-  const int c_end = (wave + 1) * nch / kStreamWaves;
+  int c_begin, c_end;
+  split_range(I / kChunk, wave, c_begin, c_end);
 
   for (int base = 0; base < bk.n; base += 16 * TB) {
     const int n_pass = min(16 * TB, bk.n - base);
@@ -226,7 +279,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_down_kernel(
     for (int q = 0; q < kTiles; ++q)
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) acc[q][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_mainloop<SW, BF16, TB, D>(wrow, xrow, ntb, c_begin, c_end, g, acc);
+    stream_pass<SW, BF16, TB>(wrow, xrow, ntb, c_begin, c_end, g, acc);
 
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
@@ -246,7 +299,10 @@ __global__ __launch_bounds__(kStreamThreads) void stream_down_kernel(
           float s = 0.f;
 #pragma unroll
           for (int w = 0; w < kStreamWaves; ++w) s += sm.part[w][hl][tk];
-          store_out<SY>(y + (size_t)sm.dst[j] * H + h0 + hl, s);
+          if (part)  // split-K: raw sums, the finish kernel adds the slices
+            part[((size_t)blockIdx.z * rm.dense_rows + sm.dst[j]) * H + h0 + hl] = s;
+          else
+            store_out<SY>(y + (size_t)sm.dst[j] * H + h0 + hl, s);
         }
       }
       __syncthreads();
@@ -254,60 +310,100 @@ __global__ __launch_bounds__(kStreamThreads) void stream_down_kernel(
   }
 }
 
-// Pipeline depth by token blocks: keeps the register ring within budget.
-template <int TB>
-constexpr int depth_bf16() { return TB <= 1 ? 4 : TB == 2 ? 3 : 2; }
+// Split-K finish (dense rows only): sums the gridDim.z slices in slice order.
+__global__ __launch_bounds__(256) void finish_gate_up_kernel(const float* __restrict__ part,
+                                                             int splits, int64_t rows, int I,
+                                                             uint16_t* __restrict__ act) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * I) return;
+  const int64_t r = idx / I;
+  const int i = (int)(idx % I);
+  float g = 0.f, u = 0.f;
+  for (int z = 0; z < splits; ++z) {
+    const float* pr = part + ((size_t)z * rows + r) * (2 * (size_t)I);
+    g += pr[i];
+    u += pr[I + i];
+  }
+  act[r * I + i] = f32_to_bf16(silu(g) * u);
+}
+
+template <class SY>
+__global__ __launch_bounds__(256) void finish_down_kernel(const float* __restrict__ part,
+                                                          int splits, int64_t rows, int H,
+                                                          typename SY::T* __restrict__ y) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * H) return;
+  float s = 0.f;
+  for (int z = 0; z < splits; ++z) s += part[(size_t)z * rows * H + idx];
+  store_out<SY>(y + idx, s);
+}
 
 template <class S, int TB>
 static void launch_gu(const void* x, const void* w13, const RowMap& rm, int E, int H, int I,
-                      uint16_t* act, hipStream_t s) {
-  constexpr int D = std::is_same<S, F32>::value ? 1 : depth_bf16<TB>();
-  hipLaunchKernelGGL((stream_gate_up_kernel<S, TB, D>), dim3(I / 32, E), dim3(kStreamThreads), 0,
-                     s, static_cast<const typename S::T*>(x),
-                     static_cast<const typename S::T*>(w13), rm, H, I, act);
+                      int splits, uint16_t* act, float* part, hipStream_t s) {
+  hipLaunchKernelGGL((stream_gate_up_kernel<S, TB>), dim3(I / 32, E, splits), dim3(kStreamThreads),
+                     0, s, static_cast<const typename S::T*>(x),
+                     static_cast<const typename S::T*>(w13), rm, H, I, act, part);
 }
 
 template <class SW, class SY, int TB>
 static void launch_dn(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H, int I,
-                      void* y, hipStream_t s) {
-  constexpr int D = std::is_same<SW, F32>::value ? 1 : depth_bf16<TB>();
-  hipLaunchKernelGGL((stream_down_kernel<SW, SY, TB, D>), dim3(H / 64, E), dim3(kStreamThreads),
-                     0, s, static_cast<const typename SW::T*>(w2), act, rm, H, I,
-                     static_cast<typename SY::T*>(y));
+                      int splits, void* y, float* part, hipStream_t s) {
+  hipLaunchKernelGGL((stream_down_kernel<SW, SY, TB>), dim3(H / 64, E, splits),
+                     dim3(kStreamThreads), 0, s, static_cast<const typename SW::T*>(w2), act, rm,
+                     H, I, static_cast<typename SY::T*>(y), part);
 }
 
 template <class S>
 static void gu_tb(const void* x, const void* w13, const RowMap& rm, int E, int H, int I, int tb,
-                  uint16_t* act, hipStream_t s) {
-  if (tb <= 1) launch_gu<S, 1>(x, w13, rm, E, H, I, act, s);
-  else if (tb == 2) launch_gu<S, 2>(x, w13, rm, E, H, I, act, s);
-  else launch_gu<S, 4>(x, w13, rm, E, H, I, act, s);
+                  int splits, uint16_t* act, float* part, hipStream_t s) {
+  if (tb <= 1) launch_gu<S, 1>(x, w13, rm, E, H, I, splits, act, part, s);
+  else if (tb == 2) launch_gu<S, 2>(x, w13, rm, E, H, I, splits, act, part, s);
+  else launch_gu<S, 4>(x, w13, rm, E, H, I, splits, act, part, s);
 }
 
 template <class SW, class SY>
 static void dn_tb(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H, int I,
-                  int tb, void* y, hipStream_t s) {
-  if (tb <= 1) launch_dn<SW, SY, 1>(w2, act, rm, E, H, I, y, s);
-  else if (tb == 2) launch_dn<SW, SY, 2>(w2, act, rm, E, H, I, y, s);
-  else launch_dn<SW, SY, 4>(w2, act, rm, E, H, I, y, s);
+                  int tb, int splits, void* y, float* part, hipStream_t s) {
+  if (tb <= 1) launch_dn<SW, SY, 1>(w2, act, rm, E, H, I, splits, y, part, s);
+  else if (tb == 2) launch_dn<SW, SY, 2>(w2, act, rm, E, H, I, splits, y, part, s);
+  else launch_dn<SW, SY, 4>(w2, act, rm, E, H, I, splits, y, part, s);
 }
 
 hipError_t launch_stream_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm, int E,
-                                 int H, int I, int tok_blocks, uint16_t* act, hipStream_t s) {
-  if (xdt == kDtF32) gu_tb<F32>(x, w13, rm, E, H, I, tok_blocks, act, s);
-  else gu_tb<BF16>(x, w13, rm, E, H, I, tok_blocks, act, s);
+                                 int H, int I, int tok_blocks, int splits, uint16_t* act,
+                                 float* part, hipStream_t s) {
+  float* p = splits > 1 ? part : nullptr;
+  if (xdt == kDtF32) gu_tb<F32>(x, w13, rm, E, H, I, tok_blocks, splits, act, p, s);
+  else gu_tb<BF16>(x, w13, rm, E, H, I, tok_blocks, splits, act, p, s);
+  if (splits > 1) {
+    const int64_t n = rm.dense_rows * I;
+    hipLaunchKernelGGL(finish_gate_up_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       part, splits, rm.dense_rows, I, act);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
-                              int E, int H, int I, int tok_blocks, void* y, int ydt,
-                              hipStream_t s) {
+                              int E, int H, int I, int tok_blocks, int splits, void* y, int ydt,
+                              float* part, hipStream_t s) {
+  float* p = splits > 1 ? part : nullptr;
   if (wdt == kDtF32) {
-    if (ydt == kDtF32) dn_tb<F32, F32>(w2, act, rm, E, H, I, tok_blocks, y, s);
-    else dn_tb<F32, BF16>(w2, act, rm, E, H, I, tok_blocks, y, s);
+    if (ydt == kDtF32) dn_tb<F32, F32>(w2, act, rm, E, H, I, tok_blocks, splits, y, p, s);
+    else dn_tb<F32, BF16>(w2, act, rm, E, H, I, tok_blocks, splits, y, p, s);
   } else {
-    if (ydt == kDtF32) dn_tb<BF16, F32>(w2, act, rm, E, H, I, tok_blocks, y, s);
-    else dn_tb<BF16, BF16>(w2, act, rm, E, H, I, tok_blocks, y, s);
+    if (ydt == kDtF32) dn_tb<BF16, F32>(w2, act, rm, E, H, I, tok_blocks, splits, y, p, s);
+    else dn_tb<BF16, BF16>(w2, act, rm, E, H, I, tok_blocks, splits, y, p, s);
+  }
+  if (splits > 1) {
+    const int64_t n = rm.dense_rows * H;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (ydt == kDtF32)
+      hipLaunchKernelGGL(finish_down_kernel<F32>, dim3(blocks), dim3(256), 0, s, part, splits,
+                         rm.dense_rows, H, static_cast<float*>(y));
+    else
+      hipLaunchKernelGGL(finish_down_kernel<BF16>, dim3(blocks), dim3(256), 0, s, part, splits,
+                         rm.dense_rows, H, static_cast<uint16_t*>(y));
   }
   return hipGetLastError();
 }

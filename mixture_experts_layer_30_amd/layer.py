@@ -38,11 +38,11 @@ class MoELayer:
         self.has_shared = inputs.get("ws13") is not None
         if self.has_shared:
             self.shared_out = torch.empty(T, H, dtype=torch.float32, device=dev)
-            self.shared_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, shape.shared_inter), 16),
+            self.shared_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, H, shape.shared_inter), 16),
                                          dtype=torch.uint8, device=dev)
         if inputs.get("wfa13") is not None:
             self.fa_out = torch.empty(T, H, dtype=out_dtype or x.dtype, device=dev)
-            self.fa_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, shape.dense_fa_inter), 16),
+            self.fa_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, H, shape.dense_fa_inter), 16),
                                      dtype=torch.uint8, device=dev)
 
     # the five steps, callable one by one (the benchmark times them separately)

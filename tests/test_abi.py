@@ -50,7 +50,9 @@ def test_align_capacity_bound(L):
     assert B.moe_align_capacity(0, 2, 8, 16) == 0
     assert B.moe_align_capacity(-1, 2, 8, 16) == -1
     assert B.moe_ffn_workspace_bytes(4864, 2048) == 4864 * 2048 * 2
-    assert B.dense_ffn_workspace_bytes(1, 512) == 128 * 512 * 2
+    # activations (128-row rounded) plus split-K partial sums
+    assert B.dense_ffn_workspace_bytes(1, 128, 512) >= 128 * 512 * 2
+    assert B.dense_ffn_workspace_bytes(1, 100, 512) == -1
 
 
 def st(r):
@@ -114,7 +116,7 @@ def test_combine_and_dense_argument_checks(L):
                             None)) == B.MOE_EINVAL
     assert st(L.moe_combine(FAKE, B.MOE_BF16, FAKE, FAKE + 4, B.MOE_F32, 4, 2, 128, FAKE,
                             B.MOE_BF16, None)) == B.MOE_EINVAL
-    ws = B.dense_ffn_workspace_bytes(32, 28672)
+    ws = B.dense_ffn_workspace_bytes(32, 4096, 28672)
     assert st(L.dense_ffn_fa(FAKE, B.MOE_BF16, 32, 4096, 28672, FAKE, FAKE, FAKE, ws - 2, FAKE,
                              B.MOE_BF16, 0, None)) == B.MOE_ECAPACITY
     assert st(L.dense_ffn_fa(FAKE, B.MOE_BF16, 32, 4096, 28600, FAKE, FAKE, FAKE, ws, FAKE,

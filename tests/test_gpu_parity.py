@@ -191,7 +191,7 @@ def test_dense_ffn_parity(T, H, I, dt, odt):
     w13, w2 = synth.swiglu_weights(I, H, dt, seed=T)
     ref = oracle.swiglu(x, w13, w2)
     out = torch.empty(T, H, dtype=odt, device=DEV)
-    ws = torch.empty(B.dense_ffn_workspace_bytes(T, I), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(T, H, I), dtype=torch.uint8, device=DEV)
     B.dense_ffn_fa(x.to(DEV), w13.to(DEV), w2.to(DEV), ws, out)
     torch.cuda.synchronize()
     assert rel_err(out, ref) <= TOL
@@ -211,7 +211,7 @@ def test_dense_unit_vector_case():
     w2 = torch.zeros(H, I)
     w2[:4, :2] = torch.tensor([[1.0, 0], [0, 1], [1, 1], [2, -1]])
     out = torch.empty(1, H, device=DEV)
-    ws = torch.empty(B.dense_ffn_workspace_bytes(1, I), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(1, H, I), dtype=torch.uint8, device=DEV)
     B.dense_ffn_fa(x.to(DEV), w13.to(DEV), w2.to(DEV), ws, out)
     torch.cuda.synchronize()
     ref = oracle.swiglu(x, w13, w2)
