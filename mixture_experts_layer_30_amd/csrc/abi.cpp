@@ -111,10 +111,28 @@ DensePlan dense_plan(int64_t T, int H, int I) {
   return p;
 }
 
-moe_schedule pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m) {
-  (void)T; (void)K; (void)E; (void)block_m;
-  if (req == MOE_SCHED_TILE) return MOE_SCHED_TILE;
-  return MOE_SCHED_STREAM;
+// The tiled schedule needs tiles that hold one expert's rows (block 64 or 128)
+// and 128-row output tiles of the down projection (H a multiple of 128).  Auto
+// picks it once an expert holds a tile's worth of tokens on average (the MFMA-
+// bound regime); below that the weight-streaming schedule, which reads every
+// active expert's weights once, is faster.
+bool tile_ok(int block_m, int H) { return (block_m == 64 || block_m == 128) && H % 128 == 0; }
+
+moe_status pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m, int H,
+                         moe_schedule* out) {
+  if (req == MOE_SCHED_TILE) {
+    if (!tile_ok(block_m, H))
+      return fail(MOE_EUNSUPPORTED, "tile schedule needs block_m 64 or 128 and H %% 128 == 0 "
+                  "(block_m = %d, H = %d)", block_m, H);
+    *out = MOE_SCHED_TILE;
+  } else if (req == MOE_SCHED_STREAM) {
+    *out = MOE_SCHED_STREAM;
+  } else if (req == MOE_SCHED_AUTO) {
+    *out = (tile_ok(block_m, H) && T * K >= 64 * (int64_t)E) ? MOE_SCHED_TILE : MOE_SCHED_STREAM;
+  } else {
+    return fail(MOE_EINVAL, "schedule %d", (int)req);
+  }
+  return MOE_OK;
 }
 
 }  // namespace
@@ -215,13 +233,18 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
   if (T == 0) return ok();
   if (!x || !w13 || !workspace || !aligned(x, 16) || !aligned(w13, 16) || !aligned(workspace, 16))
     return fail(MOE_EINVAL, "moe_grouped_gate_up: NULL or misaligned pointer");
+  moe_schedule use;
+  st = pick_schedule(sched, T, K, E, plan->block_m, H, &use);
+  if (st) return st;
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (pick_schedule(sched, T, K, E, plan->block_m) == MOE_SCHED_TILE)
-    return fail(MOE_EUNSUPPORTED, "tile schedule not available");
-  e = moe::launch_stream_gate_up(x, dt, w13, rm, E, H, I, stream_tok_blocks(T), 1,
-                                 (uint16_t*)workspace, nullptr, s);
+  if (use == MOE_SCHED_TILE)
+    e = moe::launch_tile_gate_up(x, dt, w13, rm, plan->cap / plan->block_m, H, I,
+                                 (uint16_t*)workspace, s);
+  else
+    e = moe::launch_stream_gate_up(x, dt, w13, rm, E, H, I, stream_tok_blocks(T), 1,
+                                   (uint16_t*)workspace, nullptr, s);
   return hip_status(e, "moe_grouped_gate_up");
 }
 
@@ -234,12 +257,18 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   if (!w2 || !workspace || !y_pairs || !aligned(w2, 16) || !aligned(workspace, 16) ||
       !aligned(y_pairs, 16))
     return fail(MOE_EINVAL, "moe_grouped_down: NULL or misaligned pointer");
+  moe_schedule use;
+  st = pick_schedule(sched, T, K, E, plan->block_m, H, &use);
+  if (st) return st;
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
-  if (pick_schedule(sched, T, K, E, plan->block_m) == MOE_SCHED_TILE)
-    return fail(MOE_EUNSUPPORTED, "tile schedule not available");
-  hipError_t e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, E, H, I,
-                                         stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
+  hipError_t e;
+  if (use == MOE_SCHED_TILE)
+    e = moe::launch_tile_down(w2, dt, (const uint16_t*)workspace, rm, plan->cap / plan->block_m,
+                              H, I, y_pairs, dt, s);
+  else
+    e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, E, H, I,
+                                stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
   return hip_status(e, "moe_grouped_down");
 }
 
@@ -291,7 +320,21 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   rm.dense_rows = T;
   rm.block_m = 128;
   hipStream_t s = (hipStream_t)stream;
-  if (sched == MOE_SCHED_TILE) return fail(MOE_EUNSUPPORTED, "tile schedule not available");
+  // dense rows form one expert; the tiled schedule takes them in 128-row blocks
+  // and is chosen from two blocks up (with a single block its down projection
+  // has only H/128 workgroups; the split-K streaming schedule does better)
+  moe_schedule use;
+  st = pick_schedule(sched, T, 1, 1, 128, H, &use);
+  if (st) return st;
+  if (sched == MOE_SCHED_AUTO && T < 256) use = MOE_SCHED_STREAM;
+  if (use == MOE_SCHED_TILE) {
+    uint16_t* act = (uint16_t*)workspace;
+    const int64_t nblocks = (T + 127) / 128;
+    hipError_t e = moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s);
+    if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
+    e = moe::launch_tile_down(w2, dt, act, rm, nblocks, H, I_fa, out, odt, s);
+    return hip_status(e, "dense_ffn_fa down");
+  }
   const DensePlan dp = dense_plan(T, H, I_fa);
   uint16_t* act = (uint16_t*)workspace;
   float* part = (float*)((char*)workspace + dp.act_bytes);

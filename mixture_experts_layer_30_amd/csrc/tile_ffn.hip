@@ -1,0 +1,470 @@
+// LDS-tiled grouped SwiGLU FFN on gfx950 (the MFMA-bound, prefill-shape
+// schedule).
+//
+// In prefill each expert holds hundreds of tokens, and the grouped GEMM is
+// bound by matrix-core throughput reduced by the per-expert split of the
+// batch and by block padding (Serving-tax notes, Table 1 rows "GroupGEMM" and
+// "padding"; the TEMPO page's grouped GEMM rounds the token dimension to
+// 128-row tiles).  One workgroup computes a tile of 128 weight rows x one
+// alignment block of BN tokens (BN = the plan's block, 64 or 128; every block
+// belongs to one expert), over the whole contraction in steps of 64:
+//
+//   * weights (MFMA A, M = weight rows) and token rows (MFMA B, N = tokens,
+//     gathered through the alignment for the gate/up half) go from HBM to
+//     registers to LDS, double-buffered, one barrier per step; the next
+//     step's global loads are in flight while the current one is multiplied;
+//   * LDS rows are padded by 16 bytes, so the 16 rows one fragment read
+//     touches fall in distinct banks;
+//   * 4 wavefronts in 2 x 2, each 64 x BN/2 with 16x16x32 bf16 MFMAs;
+//   * gate/up half: the tile's 16-row groups alternate gate and up rows of
+//     the same intermediate columns, so each lane holds matching gate and up
+//     sums and applies the SwiGLU in registers; down half: the rows are 128
+//     output features and results go straight to the pair's output row.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kTileThreads = 256;
+constexpr int kBM = 128;            // weight rows per workgroup
+constexpr int kBK = 64;             // contraction per step
+constexpr int kLdsRow = kBK + 8;    // bf16 elements per LDS row (16-byte pad)
+
+template <int BN>
+struct TileSmem {
+  uint16_t a[2][kBM * kLdsRow];
+  uint16_t b[2][BN * kLdsRow];
+  int tok[BN];
+  int dst[BN];
+};
+
+// kGateUp: A rows are pair-interleaved gate/up rows of w13[e]; B rows are x
+// rows of the block's tokens.  Otherwise A rows are w2[e] rows h0.., B rows
+// are the block's activation rows.
+template <class SW, class SX, class SY, int BN, bool kGateUp>
+__global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
+    const typename SW::T* __restrict__ w, const typename SX::T* __restrict__ xs, RowMap rm,
+    int H, int I, uint16_t* __restrict__ act, typename SY::T* __restrict__ y) {
+  __shared__ TileSmem<BN> sm;
+  constexpr int TN = BN / 2 / 16;   // 16-token tiles per wavefront
+  const int blk = blockIdx.y;
+  const bool dense = rm.counts == nullptr;
+  int e, row0, nvalid;
+  if (dense) {
+    e = 0;
+    row0 = blk * BN;
+    nvalid = min(BN, (int)(rm.dense_rows - row0));
+  } else {
+    e = rm.block_expert[blk];
+    if (e < 0) return;  // past the padded total
+    row0 = blk * BN;
+    nvalid = min(BN, rm.offsets[e] + rm.counts[e] - row0);
+  }
+  const int Kdim = kGateUp ? H : I;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m = lane & 15, g = lane >> 4;
+
+  // rows of the block: token (gate/up) or activation row (down), and output row
+  for (int j = tid; j < BN; j += kTileThreads) {
+    const int jj = j < nvalid ? j : 0;  // rows past the bucket reuse its first row
+    const int row = row0 + jj;
+    if (kGateUp) {
+      sm.tok[j] = dense ? row : rm.sorted_ids[row] / rm.K;
+    } else {
+      sm.tok[j] = row;
+      sm.dst[j] = dense ? row : rm.sorted_ids[row];
+    }
+  }
+  __syncthreads();
+
+  // this thread's 16-byte pieces of each step: rows (tid/8) + 32*j, segment tid%8
+  constexpr int APieces = kBM * kBK / 8 / kTileThreads;   // 4
+  constexpr int BPieces = BN * kBK / 8 / kTileThreads;    // 4 or 2
+  const int seg = tid & 7;
+  const typename SW::T* arow[APieces];
+  const int i0 = blockIdx.x * (kGateUp ? 64 : kBM);
+  const typename SW::T* wexp = w + (size_t)e * (kGateUp ? 2 * (size_t)I * H : (size_t)H * I);
+#pragma unroll
+  for (int j = 0; j < APieces; ++j) {
+    const int r = tid / 8 + 32 * j;
+    size_t wr;
+    if (kGateUp) {
+      const int q = r >> 4;                       // 16-row group: even = gate, odd = up
+      const int i = i0 + 16 * (q >> 1) + (r & 15);
+      wr = (q & 1) ? (size_t)(I + i) : (size_t)i;
+    } else {
+      wr = (size_t)(i0 + r);
+    }
+    arow[j] = wexp + wr * Kdim + seg * 8;
+  }
+  const typename SX::T* brow[BPieces];
+#pragma unroll
+  for (int j = 0; j < BPieces; ++j) {
+    const int r = tid / 8 + 32 * j;
+    brow[j] = xs + (size_t)sm.tok[r] * Kdim + seg * 8;
+  }
+
+  u32x4 ra[APieces], rb[BPieces];
+  auto gload = [&](int ks) {
+    const int k = ks * kBK;
+#pragma unroll
+    for (int j = 0; j < APieces; ++j) ra[j] = load8<SW>(arow[j] + k);
+#pragma unroll
+    for (int j = 0; j < BPieces; ++j) rb[j] = load8<SX>(brow[j] + k);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < APieces; ++j)
+      *reinterpret_cast<u32x4*>(&sm.a[buf][(tid / 8 + 32 * j) * kLdsRow + seg * 8]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < BPieces; ++j)
+      *reinterpret_cast<u32x4*>(&sm.b[buf][(tid / 8 + 32 * j) * kLdsRow + seg * 8]) = rb[j];
+  };
+
+  f32x4 acc[4][TN];
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = Kdim / kBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) gload(ks + 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 fa[4], fb[TN];
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+        fa[tm] = *reinterpret_cast<const u32x4*>(
+            &sm.a[buf][(wm * 64 + tm * 16 + m) * kLdsRow + s * 32 + g * 8]);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        fb[tn] = *reinterpret_cast<const u32x4*>(
+            &sm.b[buf][(wn * (BN / 2) + tn * 16 + m) * kLdsRow + s * 32 + g * 8]);
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(fa[tm], fb[tn], acc[tm][tn]);
+    }
+    if (ks + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 4g..4g+3 of each 16-row tile, for token column m of each tile
+  if (kGateUp) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int j = wn * (BN / 2) + tn * 16 + m;
+        if (j < nvalid) {
+          const f32x4 gs = acc[2 * p][tn], us = acc[2 * p + 1][tn];
+          const int i = i0 + 16 * (wm * 2 + p) + 4 * g;
+          uint2 v;
+          v.x = pack_bf16x2(silu(gs.x) * us.x, silu(gs.y) * us.y);
+          v.y = pack_bf16x2(silu(gs.z) * us.z, silu(gs.w) * us.w);
+          *reinterpret_cast<uint2*>(act + (size_t)(row0 + j) * I + i) = v;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int j = wn * (BN / 2) + tn * 16 + m;
+        if (j < nvalid) {
+          const int h = i0 + wm * 64 + tm * 16 + 4 * g;
+          typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
+          const f32x4 v = acc[tm][tn];
+          store_out<SY>(o + 0, v.x);
+          store_out<SY>(o + 1, v.y);
+          store_out<SY>(o + 2, v.z);
+          store_out<SY>(o + 3, v.w);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Second-generation tile for bf16 storage: 8 wavefronts, 256 weight rows x BN
+// tokens per workgroup, and a 3-stage LDS ring filled by direct global->LDS
+// loads (global_load_lds_dwordx4), so two steps of loads are in flight while
+// one is multiplied without spending registers on staging.  A direct load
+// writes its 64 lanes' 16 bytes contiguously, so instead of padding, the
+// 16-byte segments of each 128-byte LDS row are permuted (XOR with a
+// function of the row): the 16 rows one fragment read touches then fall in
+// distinct banks.
+
+constexpr int kT2Threads = 512;
+constexpr int kT2Waves = kT2Threads / kWave;
+constexpr int kT2BM = 256;
+constexpr int kT2Stages = 3;
+constexpr int kRowBytes = kBK * 2;   // 128 bytes of one row per step
+
+template <int BN>
+struct Tile2Smem {
+  uint8_t a[kT2Stages][kT2BM * kRowBytes];
+  uint8_t b[kT2Stages][BN * kRowBytes];
+  int tok[BN];
+  int dst[BN];
+};
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// byte offset of (row, 16-byte segment) inside a stage buffer
+__device__ __forceinline__ int lds_off(int row, int seg) {
+  return row * kRowBytes + ((seg ^ swz(row)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void lds_direct16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+
+// Workgroup barrier without the memory fence __syncthreads() adds (which would
+// wait for every load in flight, draining the LDS ring).  The "memory" clobber
+// keeps the compiler from moving LDS accesses across it; the loads a wave
+// needs are waited for explicitly with wait_vmcnt before it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <class SY, int BN, bool kGateUp>
+__global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
+    uint16_t* __restrict__ act, typename SY::T* __restrict__ y) {
+  __shared__ Tile2Smem<BN> sm;
+  constexpr int TN = BN / 2 / 16;                         // token tiles per wavefront
+  constexpr int AInst = kT2BM * kRowBytes / 1024 / kT2Waves;  // 4 direct loads per wave
+  constexpr int BInst = BN * kRowBytes / 1024 / kT2Waves;     // 2 (BN 128) or 1 (BN 64)
+  constexpr int kLoads = AInst + BInst;
+  const int blk = blockIdx.y;
+  const bool dense = rm.counts == nullptr;
+  int e, row0, nvalid;
+  if (dense) {
+    e = 0;
+    row0 = blk * BN;
+    nvalid = min(BN, (int)(rm.dense_rows - row0));
+  } else {
+    e = rm.block_expert[blk];
+    if (e < 0) return;
+    row0 = blk * BN;
+    nvalid = min(BN, rm.offsets[e] + rm.counts[e] - row0);
+  }
+  const int Kdim = kGateUp ? H : I;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m = lane & 15, g = lane >> 4;
+
+  for (int j = tid; j < BN; j += kT2Threads) {
+    const int jj = j < nvalid ? j : 0;
+    const int row = row0 + jj;
+    if (kGateUp) {
+      sm.tok[j] = dense ? row : rm.sorted_ids[row] / rm.K;
+    } else {
+      sm.tok[j] = row;
+      sm.dst[j] = dense ? row : rm.sorted_ids[row];
+    }
+  }
+  __syncthreads();
+
+  // Direct loads: instruction i of a stage fills LDS rows 8i..8i+7; lane l
+  // fills row 8i + l/8, slot l%8, which holds global segment (l%8) ^ swz(row).
+  const int i0 = blockIdx.x * (kGateUp ? kT2BM / 2 : kT2BM);
+  const uint16_t* wexp = w + (size_t)e * (kGateUp ? 2 * (size_t)I * H : (size_t)H * I);
+  const uint8_t* asrc[AInst];
+#pragma unroll
+  for (int j = 0; j < AInst; ++j) {
+    const int r = 8 * (wave * AInst + j) + lane / 8;
+    size_t wr;
+    if (kGateUp) {
+      const int q = r >> 4;
+      const int i = i0 + 16 * (q >> 1) + (r & 15);
+      wr = (q & 1) ? (size_t)(I + i) : (size_t)i;
+    } else {
+      wr = (size_t)(i0 + r);
+    }
+    asrc[j] = reinterpret_cast<const uint8_t*>(wexp + wr * Kdim) + (((lane & 7) ^ swz(r)) << 4);
+  }
+  const uint8_t* bsrc[BInst];
+#pragma unroll
+  for (int j = 0; j < BInst; ++j) {
+    const int r = 8 * (wave * BInst + j) + lane / 8;
+    bsrc[j] = reinterpret_cast<const uint8_t*>(xs + (size_t)sm.tok[r] * Kdim) +
+              (((lane & 7) ^ swz(r)) << 4);
+  }
+
+  auto issue = [&](int ks) {
+    const int st = ks % kT2Stages;
+    const size_t kb = (size_t)ks * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < AInst; ++j)
+      lds_direct16(asrc[j] + kb, &sm.a[st][(wave * AInst + j) * 1024]);
+#pragma unroll
+    for (int j = 0; j < BInst; ++j)
+      lds_direct16(bsrc[j] + kb, &sm.b[st][(wave * BInst + j) * 1024]);
+  };
+
+  f32x4 acc[4][TN];
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = Kdim / kBK;
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) wait_vmcnt<kLoads>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
+    if (ks + 2 < nk) issue(ks + 2);
+    const uint8_t* A = sm.a[ks % kT2Stages];
+    const uint8_t* Bt = sm.b[ks % kT2Stages];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 fa[4], fb[TN];
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+        fa[tm] = *reinterpret_cast<const u32x4*>(A + lds_off(wm * 64 + tm * 16 + m, s2 * 4 + g));
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        fb[tn] = *reinterpret_cast<const u32x4*>(
+            Bt + lds_off(wn * (BN / 2) + tn * 16 + m, s2 * 4 + g));
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(fa[tm], fb[tn], acc[tm][tn]);
+    }
+  }
+
+  if (kGateUp) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int j = wn * (BN / 2) + tn * 16 + m;
+        if (j < nvalid) {
+          const f32x4 gs = acc[2 * p][tn], us = acc[2 * p + 1][tn];
+          const int i = i0 + 16 * (wm * 2 + p) + 4 * g;
+          uint2 v;
+          v.x = pack_bf16x2(silu(gs.x) * us.x, silu(gs.y) * us.y);
+          v.y = pack_bf16x2(silu(gs.z) * us.z, silu(gs.w) * us.w);
+          *reinterpret_cast<uint2*>(act + (size_t)(row0 + j) * I + i) = v;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int j = wn * (BN / 2) + tn * 16 + m;
+        if (j < nvalid) {
+          const int h = i0 + wm * 64 + tm * 16 + 4 * g;
+          typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
+          const f32x4 v = acc[tm][tn];
+          store_out<SY>(o + 0, v.x);
+          store_out<SY>(o + 1, v.y);
+          store_out<SY>(o + 2, v.z);
+          store_out<SY>(o + 3, v.w);
+        }
+      }
+  }
+}
+
+template <class S, int BN>
+static void gu_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
+                      int I, uint16_t* act, hipStream_t s) {
+  hipLaunchKernelGGL((tile_ffn_kernel<S, S, BF16, BN, true>), dim3(I / 64, (unsigned)nblocks),
+                     dim3(kTileThreads), 0, s, static_cast<const typename S::T*>(w13),
+                     static_cast<const typename S::T*>(x), rm, H, I, act, (uint16_t*)nullptr);
+}
+
+template <class SW, class SY, int BN>
+static void dn_launch(const void* w2, const uint16_t* act, const RowMap& rm, int64_t nblocks,
+                      int H, int I, void* y, hipStream_t s) {
+  hipLaunchKernelGGL((tile_ffn_kernel<SW, BF16, SY, BN, false>), dim3(H / kBM, (unsigned)nblocks),
+                     dim3(kTileThreads), 0, s, static_cast<const typename SW::T*>(w2), act, rm, H,
+                     I, (uint16_t*)nullptr, static_cast<typename SY::T*>(y));
+}
+
+template <int BN>
+static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
+                       int I, uint16_t* act, hipStream_t s) {
+  hipLaunchKernelGGL((tile2_ffn_kernel<BF16, BN, true>), dim3(I / (kT2BM / 2), (unsigned)nblocks),
+                     dim3(kT2Threads), 0, s, static_cast<const uint16_t*>(w13),
+                     static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr);
+}
+
+template <class SY, int BN>
+static void dn2_launch(const void* w2, const uint16_t* act, const RowMap& rm, int64_t nblocks,
+                       int H, int I, void* y, hipStream_t s) {
+  hipLaunchKernelGGL((tile2_ffn_kernel<SY, BN, false>), dim3(H / kT2BM, (unsigned)nblocks),
+                     dim3(kT2Threads), 0, s, static_cast<const uint16_t*>(w2), act, rm, H, I,
+                     (uint16_t*)nullptr, static_cast<typename SY::T*>(y));
+}
+
+hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
+                               int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s) {
+  if (xdt == kDtBF16 && I % (kT2BM / 2) == 0) {
+    if (rm.block_m == 64) gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s);
+    else gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s);
+    return hipGetLastError();
+  }
+  if (rm.block_m == 64) {
+    if (xdt == kDtF32) gu_launch<F32, 64>(x, w13, rm, nblocks, H, I, act, s);
+    else gu_launch<BF16, 64>(x, w13, rm, nblocks, H, I, act, s);
+  } else {
+    if (xdt == kDtF32) gu_launch<F32, 128>(x, w13, rm, nblocks, H, I, act, s);
+    else gu_launch<BF16, 128>(x, w13, rm, nblocks, H, I, act, s);
+  }
+  return hipGetLastError();
+}
+
+template <class SW, int BN>
+static void dn_by_out(const void* w2, const uint16_t* act, const RowMap& rm, int64_t nblocks,
+                      int H, int I, void* y, int ydt, hipStream_t s) {
+  if (ydt == kDtF32) dn_launch<SW, F32, BN>(w2, act, rm, nblocks, H, I, y, s);
+  else dn_launch<SW, BF16, BN>(w2, act, rm, nblocks, H, I, y, s);
+}
+
+hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
+                            int64_t nblocks, int H, int I, void* y, int ydt, hipStream_t s) {
+  if (wdt == kDtBF16 && H % kT2BM == 0) {
+    if (rm.block_m == 64) {
+      if (ydt == kDtF32) dn2_launch<F32, 64>(w2, act, rm, nblocks, H, I, y, s);
+      else dn2_launch<BF16, 64>(w2, act, rm, nblocks, H, I, y, s);
+    } else {
+      if (ydt == kDtF32) dn2_launch<F32, 128>(w2, act, rm, nblocks, H, I, y, s);
+      else dn2_launch<BF16, 128>(w2, act, rm, nblocks, H, I, y, s);
+    }
+    return hipGetLastError();
+  }
+  if (rm.block_m == 64) {
+    if (wdt == kDtF32) dn_by_out<F32, 64>(w2, act, rm, nblocks, H, I, y, ydt, s);
+    else dn_by_out<BF16, 64>(w2, act, rm, nblocks, H, I, y, ydt, s);
+  } else {
+    if (wdt == kDtF32) dn_by_out<F32, 128>(w2, act, rm, nblocks, H, I, y, ydt, s);
+    else dn_by_out<BF16, 128>(w2, act, rm, nblocks, H, I, y, ydt, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -257,6 +257,45 @@ def test_layer_parity_small(shape, T, routing, block_m):
     assert torch.equal(out, out2)
 
 
+TILE_SHAPES = [
+    (LayerShape("tile_tiny", 128, 256, 8, 2, 0, "f32", (300,), ("uniform",)), 300, "uniform", 128),
+    (LayerShape("tile_bf16", 256, 320, 8, 2, 192, "bf16", (500,), ("zipf",)), 500, "zipf", 128),
+    (LayerShape("tile_b64", 384, 192, 16, 4, 0, "bf16", (260,), ("uniform",)), 260, "uniform", 64),
+    (LayerShape("tile_sparse", 128, 128, 64, 8, 0, "bf16", (20,), ("uniform",)), 20, "uniform", 128),
+    # the 256-row direct-to-LDS tile (bf16, I % 128 == 0, H % 256 == 0)
+    (LayerShape("tile2_b128", 512, 384, 8, 2, 256, "bf16", (700,), ("zipf",)), 700, "zipf", 128),
+    (LayerShape("tile2_b64", 256, 256, 16, 4, 0, "bf16", (300,), ("uniform",)), 300, "uniform", 64),
+    (LayerShape("tile2_short_k", 256, 128, 4, 1, 0, "bf16", (129,), ("uniform",)), 129, "uniform", 128),
+]
+
+
+@pytest.mark.parametrize("shape,T,routing,block_m", TILE_SHAPES, ids=[s[0].name for s in TILE_SHAPES])
+@pytest.mark.parametrize("sched", [B.SCHED_TILE, B.SCHED_STREAM])
+def test_layer_parity_forced_schedule(shape, T, routing, block_m, sched):
+    """Both grouped-GEMM schedules on the same inputs, including blocks with a
+    ragged tail and (tile_sparse) experts whose single block is mostly padding."""
+    d, dev = layer_case(shape, T, routing, seed=3)
+    layer = MoELayer(shape, dev, block_m=block_m, sched=sched)
+    out = layer.forward().clone()
+    fa = layer.dense_fa().clone()
+    torch.cuda.synchronize()
+    ref, rids, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], shape.topk,
+                                    d["ws13"], d["ws2"])
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    assert rel_err(out, ref) <= TOL
+    assert rel_err(fa, oracle.dense_ffn(d["x"], d["wfa13"], d["wfa2"])) <= TOL
+
+
+def test_tile_schedule_rejects_unsupported_block():
+    shape = TILE_SHAPES[1][0]
+    d, dev = layer_case(shape, 40, "zipf")
+    layer = MoELayer(shape, dev, block_m=16, sched=B.SCHED_TILE)
+    layer.route()
+    layer.align()
+    with pytest.raises(B.MoEError):
+        layer.gate_up()
+
+
 def test_layer_on_a_side_stream():
     shape = SMALL_SHAPES[1][0]
     d, dev = layer_case(shape, 70, "zipf", seed=5)
