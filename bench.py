@@ -241,6 +241,42 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
     return rec
 
 
+def run_only(name, T, routing, what, steps):
+    """Runs one piece of the pass `steps` times with nothing else on the GPU in
+    between (for hardware-counter runs of a single kernel)."""
+    if what == "copy":
+        # a plain device copy of known size, to calibrate the byte counters
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "steps": steps}))
+        return
+    shape = configs.CONFIGS[name]
+    d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=(what == "dense_fa"))
+    layer = MoELayer(shape, d)
+    layer.route()
+    layer.align()
+    layer.gate_up()
+    torch.cuda.synchronize()
+    ids = layer.topk_ids.cpu().numpy()
+    e_active = int(len(np.unique(ids)))
+    fn = {"gate_up": layer.gate_up, "down": layer.down, "dense_fa": layer.dense_fa,
+          "layer": layer.forward}[what]
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    alg = algorithmic(shape, T, e_active)
+    print(json.dumps({"only": what, "workload": f"{name} T={T} {routing}", "steps": steps,
+                      "e_active": e_active, "gate_up_algorithmic_bytes": alg["gu_bytes"],
+                      "gate_up_algorithmic_flops": alg["gu_flops"],
+                      "dense_fa_algorithmic_flops": alg["fa_flops"]}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +287,8 @@ def main():
     ap.add_argument("--routing", default=None)
     ap.add_argument("--all", action="store_true", help="one line per workload of every config")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["gate_up", "down", "dense_fa", "layer", "copy"],
+                    help="run one piece `--steps` times, untimed (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
@@ -259,6 +297,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.only:
+        shape = configs.CONFIGS[args.config or "mixtral"]
+        run_only(args.config or "mixtral", args.T or shape.tokens[0],
+                 args.routing or shape.routing[0], args.only, args.steps)
+        return
     if args.all:
         work = ALL
     elif args.config:

@@ -200,9 +200,15 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
 // loads (global_load_lds_dwordx4), so two steps of loads are in flight while
 // one is multiplied without spending registers on staging.  A direct load
 // writes its 64 lanes' 16 bytes contiguously, so instead of padding, the
-// 16-byte segments of each 128-byte LDS row are permuted (XOR with a
-// function of the row): the 16 rows one fragment read touches then fall in
-// distinct banks.
+// 16-byte segments of each 128-byte LDS row are permuted: segment s of row r
+// sits in slot s ^ (r & 7), which makes the fragment reads free of bank
+// conflicts (measured with the LDS bank-conflict counter; 16-byte row
+// padding costs 2 conflict cycles per read on gfx950, no permutation 6).
+//
+// Work order: a 1-D grid of (weight tile, token block) items, token block
+// fastest, dealt to the 8 XCDs in contiguous runs (workgroup b runs on XCD
+// b % 8), so the blocks that share a weight tile (those of one expert) run
+// together on one XCD and read the tile through that XCD's L2 once.
 
 constexpr int kT2Threads = 512;
 constexpr int kT2Waves = kT2Threads / kWave;
@@ -218,7 +224,7 @@ struct Tile2Smem {
   int dst[BN];
 };
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 // byte offset of (row, 16-byte segment) inside a stage buffer
 __device__ __forceinline__ int lds_off(int row, int seg) {
@@ -247,13 +253,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <class SY, int BN, bool kGateUp>
 __global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
-    uint16_t* __restrict__ act, typename SY::T* __restrict__ y) {
+    uint16_t* __restrict__ act, typename SY::T* __restrict__ y, int ntiles, int nblocks) {
   __shared__ Tile2Smem<BN> sm;
   constexpr int TN = BN / 2 / 16;                         // token tiles per wavefront
   constexpr int AInst = kT2BM * kRowBytes / 1024 / kT2Waves;  // 4 direct loads per wave
   constexpr int BInst = BN * kRowBytes / 1024 / kT2Waves;     // 2 (BN 128) or 1 (BN 64)
   constexpr int kLoads = AInst + BInst;
-  const int blk = blockIdx.y;
+  // XCD-aware work item: XCD b % 8 takes items [xcd * per, (xcd + 1) * per)
+  const int per = (int)(gridDim.x / 8);
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= ntiles * nblocks) return;
+  const int tile = item / nblocks;
+  const int blk = item % nblocks;
   const bool dense = rm.counts == nullptr;
   int e, row0, nvalid;
   if (dense) {
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
 
   // Direct loads: instruction i of a stage fills LDS rows 8i..8i+7; lane l
   // fills row 8i + l/8, slot l%8, which holds global segment (l%8) ^ swz(row).
-  const int i0 = blockIdx.x * (kGateUp ? kT2BM / 2 : kT2BM);
+  const int i0 = tile * (kGateUp ? kT2BM / 2 : kT2BM);
   const uint16_t* wexp = w + (size_t)e * (kGateUp ? 2 * (size_t)I * H : (size_t)H * I);
   const uint8_t* asrc[AInst];
 #pragma unroll
@@ -405,20 +416,26 @@ static void dn_launch(const void* w2, const uint16_t* act, const RowMap& rm, int
                      I, (uint16_t*)nullptr, static_cast<typename SY::T*>(y));
 }
 
+// 1-D grid of tiles x blocks items, rounded up to a multiple of the 8 XCDs
+static unsigned xcd_grid(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
+
 template <int BN>
 static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
                        int I, uint16_t* act, hipStream_t s) {
-  hipLaunchKernelGGL((tile2_ffn_kernel<BF16, BN, true>), dim3(I / (kT2BM / 2), (unsigned)nblocks),
+  const int ntiles = I / (kT2BM / 2);
+  hipLaunchKernelGGL((tile2_ffn_kernel<BF16, BN, true>), dim3(xcd_grid(ntiles * nblocks)),
                      dim3(kT2Threads), 0, s, static_cast<const uint16_t*>(w13),
-                     static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr);
+                     static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr, ntiles,
+                     (int)nblocks);
 }
 
 template <class SY, int BN>
 static void dn2_launch(const void* w2, const uint16_t* act, const RowMap& rm, int64_t nblocks,
                        int H, int I, void* y, hipStream_t s) {
-  hipLaunchKernelGGL((tile2_ffn_kernel<SY, BN, false>), dim3(H / kT2BM, (unsigned)nblocks),
+  const int ntiles = H / kT2BM;
+  hipLaunchKernelGGL((tile2_ffn_kernel<SY, BN, false>), dim3(xcd_grid(ntiles * nblocks)),
                      dim3(kT2Threads), 0, s, static_cast<const uint16_t*>(w2), act, rm, H, I,
-                     (uint16_t*)nullptr, static_cast<typename SY::T*>(y));
+                     (uint16_t*)nullptr, static_cast<typename SY::T*>(y), ntiles, (int)nblocks);
 }
 
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
