@@ -41,23 +41,24 @@ ALL = [("tiny", 64, "uniform"), ("mixtral", 32, "uniform"), ("mixtral", 1024, "u
       [("mixtral_sweep", T, "uniform") for T in (1, 8, 128, 512, 2048)]
 
 
-def kernel_source_hash():
+def source_hash(files):
+    """Hash of the kernel sources a counter measurement was taken with."""
     h = hashlib.sha256()
-    for f in ("stream_ffn.hip", "tile_ffn.hip", "common.h"):
+    for f in files:
         p = os.path.join(ROOT, "mixture_experts_layer_30_amd", "csrc", f)
-        if os.path.exists(p):
-            h.update(open(p, "rb").read())
+        h.update(open(p, "rb").read() if os.path.exists(p) else b"")
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
-    """HBM bytes per gate/up launch from committed rocprofv3 counter runs, if the
-    kernel sources are unchanged since they were taken."""
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a copy
+    of known size), or None once the kernel sources have changed since."""
     p = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(p):
         return None
-    rec = json.load(open(p)).get(workload)
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    rec = json.load(open(p)).get("workloads", {}).get(workload)
+    if not rec or rec.get("source_hash") != source_hash(rec.get("sources", [])):
         return None
     return rec.get("bytes_per_launch")
 

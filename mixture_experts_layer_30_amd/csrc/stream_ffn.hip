@@ -132,8 +132,9 @@ struct Bucket {
   int row0;  // first row of the expert in the alignment (0 for dense)
 };
 
+template <bool kDense>
 __device__ __forceinline__ Bucket bucket_of(const RowMap& rm, int e) {
-  if (rm.counts == nullptr) return Bucket{(int)rm.dense_rows, 0};
+  if (kDense) return Bucket{(int)rm.dense_rows, 0};
   return Bucket{rm.counts[e], rm.offsets[e]};
 }
 
@@ -157,15 +158,15 @@ __device__ __forceinline__ void split_range(int nch, int wave, int& c_begin, int
 // Gate/up half: act[row][i] = silu(W1_e x_t)_i * (W3_e x_t)_i, bf16.
 // Tiles of the slab: 0 = gate i0..i0+15, 1 = up i0..i0+15, 2 = gate i0+16..i0+31,
 // 3 = up i0+16..i0+31.
-template <class S, int TB>
+template <class S, int TB, bool kDense>
 __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void stream_gate_up_kernel(
     const typename S::T* __restrict__ x, const typename S::T* __restrict__ w13, RowMap rm, int H,
     int I, uint16_t* __restrict__ act, float* __restrict__ part) {
   __shared__ StreamSmem sm;
   const int e = blockIdx.y;
-  const Bucket bk = bucket_of(rm, e);
+  const Bucket bk = bucket_of<kDense>(rm, e);
   if (bk.n == 0) return;
-  const bool dense = rm.counts == nullptr;
+  constexpr bool dense = kDense;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int m = lane & 15, g = lane >> 4;
@@ -238,15 +239,15 @@ __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void str
 
 // Down half: y[p][h] = sum_i W2_e[h][i] act[row][i] for the valid rows of expert e,
 // written to the pair's row p = sorted_ids[row] (dense: row = token = output row).
-template <class SW, class SY, int TB>
+template <class SW, class SY, int TB, bool kDense>
 __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void stream_down_kernel(
     const typename SW::T* __restrict__ w2, const uint16_t* __restrict__ act, RowMap rm, int H,
     int I, typename SY::T* __restrict__ y, float* __restrict__ part) {
   __shared__ StreamSmem sm;
   const int e = blockIdx.y;
-  const Bucket bk = bucket_of(rm, e);
+  const Bucket bk = bucket_of<kDense>(rm, e);
   if (bk.n == 0) return;
-  const bool dense = rm.counts == nullptr;
+  constexpr bool dense = kDense;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int m = lane & 15, g = lane >> 4;
@@ -341,17 +342,27 @@ __global__ __launch_bounds__(256) void finish_down_kernel(const float* __restric
 template <class S, int TB>
 static void launch_gu(const void* x, const void* w13, const RowMap& rm, int E, int H, int I,
                       int splits, uint16_t* act, float* part, hipStream_t s) {
-  hipLaunchKernelGGL((stream_gate_up_kernel<S, TB>), dim3(I / 32, E, splits), dim3(kStreamThreads),
-                     0, s, static_cast<const typename S::T*>(x),
-                     static_cast<const typename S::T*>(w13), rm, H, I, act, part);
+  if (rm.counts == nullptr)
+    hipLaunchKernelGGL((stream_gate_up_kernel<S, TB, true>), dim3(I / 32, E, splits),
+                       dim3(kStreamThreads), 0, s, static_cast<const typename S::T*>(x),
+                       static_cast<const typename S::T*>(w13), rm, H, I, act, part);
+  else
+    hipLaunchKernelGGL((stream_gate_up_kernel<S, TB, false>), dim3(I / 32, E, splits),
+                       dim3(kStreamThreads), 0, s, static_cast<const typename S::T*>(x),
+                       static_cast<const typename S::T*>(w13), rm, H, I, act, part);
 }
 
 template <class SW, class SY, int TB>
 static void launch_dn(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H, int I,
                       int splits, void* y, float* part, hipStream_t s) {
-  hipLaunchKernelGGL((stream_down_kernel<SW, SY, TB>), dim3(H / 64, E, splits),
-                     dim3(kStreamThreads), 0, s, static_cast<const typename SW::T*>(w2), act, rm,
-                     H, I, static_cast<typename SY::T*>(y), part);
+  if (rm.counts == nullptr)
+    hipLaunchKernelGGL((stream_down_kernel<SW, SY, TB, true>), dim3(H / 64, E, splits),
+                       dim3(kStreamThreads), 0, s, static_cast<const typename SW::T*>(w2), act, rm,
+                       H, I, static_cast<typename SY::T*>(y), part);
+  else
+    hipLaunchKernelGGL((stream_down_kernel<SW, SY, TB, false>), dim3(H / 64, E, splits),
+                       dim3(kStreamThreads), 0, s, static_cast<const typename SW::T*>(w2), act, rm,
+                       H, I, static_cast<typename SY::T*>(y), part);
 }
 
 template <class S>
