@@ -1,6 +1,6 @@
 // C ABI of the MoE layer library: argument checks, schedule choice, launches.
 // What each call computes is documented in include/moe_layer.h.
-#include "../../include/moe_layer.h"
+#include "moe_layer.h"
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -88,7 +88,8 @@ int stream_tok_blocks(int64_t max_rows) {
 // contraction is split (deterministically, partial sums added in slice order)
 // until about 1024 workgroups exist, keeping at least 2 chunks per wavefront.
 struct DensePlan {
-  int tok_blocks, split_gu, split_dn;
+  int tok_blocks, split_gu, split_dn;  // streaming schedule
+  int tile_block, tile_split;          // tiled schedule: token block and down-projection split
   int64_t act_bytes, part_bytes;
 };
 
@@ -99,15 +100,32 @@ int pick_splits(int slabs, int nch) {
   return s < 1 ? 1 : (s > most ? most : s);
 }
 
-DensePlan dense_plan(int64_t T, int H, int I) {
+DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   DensePlan p;
   p.tok_blocks = stream_tok_blocks(T);
   p.split_gu = pick_splits(I / 32, H / 64);
   p.split_dn = pick_splits(H / 64, I / 64);
+  // tiled: 256-token blocks where the 256-row bf16 tile covers both halves and there are
+  // at least two of them (each weight tile then read once per 256 tokens); the down
+  // projection, H/256 tiles per block, is split when that leaves fewer than 256 workgroups
+  const bool tile2 = dt == MOE_BF16 && I % 128 == 0 && H % 256 == 0;
+  p.tile_block = (tile2 && T >= 512) ? 256 : 128;
+  p.tile_split = 1;
+  if (tile2) {
+    const int64_t items = (int64_t)(H / 256) * ((T + p.tile_block - 1) / p.tile_block);
+    if (items < 256) {
+      // one 512-thread workgroup per CU: aim at 256, keeping >= 8 contraction steps a slice
+      const int64_t most = I / 64 / 8 > 1 ? I / 64 / 8 : 1;
+      const int64_t want = (256 + items - 1) / items;
+      p.tile_split = (int)(want < most ? want : most);
+    }
+  }
   p.act_bytes = round_up(round_up(T, 128) * (int64_t)I * 2, 256);
   const int64_t gu = p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0;
   const int64_t dn = p.split_dn > 1 ? (int64_t)p.split_dn * T * H * 4 : 0;
+  const int64_t tdn = p.tile_split > 1 ? (int64_t)p.tile_split * T * H * 4 : 0;
   p.part_bytes = gu > dn ? gu : dn;
+  if (tdn > p.part_bytes) p.part_bytes = tdn;
   return p;
 }
 
@@ -166,8 +184,10 @@ int64_t moe_ffn_workspace_bytes(int64_t cap, int I) {
 
 int64_t dense_ffn_workspace_bytes(int64_t T, int H, int I_fa) {
   if (T < 0 || H < 64 || I_fa < 64 || H % 64 || I_fa % 64) return -1;
-  const DensePlan p = dense_plan(T, H, I_fa);
-  return p.act_bytes + p.part_bytes;
+  // sized for the larger of the two storage dtypes' plans
+  const DensePlan a = dense_plan(T, H, I_fa, MOE_BF16), b = dense_plan(T, H, I_fa, MOE_F32);
+  const int64_t pa = a.act_bytes + a.part_bytes, pb = b.act_bytes + b.part_bytes;
+  return pa > pb ? pa : pb;
 }
 
 moe_status moe_route(const float* logits, int64_t T, int E, int K, int32_t* topk_ids,
@@ -265,7 +285,7 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   hipError_t e;
   if (use == MOE_SCHED_TILE)
     e = moe::launch_tile_down(w2, dt, (const uint16_t*)workspace, rm, plan->cap / plan->block_m,
-                              H, I, y_pairs, dt, s);
+                              H, I, y_pairs, dt, 1, nullptr, s);
   else
     e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, E, H, I,
                                 stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
@@ -327,15 +347,17 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   st = pick_schedule(sched, T, 1, 1, 128, H, &use);
   if (st) return st;
   if (sched == MOE_SCHED_AUTO && T < 256) use = MOE_SCHED_STREAM;
+  const DensePlan dp = dense_plan(T, H, I_fa, dt);
   if (use == MOE_SCHED_TILE) {
     uint16_t* act = (uint16_t*)workspace;
-    const int64_t nblocks = (T + 127) / 128;
+    float* part = (float*)((char*)workspace + dp.act_bytes);
+    rm.block_m = dp.tile_block;
+    const int64_t nblocks = (T + rm.block_m - 1) / rm.block_m;
     hipError_t e = moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s);
     if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
-    e = moe::launch_tile_down(w2, dt, act, rm, nblocks, H, I_fa, out, odt, s);
+    e = moe::launch_tile_down(w2, dt, act, rm, nblocks, H, I_fa, out, odt, dp.tile_split, part, s);
     return hip_status(e, "dense_ffn_fa down");
   }
-  const DensePlan dp = dense_plan(T, H, I_fa);
   uint16_t* act = (uint16_t*)workspace;
   float* part = (float*)((char*)workspace + dp.act_bytes);
   hipError_t e = moe::launch_stream_gate_up(x, dt, w13, rm, 1, H, I_fa, dp.tok_blocks, dp.split_gu,

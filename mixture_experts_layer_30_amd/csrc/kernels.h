@@ -48,7 +48,14 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
 // LDS-tiled MFMA schedule: one workgroup per (block_m-row token block, 128 weight rows).
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
                                int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s);
+// ksplit > 1 (dense rows, bf16, H % 256 == 0 only) splits the contraction into
+// slices whose fp32 sums go to part [ksplit][rows][H], added in order by a finish kernel.
 hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
-                            int64_t nblocks, int H, int I, void* y, int ydt, hipStream_t s);
+                            int64_t nblocks, int H, int I, void* y, int ydt, int ksplit,
+                            float* part, hipStream_t s);
+
+// y[r][h] = sum over z < splits (in order) of part[z][r][h], rounded to ydt.
+hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H, void* y,
+                              int ydt, hipStream_t s);
 
 }  // namespace moe

@@ -406,16 +406,20 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
     if (ydt == kDtF32) dn_tb<BF16, F32>(w2, act, rm, E, H, I, tok_blocks, splits, y, p, s);
     else dn_tb<BF16, BF16>(w2, act, rm, E, H, I, tok_blocks, splits, y, p, s);
   }
-  if (splits > 1) {
-    const int64_t n = rm.dense_rows * H;
-    const unsigned blocks = (unsigned)((n + 255) / 256);
-    if (ydt == kDtF32)
-      hipLaunchKernelGGL(finish_down_kernel<F32>, dim3(blocks), dim3(256), 0, s, part, splits,
-                         rm.dense_rows, H, static_cast<float*>(y));
-    else
-      hipLaunchKernelGGL(finish_down_kernel<BF16>, dim3(blocks), dim3(256), 0, s, part, splits,
-                         rm.dense_rows, H, static_cast<uint16_t*>(y));
-  }
+  if (splits > 1) return launch_finish_down(part, splits, rm.dense_rows, H, y, ydt, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H, void* y,
+                              int ydt, hipStream_t s) {
+  const int64_t n = rows * H;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (ydt == kDtF32)
+    hipLaunchKernelGGL(finish_down_kernel<F32>, dim3(blocks), dim3(256), 0, s, part, splits, rows,
+                       H, static_cast<float*>(y));
+  else
+    hipLaunchKernelGGL(finish_down_kernel<BF16>, dim3(blocks), dim3(256), 0, s, part, splits,
+                       rows, H, static_cast<uint16_t*>(y));
   return hipGetLastError();
 }
 

@@ -195,34 +195,46 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Second-generation tile for bf16 storage: 8 wavefronts, 256 weight rows x BN
-// tokens per workgroup, and a 3-stage LDS ring filled by direct global->LDS
-// loads (global_load_lds_dwordx4), so two steps of loads are in flight while
-// one is multiplied without spending registers on staging.  A direct load
-// writes its 64 lanes' 16 bytes contiguously, so instead of padding, the
-// 16-byte segments of each 128-byte LDS row are permuted: segment s of row r
-// sits in slot s ^ (r & 7), which makes the fragment reads free of bank
-// conflicts (measured with the LDS bank-conflict counter; 16-byte row
-// padding costs 2 conflict cycles per read on gfx950, no permutation 6).
+// Second-generation tile for bf16 storage: 256 weight rows x BN tokens per
+// workgroup (BN = 128, or 256 for dense rows), NW wavefronts in an NW/2 x 2
+// grid, each owning a (256 / (NW/2)) x BN/2 register tile, and an ST-stage LDS
+// ring filled by direct global->LDS loads (global_load_lds_dwordx4), so ST-1
+// steps of loads are in flight while one is multiplied without spending
+// registers on staging.  8 wavefronts (2 per SIMD, 64 x 64 register tiles)
+// measure faster than 4 wavefronts of 128-row tiles, which leave one wave per
+// SIMD to hide the load latency.  The loop is bound by the loads that miss L2
+// (the part of a step's working set not already fetched by another workgroup
+// of the same XCD), not by the matrix cores.
+//
+// A direct load writes its 64 lanes' 16 bytes contiguously, so instead of
+// padding, the 16-byte segments of each 128-byte LDS row are permuted:
+// segment s of row r sits in slot s ^ (r & 7), which makes the fragment reads
+// free of bank conflicts (measured with the LDS bank-conflict counter; 16-byte
+// row padding costs 2 conflict cycles per read on gfx950, no permutation 6).
 //
 // Work order: a 1-D grid of (weight tile, token block) items, token block
 // fastest, dealt to the 8 XCDs in contiguous runs (workgroup b runs on XCD
 // b % 8), so the blocks that share a weight tile (those of one expert) run
 // together on one XCD and read the tile through that XCD's L2 once.
 
-constexpr int kT2Threads = 512;
-constexpr int kT2Waves = kT2Threads / kWave;
+#ifndef MOE_TILE_WAVES
+#define MOE_TILE_WAVES 8
+#endif
+
 constexpr int kT2BM = 256;
-constexpr int kT2Stages = 3;
 constexpr int kRowBytes = kBK * 2;   // 128 bytes of one row per step
 
-template <int BN>
+template <int BN, int ST>
 struct Tile2Smem {
-  uint8_t a[kT2Stages][kT2BM * kRowBytes];
-  uint8_t b[kT2Stages][BN * kRowBytes];
+  uint8_t a[ST][kT2BM * kRowBytes];
+  uint8_t b[ST][BN * kRowBytes];
   int tok[BN];
   int dst[BN];
 };
+
+// stages that fit the 160 KB of LDS next to the token arrays
+template <int BN>
+constexpr int tile2_stages() { return BN >= 256 ? 2 : 3; }
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
@@ -250,19 +262,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <class SY, int BN, bool kGateUp>
-__global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
+template <class SY, int BN, bool kGateUp, int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
-    uint16_t* __restrict__ act, typename SY::T* __restrict__ y, int ntiles, int nblocks) {
-  __shared__ Tile2Smem<BN> sm;
-  constexpr int TN = BN / 2 / 16;                         // token tiles per wavefront
-  constexpr int AInst = kT2BM * kRowBytes / 1024 / kT2Waves;  // 4 direct loads per wave
-  constexpr int BInst = BN * kRowBytes / 1024 / kT2Waves;     // 2 (BN 128) or 1 (BN 64)
+    uint16_t* __restrict__ act, typename SY::T* __restrict__ y, int ntiles, int nblocks,
+    int ksplit, float* __restrict__ part) {
+  constexpr int ST = tile2_stages<BN>();
+  constexpr int NT = NW * kWave;
+  constexpr int WM = NW / 2;                              // wavefront rows
+  constexpr int TM = kT2BM / WM / 16;                     // 16-row tiles per wavefront
+  constexpr int TN = BN / 2 / 16;                         // 16-token tiles per wavefront
+  constexpr int AInst = kT2BM * kRowBytes / 1024 / NW;    // direct loads per wave per step
+  constexpr int BInst = BN * kRowBytes / 1024 / NW;
   constexpr int kLoads = AInst + BInst;
+  static_assert(BInst >= 1 && kLoads * (ST - 1) < 64, "load counts");
+  __shared__ Tile2Smem<BN, ST> sm;
   // XCD-aware work item: XCD b % 8 takes items [xcd * per, (xcd + 1) * per)
   const int per = (int)(gridDim.x / 8);
-  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (item >= ntiles * nblocks) return;
+  const int item0 = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item0 >= ksplit * ntiles * nblocks) return;
+  const int zk = item0 / (ntiles * nblocks);   // slice of a split contraction (dense down only)
+  const int item = item0 % (ntiles * nblocks);
   const int tile = item / nblocks;
   const int blk = item % nblocks;
   const bool dense = rm.counts == nullptr;
@@ -284,7 +304,7 @@ __global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int m = lane & 15, g = lane >> 4;
 
-  for (int j = tid; j < BN; j += kT2Threads) {
+  for (int j = tid; j < BN; j += NT) {
     const int jj = j < nvalid ? j : 0;
     const int row = row0 + jj;
     if (kGateUp) {
@@ -306,7 +326,7 @@ __global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
     const int r = 8 * (wave * AInst + j) + lane / 8;
     size_t wr;
     if (kGateUp) {
-      const int q = r >> 4;
+      const int q = r >> 4;                       // 16-row group: even = gate, odd = up
       const int i = i0 + 16 * (q >> 1) + (r & 15);
       wr = (q & 1) ? (size_t)(I + i) : (size_t)i;
     } else {
@@ -322,9 +342,13 @@ __global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
               (((lane & 7) ^ swz(r)) << 4);
   }
 
+  // this workgroup's steps [k0, k0 + nk) of the contraction
+  const int nk_all = Kdim / kBK;
+  const int k0 = zk * nk_all / ksplit;
+  const int nk = (zk + 1) * nk_all / ksplit - k0;
   auto issue = [&](int ks) {
-    const int st = ks % kT2Stages;
-    const size_t kb = (size_t)ks * kRowBytes;
+    const int st = ks % ST;
+    const size_t kb = (size_t)(k0 + ks) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < AInst; ++j)
       lds_direct16(asrc[j] + kb, &sm.a[st][(wave * AInst + j) * 1024]);
@@ -333,48 +357,51 @@ __global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
       lds_direct16(bsrc[j] + kb, &sm.b[st][(wave * BInst + j) * 1024]);
   };
 
-  f32x4 acc[4][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = Kdim / kBK;
-  issue(0);
-  if (nk > 1) issue(1);
+#pragma unroll
+  for (int s0 = 0; s0 < ST - 1; ++s0)
+    if (s0 < nk) issue(s0);
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) wait_vmcnt<kLoads>();
+    // stage ks must be in LDS: the stages issued after it may stay in flight
+    if (ST == 3 && ks + 1 < nk) wait_vmcnt<(ST == 3 ? kLoads : 0)>();
     else wait_vmcnt<0>();
     barrier_no_fence();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
-    if (ks + 2 < nk) issue(ks + 2);
-    const uint8_t* A = sm.a[ks % kT2Stages];
-    const uint8_t* Bt = sm.b[ks % kT2Stages];
+    if (ks + ST - 1 < nk) issue(ks + ST - 1);
+    const uint8_t* A = sm.a[ks % ST];
+    const uint8_t* Bt = sm.b[ks % ST];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 fa[4], fb[TN];
+      u32x4 fa[TM], fb[TN];
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-        fa[tm] = *reinterpret_cast<const u32x4*>(A + lds_off(wm * 64 + tm * 16 + m, s2 * 4 + g));
+      for (int tm = 0; tm < TM; ++tm)
+        fa[tm] = *reinterpret_cast<const u32x4*>(
+            A + lds_off(wm * (TM * 16) + tm * 16 + m, s2 * 4 + g));
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         fb[tn] = *reinterpret_cast<const u32x4*>(
             Bt + lds_off(wn * (BN / 2) + tn * 16 + m, s2 * 4 + g));
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
+      for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(fa[tm], fb[tn], acc[tm][tn]);
     }
   }
 
+  // epilogue: lane holds rows 4g..4g+3 of each 16-row tile, for token column m of each tile
   if (kGateUp) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < TM / 2; ++p)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const int j = wn * (BN / 2) + tn * 16 + m;
         if (j < nvalid) {
           const f32x4 gs = acc[2 * p][tn], us = acc[2 * p + 1][tn];
-          const int i = i0 + 16 * (wm * 2 + p) + 4 * g;
+          const int i = i0 + 16 * (wm * (TM / 2) + p) + 4 * g;
           uint2 v;
           v.x = pack_bf16x2(silu(gs.x) * us.x, silu(gs.y) * us.y);
           v.y = pack_bf16x2(silu(gs.z) * us.z, silu(gs.w) * us.w);
@@ -383,18 +410,22 @@ __global__ __launch_bounds__(kT2Threads, 1) void tile2_ffn_kernel(
       }
   } else {
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const int j = wn * (BN / 2) + tn * 16 + m;
         if (j < nvalid) {
-          const int h = i0 + wm * 64 + tm * 16 + 4 * g;
-          typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
+          const int h = i0 + wm * (TM * 16) + tm * 16 + 4 * g;
           const f32x4 v = acc[tm][tn];
-          store_out<SY>(o + 0, v.x);
-          store_out<SY>(o + 1, v.y);
-          store_out<SY>(o + 2, v.z);
-          store_out<SY>(o + 3, v.w);
+          if (part) {  // split contraction: fp32 slice, summed in slice order by the finish kernel
+            *reinterpret_cast<f32x4*>(part + ((size_t)zk * rm.dense_rows + sm.dst[j]) * H + h) = v;
+          } else {
+            typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
+            store_out<SY>(o + 0, v.x);
+            store_out<SY>(o + 1, v.y);
+            store_out<SY>(o + 2, v.z);
+            store_out<SY>(o + 3, v.w);
+          }
         }
       }
   }
@@ -423,26 +454,30 @@ template <int BN>
 static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
                        int I, uint16_t* act, hipStream_t s) {
   const int ntiles = I / (kT2BM / 2);
-  hipLaunchKernelGGL((tile2_ffn_kernel<BF16, BN, true>), dim3(xcd_grid(ntiles * nblocks)),
-                     dim3(kT2Threads), 0, s, static_cast<const uint16_t*>(w13),
+  hipLaunchKernelGGL((tile2_ffn_kernel<BF16, BN, true, MOE_TILE_WAVES>),
+                     dim3(xcd_grid(ntiles * nblocks)), dim3(MOE_TILE_WAVES * kWave), 0, s,
+                     static_cast<const uint16_t*>(w13),
                      static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr, ntiles,
-                     (int)nblocks);
+                     (int)nblocks, 1, (float*)nullptr);
 }
 
 template <class SY, int BN>
 static void dn2_launch(const void* w2, const uint16_t* act, const RowMap& rm, int64_t nblocks,
-                       int H, int I, void* y, hipStream_t s) {
+                       int H, int I, void* y, int ksplit, float* part, hipStream_t s) {
   const int ntiles = H / kT2BM;
-  hipLaunchKernelGGL((tile2_ffn_kernel<SY, BN, false>), dim3(xcd_grid(ntiles * nblocks)),
-                     dim3(kT2Threads), 0, s, static_cast<const uint16_t*>(w2), act, rm, H, I,
-                     (uint16_t*)nullptr, static_cast<typename SY::T*>(y), ntiles, (int)nblocks);
+  hipLaunchKernelGGL((tile2_ffn_kernel<SY, BN, false, MOE_TILE_WAVES>),
+                     dim3(xcd_grid((int64_t)ksplit * ntiles * nblocks)),
+                     dim3(MOE_TILE_WAVES * kWave), 0, s, static_cast<const uint16_t*>(w2), act,
+                     rm, H, I, (uint16_t*)nullptr, static_cast<typename SY::T*>(y), ntiles,
+                     (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr);
 }
 
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
                                int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s) {
   if (xdt == kDtBF16 && I % (kT2BM / 2) == 0) {
-    if (rm.block_m == 64) gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s);
-    else gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s);
+    if (rm.block_m == 256) gu2_launch<256>(x, w13, rm, nblocks, H, I, act, s);
+    else if (rm.block_m == 128) gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s);
+    else gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s);
     return hipGetLastError();
   }
   if (rm.block_m == 64) {
@@ -463,15 +498,20 @@ static void dn_by_out(const void* w2, const uint16_t* act, const RowMap& rm, int
 }
 
 hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
-                            int64_t nblocks, int H, int I, void* y, int ydt, hipStream_t s) {
+                            int64_t nblocks, int H, int I, void* y, int ydt, int ksplit,
+                            float* part, hipStream_t s) {
   if (wdt == kDtBF16 && H % kT2BM == 0) {
-    if (rm.block_m == 64) {
-      if (ydt == kDtF32) dn2_launch<F32, 64>(w2, act, rm, nblocks, H, I, y, s);
-      else dn2_launch<BF16, 64>(w2, act, rm, nblocks, H, I, y, s);
+    if (rm.block_m == 256) {
+      if (ydt == kDtF32) dn2_launch<F32, 256>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
+      else dn2_launch<BF16, 256>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
+    } else if (rm.block_m == 128) {
+      if (ydt == kDtF32) dn2_launch<F32, 128>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
+      else dn2_launch<BF16, 128>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
     } else {
-      if (ydt == kDtF32) dn2_launch<F32, 128>(w2, act, rm, nblocks, H, I, y, s);
-      else dn2_launch<BF16, 128>(w2, act, rm, nblocks, H, I, y, s);
+      if (ydt == kDtF32) dn2_launch<F32, 64>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
+      else dn2_launch<BF16, 64>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
     }
+    if (ksplit > 1) return launch_finish_down(part, ksplit, rm.dense_rows, H, y, ydt, s);
     return hipGetLastError();
   }
   if (rm.block_m == 64) {

@@ -197,6 +197,34 @@ def test_dense_ffn_parity(T, H, I, dt, odt):
     assert rel_err(out, ref) <= TOL
 
 
+DENSE_TILE_CASES = [
+    # (T, H, I): 256-token blocks with a ragged tail and the down projection split in 7
+    # uneven slices; 128-token blocks split in 2; two full 256-token blocks
+    (600, 256, 3968),
+    (333, 512, 1280),
+    (512, 256, 1024),
+]
+
+
+@pytest.mark.parametrize("T,H,I", DENSE_TILE_CASES)
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_dense_ffn_tile_parity(T, H, I, odt):
+    """The tiled schedule on dense rows, where few output tiles make the down
+    projection split its contraction (fp32 slices summed in slice order)."""
+    x = synth.tokens(T, H, "bf16", seed=I)
+    w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T)
+    ref = oracle.swiglu(x, w13, w2)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(T, H, I), dtype=torch.uint8, device=DEV)
+    xd, w13d, w2d = x.to(DEV), w13.to(DEV), w2.to(DEV)
+    out = torch.empty(T, H, dtype=odt, device=DEV)
+    B.dense_ffn_fa(xd, w13d, w2d, ws, out, sched=B.SCHED_TILE)
+    out2 = torch.empty_like(out)
+    B.dense_ffn_fa(xd, w13d, w2d, ws, out2, sched=B.SCHED_TILE)
+    torch.cuda.synchronize()
+    assert rel_err(out, ref) <= TOL
+    assert torch.equal(out, out2)   # the split sums are deterministic
+
+
 def test_dense_unit_vector_case():
     """The oracle's closed-form SwiGLU case (gate picks x0, x2; up picks x1, x3),
     padded to the kernel's 64-multiple sizes."""
@@ -266,6 +294,9 @@ TILE_SHAPES = [
     (LayerShape("tile2_b128", 512, 384, 8, 2, 256, "bf16", (700,), ("zipf",)), 700, "zipf", 128),
     (LayerShape("tile2_b64", 256, 256, 16, 4, 0, "bf16", (300,), ("uniform",)), 300, "uniform", 64),
     (LayerShape("tile2_short_k", 256, 128, 4, 1, 0, "bf16", (129,), ("uniform",)), 129, "uniform", 128),
+    # the 256-row tile on both halves, ragged last block
+    (LayerShape("tile2_both", 512, 512, 8, 2, 256, "bf16", (333,), ("zipf",)), 333, "zipf", 128),
+    (LayerShape("tile2_both_b64", 256, 256, 8, 2, 0, "bf16", (190,), ("uniform",)), 190, "uniform", 64),
 ]
 
 
