@@ -55,11 +55,16 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Schedules of the grouped FFN (and of the dense FFN). */
 typedef enum {
-    MOE_SCHED_AUTO = 0,    /* chosen from the shape */
+    MOE_SCHED_AUTO = 0,    /* chosen from the shape: TILE once an expert holds a tile's worth
+                              of tokens on average, else RING where it applies, else STREAM */
     MOE_SCHED_STREAM = 1,  /* weight-streaming: each active expert's weights read once per
-                              pass of up to 128 tokens; for HBM-bound (decode) shapes */
-    MOE_SCHED_TILE = 2     /* MFMA tiles of block_m tokens x 128 weight rows staged through
+                              pass of up to 64 tokens, straight into MFMA operand registers;
+                              any supported shape and dtype; for HBM-bound (decode) shapes */
+    MOE_SCHED_TILE = 2,    /* MFMA tiles of block_m tokens x 128 weight rows staged through
                               LDS; for MFMA-bound (prefill) shapes; needs block_m 64 or 128 */
+    MOE_SCHED_RING = 3     /* weight-streaming through an LDS ring filled by whole-line
+                              direct loads, one persistent workgroup per CU; needs bf16,
+                              H % 128 == 0 and I % 64 == 0 (gate/up), I % 128 == 0 (down) */
 } moe_schedule;
 
 /*

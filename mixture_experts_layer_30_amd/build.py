@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libmoe_layer.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "route.hip", "align.hip", "combine.hip", "stream_ffn.hip", "tile_ffn.hip"]
+SOURCES = ["abi.cpp", "route.hip", "align.hip", "combine.hip", "stream_ffn.hip", "ring_ffn.hip", "tile_ffn.hip"]
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           # no packed-fp32 instructions in device code

@@ -3,6 +3,7 @@
 #include "moe_layer.h"
 
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -84,12 +85,27 @@ int stream_tok_blocks(int64_t max_rows) {
   return 4;
 }
 
+// Token blocks per pass of the LDS-ring schedule, whose LDS holds the pass's
+// token rows next to the weights (more blocks, fewer stages in flight): the
+// expected load of an expert, T*K/E, with a margin.  An expert above 16 times
+// that takes several passes.
+int ring_tok_blocks(int64_t T, int K, int E) {
+  const int64_t lam = (T * K + E - 1) / E;
+  int64_t want = 2 * lam + 8;
+  if (want > T) want = T;
+  // four blocks would leave room for only three stages (measured slower than
+  // handing the busier experts to the register-streaming kernel)
+  return stream_tok_blocks(want < 32 ? want : 32);
+}
+
 // Dense FFN plan: workgroups per streaming launch are slabs x splits; the
 // contraction is split (deterministically, partial sums added in slice order)
 // until about 1024 workgroups exist, keeping at least 2 chunks per wavefront.
 struct DensePlan {
   int tok_blocks, split_gu, split_dn;  // streaming schedule
   int tile_block, tile_split;          // tiled schedule: token block and down-projection split
+  bool ring_gu, ring_dn;               // LDS-ring streaming applies to the half
+  int ring_split_gu, ring_split_dn;    // and the contraction split it uses
   int64_t act_bytes, part_bytes;
 };
 
@@ -120,12 +136,19 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
       p.tile_split = (int)(want < most ? want : most);
     }
   }
+  p.ring_gu = moe::ring_gate_up_ok(dt, dt, H, I);
+  p.ring_dn = moe::ring_down_ok(dt, H, I);
+  p.ring_split_gu = p.ring_gu ? moe::ring_gate_up_splits(T, H, I) : 1;
+  p.ring_split_dn = p.ring_dn ? moe::ring_down_splits(T, H, I) : 1;
   p.act_bytes = round_up(round_up(T, 128) * (int64_t)I * 2, 256);
-  const int64_t gu = p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0;
-  const int64_t dn = p.split_dn > 1 ? (int64_t)p.split_dn * T * H * 4 : 0;
-  const int64_t tdn = p.tile_split > 1 ? (int64_t)p.tile_split * T * H * 4 : 0;
-  p.part_bytes = gu > dn ? gu : dn;
-  if (tdn > p.part_bytes) p.part_bytes = tdn;
+  // partial sums of whichever split schedule runs: the largest of them
+  const int64_t cand[5] = {p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0,
+                           p.split_dn > 1 ? (int64_t)p.split_dn * T * H * 4 : 0,
+                           p.tile_split > 1 ? (int64_t)p.tile_split * T * H * 4 : 0,
+                           p.ring_split_gu > 1 ? (int64_t)p.ring_split_gu * T * 2 * I * 4 : 0,
+                           p.ring_split_dn > 1 ? (int64_t)p.ring_split_dn * T * H * 4 : 0};
+  p.part_bytes = 0;
+  for (int64_t c : cand) p.part_bytes = c > p.part_bytes ? c : p.part_bytes;
   return p;
 }
 
@@ -143,13 +166,26 @@ moe_status pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m,
       return fail(MOE_EUNSUPPORTED, "tile schedule needs block_m 64 or 128 and H %% 128 == 0 "
                   "(block_m = %d, H = %d)", block_m, H);
     *out = MOE_SCHED_TILE;
-  } else if (req == MOE_SCHED_STREAM) {
-    *out = MOE_SCHED_STREAM;
+  } else if (req == MOE_SCHED_STREAM || req == MOE_SCHED_RING) {
+    *out = req;
   } else if (req == MOE_SCHED_AUTO) {
     *out = (tile_ok(block_m, H) && T * K >= 64 * (int64_t)E) ? MOE_SCHED_TILE : MOE_SCHED_STREAM;
   } else {
     return fail(MOE_EINVAL, "schedule %d", (int)req);
   }
+  return MOE_OK;
+}
+
+// The streaming schedules of one half: an explicit RING request needs a shape
+// the ring kernel takes (ring_ok); AUTO upgrades STREAM to RING where it also
+// expects it to be faster (auto_ok).
+moe_status pick_stream(moe_schedule req, bool ring_ok, bool auto_ok, const char* what,
+                       moe_schedule* use) {
+  if (*use == MOE_SCHED_RING && !ring_ok)
+    return fail(MOE_EUNSUPPORTED, "%s: ring schedule needs bf16, H %% 128 == 0 and "
+                "I %% 64 == 0 (gate/up) or I %% 128 == 0 (down)", what);
+  if (*use == MOE_SCHED_STREAM && req == MOE_SCHED_AUTO && ring_ok && auto_ok)
+    *use = MOE_SCHED_RING;
   return MOE_OK;
 }
 
@@ -242,6 +278,8 @@ static moe::RowMap grouped_rows(const moe_plan* plan, int K) {
   rm.K = K;
   rm.dense_rows = 0;
   rm.block_m = plan->block_m;
+  rm.min_rows = 1;
+  rm.max_rows = INT32_MAX;
   return rm;
 }
 
@@ -256,12 +294,27 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
   moe_schedule use;
   st = pick_schedule(sched, T, K, E, plan->block_m, H, &use);
   if (st) return st;
+  const bool ring = moe::ring_gate_up_ok(dt, dt, H, I);
+  st = pick_stream(sched, ring, ring, "moe_grouped_gate_up", &use);
+  if (st) return st;
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (use == MOE_SCHED_TILE)
     e = moe::launch_tile_gate_up(x, dt, w13, rm, plan->cap / plan->block_m, H, I,
                                  (uint16_t*)workspace, s);
+  else if (use == MOE_SCHED_RING) {
+    // experts whose tokens fit one ring pass go to the ring kernel, busier ones
+    // (possible only when T exceeds a pass) to the register-streaming kernel
+    const int nb = ring_tok_blocks(T, K, E);
+    moe::RowMap cold = rm, hot = rm;
+    cold.max_rows = 16 * nb;
+    hot.min_rows = 16 * nb + 1;
+    e = moe::launch_ring_gate_up(x, w13, cold, E, H, I, T, nb, 1, (uint16_t*)workspace, nullptr, s);
+    if (e == hipSuccess && T > 16 * nb)
+      e = moe::launch_stream_gate_up(x, dt, w13, hot, E, H, I, stream_tok_blocks(T), 1,
+                                     (uint16_t*)workspace, nullptr, s);
+  }
   else
     e = moe::launch_stream_gate_up(x, dt, w13, rm, E, H, I, stream_tok_blocks(T), 1,
                                    (uint16_t*)workspace, nullptr, s);
@@ -280,12 +333,26 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   moe_schedule use;
   st = pick_schedule(sched, T, K, E, plan->block_m, H, &use);
   if (st) return st;
+  const bool ring = moe::ring_down_ok(dt, H, I);
+  st = pick_stream(sched, ring, ring, "moe_grouped_down", &use);
+  if (st) return st;
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (use == MOE_SCHED_TILE)
     e = moe::launch_tile_down(w2, dt, (const uint16_t*)workspace, rm, plan->cap / plan->block_m,
                               H, I, y_pairs, dt, 1, nullptr, s);
+  else if (use == MOE_SCHED_RING) {
+    const int nb = ring_tok_blocks(T, K, E);
+    moe::RowMap cold = rm, hot = rm;
+    cold.max_rows = 16 * nb;
+    hot.min_rows = 16 * nb + 1;
+    e = moe::launch_ring_down(w2, (const uint16_t*)workspace, cold, E, H, I, T, nb, 1, y_pairs, dt,
+                              nullptr, s);
+    if (e == hipSuccess && T > 16 * nb)
+      e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, hot, E, H, I,
+                                  stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
+  }
   else
     e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, E, H, I,
                                 stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
@@ -339,6 +406,8 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   rm.K = 1;
   rm.dense_rows = T;
   rm.block_m = 128;
+  rm.min_rows = 1;
+  rm.max_rows = INT32_MAX;
   hipStream_t s = (hipStream_t)stream;
   // dense rows form one expert; the tiled schedule takes them in 128-row blocks
   // and is chosen from two blocks up (with a single block its down projection
@@ -358,13 +427,27 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
     e = moe::launch_tile_down(w2, dt, act, rm, nblocks, H, I_fa, out, odt, dp.tile_split, part, s);
     return hip_status(e, "dense_ffn_fa down");
   }
+  moe_schedule use_gu = use, use_dn = use;
+  // (AUTO: the ring kernel while a pass of at most 32 rows covers every token;
+  // past that its four-block layout is the slower one)
+  st = pick_stream(sched, dp.ring_gu, T <= 32, "dense_ffn_fa gate/up", &use_gu);
+  if (st) return st;
+  st = pick_stream(sched, dp.ring_dn, T <= 32, "dense_ffn_fa down", &use_dn);
+  if (st) return st;
   uint16_t* act = (uint16_t*)workspace;
   float* part = (float*)((char*)workspace + dp.act_bytes);
-  hipError_t e = moe::launch_stream_gate_up(x, dt, w13, rm, 1, H, I_fa, dp.tok_blocks, dp.split_gu,
-                                            act, part, s);
+  hipError_t e =
+      use_gu == MOE_SCHED_RING
+          ? moe::launch_ring_gate_up(x, w13, rm, 1, H, I_fa, T, dp.tok_blocks, dp.ring_split_gu,
+                                     act, part, s)
+          : moe::launch_stream_gate_up(x, dt, w13, rm, 1, H, I_fa, dp.tok_blocks, dp.split_gu, act,
+                                       part, s);
   if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
-  e = moe::launch_stream_down(w2, dt, act, rm, 1, H, I_fa, dp.tok_blocks, dp.split_dn, out, odt,
-                              part, s);
+  e = use_dn == MOE_SCHED_RING
+          ? moe::launch_ring_down(w2, act, rm, 1, H, I_fa, T, dp.tok_blocks, dp.ring_split_dn,
+                                  out, odt, part, s)
+          : moe::launch_stream_down(w2, dt, act, rm, 1, H, I_fa, dp.tok_blocks, dp.split_dn, out,
+                                    odt, part, s);
   return hip_status(e, "dense_ffn_fa down");
 }
 

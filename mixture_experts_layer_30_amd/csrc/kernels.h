@@ -23,6 +23,11 @@ hipError_t launch_combine(const void* y, int ydt, const float* w, const void* sh
 // offsets[e] .. offsets[e] + counts[e] - 1 of the alignment; row r holds pair
 // sorted_ids[r], i.e. token sorted_ids[r] / K.  Dense (counts == nullptr): one
 // "expert" whose row r is token r, for r < dense_rows.
+//
+// min_rows / max_rows (grouped rows; 1 and INT32_MAX by default) restrict the
+// weight-streaming kernels to the experts with min_rows <= count <= max_rows:
+// the LDS-ring kernel takes the experts whose tokens fit its passes and the
+// register-streaming kernel the rest.
 struct RowMap {
   const int32_t* counts;
   const int32_t* offsets;
@@ -31,6 +36,7 @@ struct RowMap {
   int K;
   int64_t dense_rows;
   int block_m;
+  int min_rows, max_rows;
 };
 
 // Weight-streaming schedule.  tok_blocks: 16-token MFMA blocks per pass over
@@ -54,8 +60,31 @@ hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const 
                             int64_t nblocks, int H, int I, void* y, int ydt, int ksplit,
                             float* part, hipStream_t s);
 
+// act[r][i] = silu(g) * u with g, u the in-order sums over z < splits of
+// part[z][r][i] and part[z][r][I + i].
+hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, int I,
+                                 uint16_t* act, hipStream_t s);
+
 // y[r][h] = sum over z < splits (in order) of part[z][r][h], rounded to ydt.
 hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H, void* y,
                               int ydt, hipStream_t s);
+
+// LDS-ring variant of the weight-streaming schedule: bf16 weights and tokens,
+// 128-row weight slabs streamed in 128-k stages by persistent workgroups (one
+// per CU).  *_ok tells whether a shape qualifies; *_splits is the contraction
+// split it uses for `rows` dense rows (part holds [splits][rows][2I] resp.
+// [splits][rows][H] fp32); grouped rows never split.
+bool ring_gate_up_ok(int xdt, int wdt, int H, int I);
+bool ring_down_ok(int wdt, int H, int I);
+int ring_gate_up_splits(int64_t rows, int H, int I);
+int ring_down_splits(int64_t rows, int H, int I);
+// T bounds the rows of any expert; tok_blocks (1, 2, 4) is the 16-token blocks
+// per pass over the weights (an expert with more tokens takes more passes).
+hipError_t launch_ring_gate_up(const void* x, const void* w13, const RowMap& rm, int E, int H,
+                               int I, int64_t T, int tok_blocks, int splits, uint16_t* act,
+                               float* part, hipStream_t s);
+hipError_t launch_ring_down(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H,
+                            int I, int64_t T, int tok_blocks, int splits, void* y, int ydt,
+                            float* part, hipStream_t s);
 
 }  // namespace moe

@@ -1,0 +1,502 @@
+// Weight-streaming grouped SwiGLU FFN, LDS-ring variant for bf16 storage (the
+// decode-shape schedule when weights and tokens are bf16 and the shapes tile).
+//
+// Decode time is the time to read every active expert's weights from HBM once
+// (weight amplification, Serving-tax notes, decode-phase section).  Register
+// loads shaped for the MFMA operands touch half a 128-byte line per row per
+// instruction and read HBM at about 5.8 TB/s on gfx950.  This variant streams
+// the weights with non-temporal direct global->LDS loads
+// (global_load_lds_dwordx4), whose 64 lanes fetch 4 rows x 256 contiguous
+// bytes, through a ring of stages in LDS, and reads the MFMA fragments back
+// from LDS (a small fraction of LDS bandwidth at HBM rates): 6.3-6.6 TB/s.
+//
+// Workgroup = 8 wavefronts, one per CU (the ring takes 144-160 KB of LDS),
+// persistent.  A work unit is one pass of up to 16*NB of an expert's tokens
+// over one contraction slice of one 128-row weight slab; the U units are
+// numbered expert-major and workgroup b takes the contiguous run
+// [U*b/G, U*(b+1)/G), so every workgroup gets the same number of units
+// whatever the experts' loads.  One stage holds, for 128 k, the slab's 128
+// weight rows and the pass's token rows; the load side runs ST-1 stages ahead
+// of the multiply side across unit boundaries, so the ring never drains
+// between units.  Wavefront w owns weight rows 16w..16w+15 of the slab and
+// multiplies them by every token block over the whole slice, so no
+// cross-wavefront reduction is needed.
+//
+//   gate/up: a slab is 64 intermediate columns; wavefront w's 16 rows are
+//            gate and up rows of 8 columns ordered so that each lane's 4
+//            accumulator rows are (gate c, gate c+1, up c, up c+1): the
+//            SwiGLU is applied in registers.
+//   down:    a slab is 128 consecutive output features.
+//
+// The token rows share the stage with the weights, so more token blocks per
+// pass leave fewer stages in flight; the library runs this kernel with one or
+// two blocks and hands experts with more tokens than a pass to the
+// register-streaming kernel (RowMap min_rows / max_rows).
+//
+// Rows of the alignment (token ids, output rows) and the experts' counts are
+// read with scalar loads, which complete on a different counter than the
+// vector loads: waiting for them does not wait for the stages in flight (a
+// vector load of them would, since vector loads complete in order).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kRWaves = 8;
+constexpr int kRThreads = kRWaves * kWave;
+constexpr int kRRows = 128;      // weight rows per slab
+constexpr int kRK = 128;         // contraction elements per stage
+constexpr int kRRowBytes = 256;  // bytes of one row per stage
+constexpr int kRWLoads = 4;      // direct loads per wavefront per stage for its 16 weight rows
+
+// NB: token blocks of 16 per pass.  Stages and token loads per wavefront per
+// stage (every wavefront issues the same number, so one vmcnt bound serves all).
+template <int NB>
+constexpr int ring_stages() { return NB == 4 ? 3 : 4; }
+
+template <int NB>
+constexpr int ring_tok_loads() { return NB == 4 ? 2 : 1; }
+template <int NB>
+constexpr int ring_slot_bytes() { return (kRRows + 16 * NB) * kRRowBytes; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 64 lanes x 16 bytes from global memory (lane's own address) into LDS at
+// lds + 16 * lane, without passing through registers.  kStream marks the data
+// as read once (non-temporal), which on gfx950 raises the HBM read rate of
+// these strided row segments by about 15 % (measured) and keeps them from
+// displacing the token rows in the caches.
+template <bool kStream>
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, kStream ? 2 : 0);
+}
+
+// Byte offset of 16-byte segment s of row r in a stage: segments are permuted
+// by the row's low 4 bits, so the 16 rows a fragment read touches hit 16
+// different 16-byte bank groups.
+__device__ __forceinline__ int roff(int r, int s) { return r * kRRowBytes + ((s ^ (r & 15)) << 4); }
+
+__device__ __forceinline__ void barrier_nf() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct RingWork {
+  int nslabs;   // 128-row slabs per expert
+  int nexp;     // experts (1 for dense rows)
+  int ksplit;   // contraction slices (dense rows only)
+  int nks;      // stages over the whole contraction (Kdim / 128)
+};
+
+// Position in the workgroup's run of work units.  A unit is one pass of up to
+// 16*NB of an expert's tokens over one contraction slice of one 128-row slab;
+// units are numbered expert-major, then slab, slice, pass, and workgroup b
+// takes the contiguous run [U*b/G, U*(b+1)/G) of the U units, so workgroups
+// get equal numbers of units whatever the experts' loads.
+struct RingIt {
+  int left;                // units still to visit, counting the current one
+  int e, slab, z, pass;    // current unit
+  int n, row0, npass;      // tokens of expert e, its first alignment row, its passes
+  int ks, ks0, ks1;        // stage, and the stages of slice z
+};
+
+template <int NB, bool kDense>
+__device__ __forceinline__ void ring_expert(RingIt& it, const RowMap& rm,
+                                            const int32_t* __restrict__ counts,
+                                            const int32_t* __restrict__ offsets) {
+  it.n = kDense ? (int)rm.dense_rows : counts[it.e];
+  it.row0 = kDense ? 0 : offsets[it.e];
+  it.npass = (it.n + 16 * NB - 1) / (16 * NB);
+}
+
+__device__ __forceinline__ void ring_slice(RingIt& it, const RingWork& wk) {
+  it.ks0 = it.z * wk.nks / wk.ksplit;
+  it.ks1 = (it.z + 1) * wk.nks / wk.ksplit;
+  it.ks = it.ks0;
+}
+
+// Advances one stage; at the end of a unit, to the next unit (skipping experts
+// without tokens).  it.left == 0 once the run is done.
+template <int NB, bool kDense>
+__device__ __forceinline__ void ring_next(RingIt& it, const RowMap& rm, const RingWork& wk,
+                                          const int32_t* __restrict__ counts,
+                                          const int32_t* __restrict__ offsets) {
+  if (++it.ks < it.ks1) return;
+  if (--it.left == 0) return;
+  it.ks = it.ks0;
+  if (++it.pass < it.npass) return;
+  it.pass = 0;
+  if (++it.z < wk.ksplit) {
+    ring_slice(it, wk);
+    return;
+  }
+  it.z = 0;
+  ring_slice(it, wk);
+  if (++it.slab < wk.nslabs) return;
+  it.slab = 0;
+  // next expert with units: tokens, and no more than max_rows of them
+  int n;
+  do {
+    ++it.e;
+    n = kDense ? (int)rm.dense_rows : counts[it.e];
+  } while (it.e < wk.nexp - 1 && (n == 0 || (!kDense && n > rm.max_rows)));
+  ring_expert<NB, kDense>(it, rm, counts, offsets);
+}
+
+// kGateUp: w = w13 [E][2I][H], xs = x [T][H], writes act [rows][I] (or fp32 gate/up
+// sums to part [ksplit][rows][2I]).  Down: w = w2 [E][H][I], xs = act, writes
+// y [pairs][H] at the pair of each row (or fp32 sums to part [ksplit][rows][H]).
+// ids / counts / offsets are the plan's sorted_ids, expert_counts and
+// expert_offsets (unused for dense rows); passed as restrict-qualified
+// arguments, their wave-uniform reads compile to scalar loads.
+template <class SY, int NB, bool kGateUp, bool kDense>
+__global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
+    RingWork wk, uint16_t* __restrict__ act, typename SY::T* __restrict__ y,
+    float* __restrict__ part, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets) {
+  constexpr int ST = ring_stages<NB>();
+  constexpr int SB = ring_slot_bytes<NB>();
+  constexpr int TL = ring_tok_loads<NB>();
+  constexpr int L = kRWLoads + TL;  // vector loads per wavefront per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[ST * SB];
+
+  RingIt is;
+  const int lane = threadIdx.x & (kWave - 1);
+  // wave-uniform, so that indices derived from it stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int m = lane & 15, g = lane >> 4;
+  const int G = (int)gridDim.x;
+  const int Kdim = kGateUp ? H : I;      // contraction length
+  const int64_t wrows = kGateUp ? 2 * (int64_t)I : H;  // weight rows per expert
+
+  // Weight row of row t (0..15) of wavefront `wave`'s tile in slab `slab`.
+  auto wrow = [&](int slab, int t) -> int64_t {
+    if (kGateUp) {
+      const int col = slab * 64 + 8 * wave + 2 * (t >> 2) + (t & 1);
+      return ((t >> 1) & 1) * (int64_t)I + col;
+    }
+    return (int64_t)slab * kRRows + 16 * wave + t;
+  };
+  // Row of the token operand for row r (< 16*NB) of the current pass: rows past
+  // the expert's tokens repeat the pass's first row (their products are never
+  // stored).  Gate/up: the token's row of x; down: the row of act.
+  auto tok_row = [&](const RingIt& it, int r) -> int64_t {
+    const int base = it.pass * 16 * NB;
+    const int rr = base + r < it.n ? base + r : base;
+    if (kDense) return rr;
+    if (kGateUp) return ids[it.row0 + rr] / rm.K;
+    return it.row0 + rr;
+  };
+
+  // ---- load side ----
+  // Lane's weight rows for its kRWLoads direct loads (4 rows x 256 B each) and
+  // token rows for its TL loads, refreshed at the first stage of every pass.
+  const uint16_t* wsrc[kRWLoads];
+  const uint16_t* tsrc[TL];
+  auto refresh = [&](const RingIt& it) {
+    const uint16_t* wexp = w + (size_t)it.e * wrows * Kdim;
+#pragma unroll
+    for (int j = 0; j < kRWLoads; ++j) {
+      const int t = 4 * j + g;
+      const int seg = m ^ t;  // logical segment this lane fetches (row t & 15 == t)
+      wsrc[j] = wexp + (size_t)wrow(it.slab, t) * Kdim + seg * 8;
+    }
+    // token rows: NB == 1: rows 2w, 2w+1 (lanes 0..31); NB == 2: rows 4w..4w+3;
+    // NB == 4: rows 4w..4w+3 and 32+4w..32+4w+3.  Uniform per 16 lanes.
+#pragma unroll
+    for (int q = 0; q < TL; ++q) {
+      const int rbase = NB == 1 ? 2 * wave : 4 * wave + 32 * q;
+      constexpr int nr = NB == 1 ? 2 : 4;  // rows of this load (lanes of row i: g == i)
+      int64_t tr = 0;
+#pragma unroll
+      for (int i = 0; i < nr; ++i) {
+        const int64_t ri = tok_row(it, rbase + i);
+        tr = (g & (nr - 1)) == i ? ri : tr;
+      }
+      const int r = kRRows + (NB == 1 ? rbase + (g & 1) : rbase + g);
+      const int seg = m ^ (r & 15);
+      tsrc[q] = xs + (size_t)tr * Kdim + seg * 8;
+    }
+  };
+  auto issue = [&](const RingIt& it, int slot) {
+    uint8_t* sl = ring + slot * SB;
+    const size_t k = (size_t)it.ks * kRK;
+#pragma unroll
+    for (int j = 0; j < kRWLoads; ++j)
+      load_lds16<true>(wsrc[j] + k, sl + (16 * wave + 4 * j) * kRRowBytes);
+#pragma unroll
+    for (int q = 0; q < TL; ++q) {
+      const int rbase = kRRows + (NB == 1 ? 2 * wave : 4 * wave + 32 * q);
+      if (NB > 1 || lane < 32)
+        load_lds16<false>(tsrc[q] + k, sl + rbase * kRRowBytes);
+    }
+  };
+
+  // ---- this workgroup's run of units ----
+  {
+    // units per expert, scanned across the workgroup (E <= 256 < kRThreads),
+    // in LDS that the ring only uses after the barrier below
+    int* sc = reinterpret_cast<int*>(ring);
+    const int t = threadIdx.x;
+    int u = 0;
+    if (t < wk.nexp) {
+      const int n = kDense ? (int)rm.dense_rows : counts[t];
+      if (kDense || n <= rm.max_rows) u = (n + 16 * NB - 1) / (16 * NB) * wk.nslabs * wk.ksplit;
+    }
+    int incl = u;  // inclusive scan within the wavefront
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += v;
+    }
+    if (lane == kWave - 1) sc[kRThreads + wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < kRWaves; ++v) {
+      const int sv = sc[kRThreads + v];
+      before += v < wave ? sv : 0;
+      total += sv;
+    }
+    incl += before;
+    const int b = (int)blockIdx.x;
+    const int u0 = (int)((int64_t)total * b / G), u1 = (int)((int64_t)total * (b + 1) / G);
+    if (u > 0 && incl - u <= u0 && u0 < incl) {  // the expert holding unit u0
+      sc[kRThreads + kRWaves] = t;
+      sc[kRThreads + kRWaves + 1] = u0 - (incl - u);
+    }
+    __syncthreads();
+    is.left = u1 - u0;
+    if (is.left > 0) {
+      is.e = sc[kRThreads + kRWaves];
+      const int r = sc[kRThreads + kRWaves + 1];
+      ring_expert<NB, kDense>(is, rm, counts, offsets);
+      is.pass = r % is.npass;
+      const int q = r / is.npass;
+      is.z = q % wk.ksplit;
+      is.slab = q / wk.ksplit;
+      ring_slice(is, wk);
+    }
+    __syncthreads();  // the scan's LDS is the ring's first slot
+  }
+  if (is.left == 0) return;
+  RingIt ic = is;
+
+  int issued = 0;
+#pragma unroll
+  for (int d = 0; d < ST - 1; ++d) {
+    if (is.left > 0) {
+      if (is.ks == is.ks0) refresh(is);
+      issue(is, d);
+      ++issued;
+      ring_next<NB, kDense>(is, rm, wk, counts, offsets);
+    }
+  }
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int computed = 0, slot_c = 0, slot_i = ST - 1;
+
+  while (ic.left > 0) {
+    // stage `computed` has landed for this wavefront; the barrier makes every
+    // wavefront's loads of it visible and retires every read of the slot
+    // about to be refilled (last used by stage computed - 1)
+    if (issued - computed - 1 >= ST - 2) wait_vm<(ST - 2) * L>();
+    else wait_vm<0>();
+    barrier_nf();
+    if (is.left > 0) {
+      if (is.ks == is.ks0) refresh(is);
+      issue(is, slot_i);
+      ++issued;
+      slot_i = slot_i + 1 == ST ? 0 : slot_i + 1;
+      ring_next<NB, kDense>(is, rm, wk, counts, offsets);
+    }
+
+    const int ntb = min(NB, (ic.n - ic.pass * 16 * NB + 15) / 16);
+    const uint8_t* sl = ring + slot_c * SB;
+#pragma unroll
+    for (int kk = 0; kk < kRK / 32; ++kk) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sl + roff(16 * wave + m, 4 * kk + g));
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) {
+        if (tb < ntb) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(sl + roff(kRRows + 16 * tb + m, 4 * kk + g));
+          acc[tb] = mfma16x16x32(a, b, acc[tb]);
+        }
+      }
+    }
+    ++computed;
+    slot_c = slot_c + 1 == ST ? 0 : slot_c + 1;
+
+    if (ic.ks + 1 == ic.ks1) {
+      // epilogue of the pass: lane holds rows 4g..4g+3 of its tile for token m of each block
+      const int base = ic.pass * 16 * NB;
+      const int rows = kDense ? (int)rm.dense_rows : 0;
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) {
+        if (tb < ntb) {
+          const int j = base + 16 * tb + m;  // row of the pass within the expert
+          const f32x4 v = acc[tb];
+          if (kGateUp) {
+            if (j < ic.n) {
+              const int64_t row = (int64_t)ic.row0 + j;
+              const int c = ic.slab * 64 + 8 * wave + 2 * g;
+              if (part) {
+                float* pr = part + ((size_t)ic.z * rows + row) * (2 * (size_t)I);
+                pr[c] = v.x;
+                pr[c + 1] = v.y;
+                pr[I + c] = v.z;
+                pr[I + c + 1] = v.w;
+              } else {
+                *reinterpret_cast<uint32_t*>(act + row * I + c) =
+                    pack_bf16x2(silu(v.x) * v.z, silu(v.y) * v.w);
+              }
+            }
+          } else {
+            // output row of each token column (pair index for grouped rows)
+            int64_t dst;
+            if (kDense) {
+              dst = j;
+            } else {
+              const int jb = base + 16 * tb;
+              const int last = ic.n - 1 - jb;  // last valid column of this block
+              int d = 0;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int di = ids[ic.row0 + jb + (i < last ? i : last)];
+                d = m == i ? di : d;
+              }
+              dst = d;
+            }
+            if (j < ic.n) {
+              const int h = ic.slab * kRRows + 16 * wave + 4 * g;
+              if (part) {
+                *reinterpret_cast<f32x4*>(part + ((size_t)ic.z * rows + dst) * H + h) = v;
+              } else {
+                typename SY::T* o = y + (size_t)dst * H + h;
+                store_out<SY>(o + 0, v.x);
+                store_out<SY>(o + 1, v.y);
+                store_out<SY>(o + 2, v.z);
+                store_out<SY>(o + 3, v.w);
+              }
+            }
+          }
+        }
+        acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    ring_next<NB, kDense>(ic, rm, wk, counts, offsets);
+  }
+}
+
+namespace {
+
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+// Contraction slices for dense rows: the count minimising the stages on the
+// critical path (rounds of G slab slices x stages per slice) plus the fp32 partial
+// sums' round trip, in units of one stage of all G workgroups.
+int ring_splits(int nslabs, int nks, int64_t rows, int outdim, int G) {
+  int best = 1;
+  double best_t = 1e30;
+  const double stage_bytes = (double)kRRows * kRRowBytes * G;
+  for (int ks = 1; ks <= 16 && ks * 4 <= nks; ++ks) {
+    const int64_t items = (int64_t)nslabs * ks;
+    double t = (double)((items + G - 1) / G) * ((nks + ks - 1) / ks);
+    if (ks > 1) t += 2.0 * ks * rows * outdim * 4 / stage_bytes;
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = ks;
+    }
+  }
+  return best;
+}
+
+template <class SY, int NB, bool kGateUp, bool kDense>
+void ring_go(const void* w, const void* xs, const RowMap& rm, int E, int H, int I, int ksplit,
+             int64_t rows_bound, uint16_t* act, void* y, float* part, hipStream_t s) {
+  RingWork wk;
+  wk.nslabs = kGateUp ? I / 64 : H / kRRows;
+  wk.nexp = kDense ? 1 : E;
+  wk.ksplit = ksplit;
+  wk.nks = (kGateUp ? H : I) / kRK;
+  // units: at most every expert x slab x slice x pass of T tokens
+  const int64_t most = (int64_t)wk.nexp * wk.nslabs * ksplit * ((rows_bound + 16 * NB - 1) / (16 * NB));
+  const int G = (int)(most < num_cus() ? most : num_cus());
+  if (G <= 0) return;
+  hipLaunchKernelGGL((ring_ffn_kernel<SY, NB, kGateUp, kDense>), dim3(G), dim3(kRThreads), 0, s,
+                     static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(xs), rm, H, I,
+                     wk, act, static_cast<typename SY::T*>(y), ksplit > 1 ? part : nullptr,
+                     rm.sorted_ids, rm.counts, rm.offsets);
+}
+
+template <class SY, bool kGateUp, bool kDense>
+void ring_nb(const void* w, const void* xs, const RowMap& rm, int E, int H, int I, int64_t T,
+             int tok_blocks, int ksplit, uint16_t* act, void* y, float* part, hipStream_t s) {
+  if (tok_blocks <= 1)
+    ring_go<SY, 1, kGateUp, kDense>(w, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+  else if (tok_blocks == 2)
+    ring_go<SY, 2, kGateUp, kDense>(w, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+  else
+    ring_go<SY, 4, kGateUp, kDense>(w, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+}
+
+}  // namespace
+
+bool ring_gate_up_ok(int xdt, int wdt, int H, int I) {
+  return xdt == kDtBF16 && wdt == kDtBF16 && H % kRK == 0 && I % 64 == 0;
+}
+
+bool ring_down_ok(int wdt, int H, int I) { return wdt == kDtBF16 && H % kRRows == 0 && I % kRK == 0; }
+
+// (sized for 256 CUs, MI355X's count, so that workspace sizes do not depend on
+// the device queried)
+int ring_gate_up_splits(int64_t rows, int H, int I) { return ring_splits(I / 64, H / kRK, rows, 2 * I, 256); }
+
+int ring_down_splits(int64_t rows, int H, int I) { return ring_splits(H / kRRows, I / kRK, rows, H, 256); }
+
+hipError_t launch_ring_gate_up(const void* x, const void* w13, const RowMap& rm, int E, int H,
+                               int I, int64_t T, int tok_blocks, int splits, uint16_t* act,
+                               float* part, hipStream_t s) {
+  if (rm.counts == nullptr)
+    ring_nb<BF16, true, true>(w13, x, rm, E, H, I, T, tok_blocks, splits, act, nullptr, part, s);
+  else
+    ring_nb<BF16, true, false>(w13, x, rm, E, H, I, T, tok_blocks, 1, act, nullptr, nullptr, s);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && rm.counts == nullptr && splits > 1)
+    e = launch_finish_gate_up(part, splits, rm.dense_rows, I, act, s);
+  return e;
+}
+
+hipError_t launch_ring_down(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H,
+                            int I, int64_t T, int tok_blocks, int splits, void* y, int ydt,
+                            float* part, hipStream_t s) {
+  const bool dense = rm.counts == nullptr;
+  if (!dense) splits = 1;
+  if (ydt == kDtF32) {
+    if (dense) ring_nb<F32, false, true>(w2, act, rm, E, H, I, T, tok_blocks, splits, nullptr, y, part, s);
+    else ring_nb<F32, false, false>(w2, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y, nullptr, s);
+  } else {
+    if (dense) ring_nb<BF16, false, true>(w2, act, rm, E, H, I, T, tok_blocks, splits, nullptr, y, part, s);
+    else ring_nb<BF16, false, false>(w2, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y, nullptr, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && splits > 1) e = launch_finish_down(part, splits, rm.dense_rows, H, y, ydt, s);
+  return e;
+}
+
+}  // namespace moe

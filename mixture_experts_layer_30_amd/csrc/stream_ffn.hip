@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void str
   __shared__ StreamSmem sm;
   const int e = blockIdx.y;
   const Bucket bk = bucket_of<kDense>(rm, e);
-  if (bk.n == 0) return;
+  if (bk.n == 0 || (!kDense && bk.n < rm.min_rows)) return;
   constexpr bool dense = kDense;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void str
   __shared__ StreamSmem sm;
   const int e = blockIdx.y;
   const Bucket bk = bucket_of<kDense>(rm, e);
-  if (bk.n == 0) return;
+  if (bk.n == 0 || (!kDense && bk.n < rm.min_rows)) return;
   constexpr bool dense = kDense;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -387,11 +387,7 @@ hipError_t launch_stream_gate_up(const void* x, int xdt, const void* w13, const 
   float* p = splits > 1 ? part : nullptr;
   if (xdt == kDtF32) gu_tb<F32>(x, w13, rm, E, H, I, tok_blocks, splits, act, p, s);
   else gu_tb<BF16>(x, w13, rm, E, H, I, tok_blocks, splits, act, p, s);
-  if (splits > 1) {
-    const int64_t n = rm.dense_rows * I;
-    hipLaunchKernelGGL(finish_gate_up_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       part, splits, rm.dense_rows, I, act);
-  }
+  if (splits > 1) return launch_finish_gate_up(part, splits, rm.dense_rows, I, act, s);
   return hipGetLastError();
 }
 
@@ -407,6 +403,14 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
     else dn_tb<BF16, BF16>(w2, act, rm, E, H, I, tok_blocks, splits, y, p, s);
   }
   if (splits > 1) return launch_finish_down(part, splits, rm.dense_rows, H, y, ydt, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, int I,
+                                 uint16_t* act, hipStream_t s) {
+  const int64_t n = rows * I;
+  hipLaunchKernelGGL(finish_gate_up_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     part, splits, rows, I, act);
   return hipGetLastError();
 }
 

@@ -317,6 +317,74 @@ def test_layer_parity_forced_schedule(shape, T, routing, block_m, sched):
     assert rel_err(fa, oracle.dense_ffn(d["x"], d["wfa13"], d["wfa2"])) <= TOL
 
 
+RING_SHAPES = [
+    # (shape, T, routing): one and two 16-token blocks per pass; experts busier than
+    # a pass (handed to the register-streaming kernel); more work than workgroups
+    (LayerShape("ring_nb1", 256, 256, 8, 2, 128, "bf16", (6,), ("uniform",)), 6, "uniform"),
+    (LayerShape("ring_nb2", 384, 128, 4, 2, 0, "bf16", (30,), ("zipf",)), 30, "zipf"),
+    (LayerShape("ring_hot_experts", 256, 256, 8, 2, 256, "bf16", (300,), ("zipf",)), 300, "zipf"),
+    (LayerShape("ring_items", 128, 512, 64, 6, 0, "bf16", (50,), ("uniform",)), 50, "uniform"),
+]
+
+
+@pytest.mark.parametrize("shape,T,routing", RING_SHAPES, ids=[s[0].name for s in RING_SHAPES])
+@pytest.mark.parametrize("block_m", [16, 128])
+def test_layer_parity_ring(shape, T, routing, block_m):
+    """The LDS-ring streaming schedule forced on every half (routed experts,
+    shared expert and DenseFA, whose down projection splits its contraction)."""
+    d, dev = layer_case(shape, T, routing, seed=11)
+    layer = MoELayer(shape, dev, block_m=block_m, sched=B.SCHED_RING)
+    out = layer.forward().clone()
+    fa = layer.dense_fa().clone()
+    torch.cuda.synchronize()
+    ref, rids, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], shape.topk,
+                                    d["ws13"], d["ws2"])
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    assert rel_err(out, ref) <= TOL
+    assert rel_err(fa, oracle.dense_ffn(d["x"], d["wfa13"], d["wfa2"])) <= TOL
+    out2 = layer.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+DENSE_RING_CASES = [
+    # (T, H, I): down projection split 8 ways (32 stages, 2 slabs); several token
+    # blocks; a ragged last block; two passes of four blocks
+    (1, 256, 4096),
+    (40, 128, 1024),
+    (17, 512, 640),
+    (100, 256, 512),
+]
+
+
+@pytest.mark.parametrize("T,H,I", DENSE_RING_CASES)
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_dense_ffn_ring_parity(T, H, I, odt):
+    x = synth.tokens(T, H, "bf16", seed=I + 1)
+    w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T + 1)
+    ref = oracle.swiglu(x, w13, w2)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(T, H, I), dtype=torch.uint8, device=DEV)
+    xd, w13d, w2d = x.to(DEV), w13.to(DEV), w2.to(DEV)
+    out = torch.empty(T, H, dtype=odt, device=DEV)
+    B.dense_ffn_fa(xd, w13d, w2d, ws, out, sched=B.SCHED_RING)
+    out2 = torch.empty_like(out)
+    B.dense_ffn_fa(xd, w13d, w2d, ws, out2, sched=B.SCHED_RING)
+    torch.cuda.synchronize()
+    assert rel_err(out, ref) <= TOL
+    assert torch.equal(out, out2)
+
+
+def test_ring_schedule_rejects_unsupported_shape():
+    shape = SMALL_SHAPES[1][0]   # I = 320: the down projection's I is not a multiple of 128
+    d, dev = layer_case(shape, 40, "zipf")
+    layer = MoELayer(shape, dev, sched=B.SCHED_RING)
+    layer.route()
+    layer.align()
+    layer.gate_up()
+    with pytest.raises(B.MoEError):
+        layer.down()
+
+
 def test_tile_schedule_rejects_unsupported_block():
     shape = TILE_SHAPES[1][0]
     d, dev = layer_case(shape, 40, "zipf")
