@@ -63,6 +63,17 @@ def measured_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
+def gate_up_kernel(shape, T, block_m):
+    """The kernel the library's automatic schedule runs for the gate/up half
+    (mirrors the choice made in the C ABI; for the record only)."""
+    H, I, K, E = shape.hidden, shape.inter, shape.topk, shape.experts
+    if block_m in (64, 128) and H % 128 == 0 and T * K >= 64 * E:
+        return "tile2_ffn_kernel (MFMA tiles through an LDS ring)"
+    if shape.dtype == "bf16" and H % 128 == 0 and I % 64 == 0:
+        return "ring_ffn_kernel (LDS-ring weight streaming, gate/up + SwiGLU)"
+    return "stream_gate_up_kernel (register weight streaming, gate/up + SwiGLU)"
+
+
 def algorithmic(shape, T, e_active):
     """Unpadded algorithmic bytes and flops (weights of active experts read once)."""
     H, I, K, Is = shape.hidden, shape.inter, shape.topk, shape.shared_inter
@@ -200,7 +211,7 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
     workload = f"{name} T={T} {routing}"
     traffic = measured_traffic(workload)
     roof["traffic"] = traffic
-    roof["kernel"] = "moe_grouped_gate_up (gate/up GEMM + SwiGLU)"
+    roof["kernel"] = gate_up_kernel(shape, T, layer.block_m)
     roof["algorithmic_bytes"] = alg["gu_bytes"]
     roof["algorithmic_flops"] = alg["gu_flops"]
     roof["avg_launch_us"] = round(gu_ms * 1e3, 2)
