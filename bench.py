@@ -9,8 +9,10 @@ combine.  W untimed steps, then exactly K timed steps between two device
 synchronisations.  Prints one JSON line with tokens/s (the layer's T tokens
 per step), the roofline of the dominant kernel (the grouped gate/up GEMM,
 timed live with HIP events on the stream it runs on), the tax tau against the
-FLOP-matched dense FFN (DenseFA) timed the same way, and the CPU oracle timed
-on the host's cores on a bounded sample of the same workload.
+FLOP-matched dense FFN (DenseFA) timed the same way (and against DensePA, the
+parameter-matched one), the analytic tax model's prediction with MI355X
+constants, and the CPU oracle timed on the host's cores on a bounded sample of
+the same workload.
 """
 import argparse
 import hashlib
@@ -25,7 +27,7 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from mixture_experts_layer_30_amd import configs, synth  # noqa: E402
+from mixture_experts_layer_30_amd import configs, synth, taxmodel  # noqa: E402
 from mixture_experts_layer_30_amd.layer import MoELayer  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
@@ -85,8 +87,11 @@ def algorithmic(shape, T, e_active):
     layer_flops = 6 * T * K * H * I + 6 * T * H * Is
     fa_bytes = 3 * H * shape.dense_fa_inter * eb + 2 * T * H * eb
     fa_flops = 6 * T * H * shape.dense_fa_inter
+    pa_bytes = 3 * H * shape.dense_pa_inter * eb + 2 * T * H * eb
+    pa_flops = 6 * T * H * shape.dense_pa_inter
     return dict(gu_bytes=gu_bytes, layer_bytes=layer_bytes, gu_flops=gu_flops,
-                layer_flops=layer_flops, fa_bytes=fa_bytes, fa_flops=fa_flops)
+                layer_flops=layer_flops, fa_bytes=fa_bytes, fa_flops=fa_flops,
+                pa_bytes=pa_bytes, pa_flops=pa_flops)
 
 
 def time_steps(fn, steps, warmup, mid=None):
@@ -116,6 +121,28 @@ def time_steps(fn, steps, warmup, mid=None):
     if evs:
         kern_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
     return gpu_ms / steps, wall * 1e3 / steps, kern_ms
+
+
+def time_flushed(fn, steps):
+    """Per-call device times (HIP events) with a 512 MiB write between calls,
+    outside the events, so no call finds its weights in the 256 MB Infinity
+    Cache; returns median, p10 and p90 in ms."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fn()
+    torch.cuda.synchronize()
+    pairs = []
+    for i in range(steps):
+        scratch.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    del scratch
+    return {"median_ms": round(float(np.median(ms)), 4), "p10_ms": round(float(np.percentile(ms, 10)), 4),
+            "p90_ms": round(float(np.percentile(ms, 90)), 4)}
 
 
 def breakdown(layer, reps=10):
@@ -171,7 +198,7 @@ def cpu_baseline(shape, dev_inputs, T, budget_s=20.0):
 def run_workload(name, T, routing, steps, warmup, do_cpu):
     shape = configs.CONFIGS[name]
     torch.manual_seed(0)
-    d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=True)
+    d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=True, densepa=True)
     layer = MoELayer(shape, d)
     layer.forward()
     torch.cuda.synchronize()
@@ -194,7 +221,12 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
 
     ms, wall_ms, gu_ms = time_steps(step, steps, warmup, mid=True)
     fa_ms, _, _ = time_steps(layer.dense_fa, steps, warmup)
+    pa_ms, _, _ = time_steps(layer.dense_pa, steps, warmup)
     bd = breakdown(layer)
+    fl_moe = time_flushed(layer.forward, steps)
+    fl_fa = time_flushed(layer.dense_fa, steps)
+    model = taxmodel.tax(shape, T, e_active=e_active)
+    model_uniform = taxmodel.tax(shape, T)
 
     dtype = "f32" if shape.dtype == "f32" else "bf16"
     gu_s = gu_ms * 1e-3
@@ -244,7 +276,27 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
         "tau": round(ms / fa_ms, 4),
         "dense_fa": {"ms": round(fa_ms, 4), "inter": shape.dense_fa_inter,
                      "achieved_GBps": round(alg["fa_bytes"] / (fa_ms * 1e-3) / 1e9, 1),
-                     "achieved_TFLOPs": round(alg["fa_flops"] / (fa_ms * 1e-3) / 1e12, 2)},
+                     "achieved_TFLOPs": round(alg["fa_flops"] / (fa_ms * 1e-3) / 1e12, 2),
+                     "hbm_frac": round(alg["fa_bytes"] / (fa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_frac": round(alg["fa_flops"] / (fa_ms * 1e-3) / 1e12 / peak_flops, 4)},
+        "tau_pa": round(ms / pa_ms, 4),
+        "dense_pa": {"ms": round(pa_ms, 4), "inter": shape.dense_pa_inter,
+                     "achieved_GBps": round(alg["pa_bytes"] / (pa_ms * 1e-3) / 1e9, 1),
+                     "achieved_TFLOPs": round(alg["pa_flops"] / (pa_ms * 1e-3) / 1e12, 2)},
+        "per_call_flushed": {"moe_layer": fl_moe, "dense_fa": fl_fa,
+                             "tau_median": round(fl_moe["median_ms"] / fl_fa["median_ms"], 4)},
+        "tax_model": {"constants": {"hbm_GBps": taxmodel.MI355X_HBM_BPS / 1e9,
+                                    "bf16_TFLOPs": taxmodel.MI355X_BF16_FLOPS / 1e12,
+                                    "eta": model["eta"]},
+                      "e_active_measured": e_active,
+                      "e_active_uniform": round(model_uniform["e_active"], 3),
+                      "regime": model["regime"],
+                      "tau_fa_pred": round(model["tau_fa"], 4),
+                      "tau_fa_pred_uniform": round(model_uniform["tau_fa"], 4),
+                      "tau_pa_pred": round(model["tau_pa"], 4),
+                      "tau_fa_rel_err": round(model["tau_fa"] / (ms / fa_ms) - 1, 4),
+                      "t_moe_pred_ms": round(model["t_moe_s"] * 1e3, 4),
+                      "t_densefa_pred_ms": round(model["t_densefa_s"] * 1e3, 4)},
     }
     if do_cpu:
         rec["cpu_baseline"] = cpu_baseline(shape, d, T)

@@ -6,8 +6,9 @@ enqueues the library's kernels on the current stream:
   moe_route -> moe_align -> moe_grouped_gate_up -> moe_grouped_down
   [-> dense_ffn_fa for the shared experts] -> moe_combine
 
-and the DenseFA baseline is one dense_ffn_fa call.  The tax of the
-Serving-tax notes (section "定義", Eq. 1) is tau = T(MoE, b) / T(DenseFA, b).
+and the DenseFA baseline is one dense_ffn_fa call (DensePA, the dense FFN
+with the MoE's parameter count, another one of width E*I + I_s).  The tax of
+the Serving-tax notes (section "定義", Eq. 1) is tau = T(MoE, b) / T(DenseFA, b).
 """
 import torch
 
@@ -43,6 +44,10 @@ class MoELayer:
         if inputs.get("wfa13") is not None:
             self.fa_out = torch.empty(T, H, dtype=out_dtype or x.dtype, device=dev)
             self.fa_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, H, shape.dense_fa_inter), 16),
+                                     dtype=torch.uint8, device=dev)
+        if inputs.get("wpa13") is not None:
+            self.pa_out = torch.empty(T, H, dtype=out_dtype or x.dtype, device=dev)
+            self.pa_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, H, shape.dense_pa_inter), 16),
                                      dtype=torch.uint8, device=dev)
 
     # the five steps, callable one by one (the benchmark times them separately)
@@ -82,3 +87,8 @@ class MoELayer:
         B.dense_ffn_fa(self.inputs["x"], self.inputs["wfa13"], self.inputs["wfa2"], self.fa_ws,
                        self.fa_out, self.sched)
         return self.fa_out
+
+    def dense_pa(self):
+        B.dense_ffn_fa(self.inputs["x"], self.inputs["wpa13"], self.inputs["wpa2"], self.pa_ws,
+                       self.pa_out, self.sched)
+        return self.pa_out

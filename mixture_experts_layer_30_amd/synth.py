@@ -72,8 +72,9 @@ def swiglu_weights(n_out_inter, H, dtype="bf16", seed=0, device="cpu", prefix="w
     return w13, w2
 
 
-def layer_inputs(shape, T, routing=None, seed=0, device="cpu", dense=True, moe=True):
-    """All inputs of one MoE layer pass (and its DenseFA baseline) for a LayerShape."""
+def layer_inputs(shape, T, routing=None, seed=0, device="cpu", dense=True, moe=True,
+                 densepa=False):
+    """All inputs of one MoE layer pass (and its DenseFA / DensePA baselines) for a LayerShape."""
     routing = routing or shape.routing[0]
     d = {"T": T, "routing": routing}
     d["x"] = tokens(T, shape.hidden, shape.dtype, seed, device)
@@ -89,4 +90,7 @@ def layer_inputs(shape, T, routing=None, seed=0, device="cpu", dense=True, moe=T
     if dense:
         d["wfa13"], d["wfa2"] = swiglu_weights(shape.dense_fa_inter, shape.hidden, shape.dtype, seed,
                                                device, "densefa_w")
+    if densepa:
+        d["wpa13"], d["wpa2"] = swiglu_weights(shape.dense_pa_inter, shape.hidden, shape.dtype, seed,
+                                               device, "densepa_w")
     return d

@@ -385,6 +385,21 @@ def test_ring_schedule_rejects_unsupported_shape():
         layer.down()
 
 
+@pytest.mark.parametrize("T", [5, 40, 300])
+def test_dense_pa_parity(T):
+    """DensePA (width E*I + I_s, the MoE's parameter count) through dense_ffn_fa."""
+    shape = LayerShape("pa_small", 256, 192, 8, 2, 128, "bf16", (T,), ("uniform",))
+    d = synth.layer_inputs(shape, T, seed=7, device="cpu", dense=False, moe=False, densepa=True)
+    dev = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in d.items()}
+    pa_ws = torch.empty(B.dense_ffn_workspace_bytes(T, shape.hidden, shape.dense_pa_inter),
+                        dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, shape.hidden, dtype=torch.bfloat16, device=DEV)
+    B.dense_ffn_fa(dev["x"], dev["wpa13"], dev["wpa2"], pa_ws, out)
+    torch.cuda.synchronize()
+    assert dev["wpa13"].shape[0] == 2 * shape.dense_pa_inter
+    assert rel_err(out, oracle.dense_ffn(d["x"], d["wpa13"], d["wpa2"])) <= TOL
+
+
 def test_tile_schedule_rejects_unsupported_block():
     shape = TILE_SHAPES[1][0]
     d, dev = layer_case(shape, 40, "zipf")
@@ -455,7 +470,8 @@ FULL_CASES = [
 def test_layer_parity_full_size_sampled(name, T, routing):
     shape = configs.CONFIGS[name]
     print(f"\n[full-size parity] {name} T={T} {routing}", flush=True)
-    dev = synth.layer_inputs(shape, T, routing, seed=0, device=DEV, dense=(name == "mixtral"))
+    dev = synth.layer_inputs(shape, T, routing, seed=0, device=DEV, dense=(name == "mixtral"),
+                             densepa=(name == "mixtral" and T == 32))
     layer = MoELayer(shape, dev)
     out = layer.forward()
     torch.cuda.synchronize()
@@ -479,5 +495,10 @@ def test_layer_parity_full_size_sampled(name, T, routing):
         x = dev["x"][tokens].cpu()
         ref_fa = oracle.dense_ffn(x, dev["wfa13"].cpu(), dev["wfa2"].cpu())
         assert rel_err(fa[tokens], ref_fa) <= TOL
+    if "wpa13" in dev:   # DensePA: the dense FFN of width E*I holding the MoE's parameter count
+        pa = layer.dense_pa()
+        torch.cuda.synchronize()
+        ref_pa = oracle.dense_ffn(dev["x"][tokens].cpu(), dev["wpa13"].cpu(), dev["wpa2"].cpu())
+        assert rel_err(pa[tokens], ref_pa) <= TOL
     del dev, layer
     torch.cuda.empty_cache()
