@@ -69,7 +69,7 @@ def gate_up_kernel(shape, T, block_m):
     """The kernel the library's automatic schedule runs for the gate/up half
     (mirrors the choice made in the C ABI; for the record only)."""
     H, I, K, E = shape.hidden, shape.inter, shape.topk, shape.experts
-    if block_m in (64, 128) and H % 128 == 0 and T * K >= 64 * E:
+    if block_m in (64, 128) and H % 128 == 0 and T * K >= 24 * E:
         return "tile2_ffn_kernel (MFMA tiles through an LDS ring)"
     if shape.dtype == "bf16" and H % 128 == 0 and I % 64 == 0:
         return "ring_ffn_kernel (LDS-ring weight streaming, gate/up + SwiGLU)"

@@ -121,11 +121,12 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   p.tok_blocks = stream_tok_blocks(T);
   p.split_gu = pick_splits(I / 32, H / 64);
   p.split_dn = pick_splits(H / 64, I / 64);
-  // tiled: 256-token blocks where the 256-row bf16 tile covers both halves and there are
-  // at least two of them (each weight tile then read once per 256 tokens); the down
-  // projection, H/256 tiles per block, is split when that leaves fewer than 256 workgroups
+  // tiled: 256-token blocks where the 256-row bf16 tile covers both halves and more than
+  // 128 rows come (each weight tile then read once per 256 tokens; measured faster than
+  // 128-token blocks from 192 rows up); the down projection, H/256 tiles per block, is
+  // split when that leaves fewer than 256 workgroups
   const bool tile2 = dt == MOE_BF16 && I % 128 == 0 && H % 256 == 0;
-  p.tile_block = (tile2 && T >= 512) ? 256 : 128;
+  p.tile_block = (tile2 && T > 128) ? 256 : 128;
   p.tile_split = 1;
   if (tile2) {
     const int64_t items = (int64_t)(H / 256) * ((T + p.tile_block - 1) / p.tile_block);
@@ -154,9 +155,10 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
 
 // The tiled schedule needs tiles that hold one expert's rows (block 64 or 128)
 // and 128-row output tiles of the down projection (H a multiple of 128).  Auto
-// picks it once an expert holds a tile's worth of tokens on average (the MFMA-
-// bound regime); below that the weight-streaming schedule, which reads every
-// active expert's weights once, is faster.
+// picks it once experts average kTileFrom tokens: measured on MI355X, from
+// there one pass of a tile over each weight tile beats the weight-streaming
+// schedules, whose passes hold at most 32 (ring) or 64 (register) tokens.
+constexpr int kTileFrom = 24;
 bool tile_ok(int block_m, int H) { return (block_m == 64 || block_m == 128) && H % 128 == 0; }
 
 moe_status pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m, int H,
@@ -169,7 +171,8 @@ moe_status pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m,
   } else if (req == MOE_SCHED_STREAM || req == MOE_SCHED_RING) {
     *out = req;
   } else if (req == MOE_SCHED_AUTO) {
-    *out = (tile_ok(block_m, H) && T * K >= 64 * (int64_t)E) ? MOE_SCHED_TILE : MOE_SCHED_STREAM;
+    *out = (tile_ok(block_m, H) && T * K >= kTileFrom * (int64_t)E) ? MOE_SCHED_TILE
+                                                                     : MOE_SCHED_STREAM;
   } else {
     return fail(MOE_EINVAL, "schedule %d", (int)req);
   }
@@ -409,13 +412,13 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   rm.min_rows = 1;
   rm.max_rows = INT32_MAX;
   hipStream_t s = (hipStream_t)stream;
-  // dense rows form one expert; the tiled schedule takes them in 128-row blocks
-  // and is chosen from two blocks up (with a single block its down projection
-  // has only H/128 workgroups; the split-K streaming schedule does better)
+  // dense rows form one expert; auto: the LDS ring up to 32 rows (one pass of
+  // two token blocks), the tiled schedule above (measured: from 48 rows it
+  // reads the weights once where the streaming passes would read them twice)
   moe_schedule use;
   st = pick_schedule(sched, T, 1, 1, 128, H, &use);
   if (st) return st;
-  if (sched == MOE_SCHED_AUTO && T < 256) use = MOE_SCHED_STREAM;
+  if (sched == MOE_SCHED_AUTO) use = (T <= 32 || !tile_ok(128, H)) ? MOE_SCHED_STREAM : MOE_SCHED_TILE;
   const DensePlan dp = dense_plan(T, H, I_fa, dt);
   if (use == MOE_SCHED_TILE) {
     uint16_t* act = (uint16_t*)workspace;

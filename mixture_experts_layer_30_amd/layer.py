@@ -16,9 +16,12 @@ from . import binding as B
 
 
 def default_block_m(T, K, E):
-    """Padding block: 128 (the grouped-GEMM M tile) once experts hold a tile's
-    worth of tokens on average, else 16 (one MFMA token block)."""
-    return 128 if T * K >= 64 * E else 16
+    """Padding block: 16 (one MFMA token block) for the streaming schedules,
+    64 or 128 (the tile's token block) once experts average 24 tokens, the
+    tiled schedule's range; 128 from 96 tokens on average (measured crossover)."""
+    if T * K >= 96 * E:
+        return 128
+    return 64 if T * K >= 24 * E else 16
 
 
 class MoELayer:
