@@ -196,21 +196,22 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
 
 // ---------------------------------------------------------------------------
 // Second-generation tile for bf16 storage: 256 weight rows x BN tokens per
-// workgroup (BN = 128, or 256 for dense rows), NW wavefronts in an NW/2 x 2
-// grid, each owning a (256 / (NW/2)) x BN/2 register tile, and an ST-stage LDS
-// ring filled by direct global->LDS loads (global_load_lds_dwordx4), so ST-1
-// steps of loads are in flight while one is multiplied without spending
-// registers on staging.  8 wavefronts (2 per SIMD, 64 x 64 register tiles)
-// measure faster than 4 wavefronts of 128-row tiles, which leave one wave per
-// SIMD to hide the load latency.  The loop is bound by the loads that miss L2
-// (the part of a step's working set not already fetched by another workgroup
-// of the same XCD), not by the matrix cores.
+// workgroup (BN = block_m: 64 or 128, or 256 for dense rows), NW wavefronts in
+// an NW/2 x 2 grid, each owning a (256 / (NW/2)) x BN/2 register tile, and an
+// ST-stage LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4), so ST-1 steps of loads are in flight while one is
+// multiplied without spending registers on staging.  8 wavefronts (2 per
+// SIMD) measure faster than 4, which leave one wave per SIMD to hide the load
+// latency.  Measured and not kept: 32-deep steps with four stages for
+// 256-token blocks, and 256-token workgroups over two 128-row blocks of one
+// expert (both 5-15 % slower than 64-deep steps over 128-token blocks).
 //
 // A direct load writes its 64 lanes' 16 bytes contiguously, so instead of
 // padding, the 16-byte segments of each 128-byte LDS row are permuted:
 // segment s of row r sits in slot s ^ (r & 7), which makes the fragment reads
 // free of bank conflicts (measured with the LDS bank-conflict counter; 16-byte
 // row padding costs 2 conflict cycles per read on gfx950, no permutation 6).
+// 16-token tiles that hold only padding rows skip their matrix ops.
 //
 // Work order: a 1-D grid of (weight tile, token block) items, token block
 // fastest, dealt to the 8 XCDs in contiguous runs (workgroup b runs on XCD
@@ -357,6 +358,9 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
       lds_direct16(bsrc[j] + kb, &sm.b[st][(wave * BInst + j) * 1024]);
   };
 
+  // this wavefront's 16-token tiles that hold at least one token
+  const int tn_live = min(TN, max(0, (nvalid - wn * (BN / 2) + 15) / 16));
+
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm)
@@ -367,8 +371,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   for (int s0 = 0; s0 < ST - 1; ++s0)
     if (s0 < nk) issue(s0);
   for (int ks = 0; ks < nk; ++ks) {
-    // stage ks must be in LDS: the stages issued after it may stay in flight
-    if (ST == 3 && ks + 1 < nk) wait_vmcnt<(ST == 3 ? kLoads : 0)>();
+    // stage ks must be in LDS: the ST-2 stages issued after it may stay in flight
+    if (ks + ST - 2 < nk) wait_vmcnt<(ST - 2) * kLoads>();
     else wait_vmcnt<0>();
     barrier_no_fence();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
     if (ks + ST - 1 < nk) issue(ks + ST - 1);
@@ -386,9 +390,12 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
         fb[tn] = *reinterpret_cast<const u32x4*>(
             Bt + lds_off(wn * (BN / 2) + tn * 16 + m, s2 * 4 + g));
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int tn = 0; tn < TN; ++tn) {
+        if (tn < tn_live) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(fa[tm], fb[tn], acc[tm][tn]);
+          for (int tm = 0; tm < TM; ++tm) acc[tm][tn] = mfma16x16x32(fa[tm], fb[tn], acc[tm][tn]);
+        }
+      }
     }
   }
 
