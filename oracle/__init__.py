@@ -44,6 +44,8 @@ def lib():
         L.orc_route.restype = i32
         L.orc_align.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
         L.orc_align.restype = i32
+        L.orc_align_mode.argtypes = [vp, i64, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp]
+        L.orc_align_mode.restype = i32
         L.orc_swiglu.argtypes = [vp, i32, i64, i32, i32, vp, vp, i32, dp]
         L.orc_swiglu.restype = None
         L.orc_combine.argtypes = [dp, dp, dp, i64, i32, i32, dp]
@@ -102,16 +104,20 @@ def route(logits, K):
     return ids, w
 
 
-def align(ids, E, B, cap):
-    """Block-padded alignment of the T*K pairs; returns a dict of int32 arrays."""
+PAD_MODES = {"block": 0, "max": 1}
+
+
+def align(ids, E, B, cap, mode="block"):
+    """Padded alignment of the T*K pairs (block-wise or max padding, Section 5.1
+    of the Serving-tax notes); returns a dict of int32 arrays."""
     ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
     T, K = ids.shape
     out = dict(expert_counts=np.empty(E, np.int32), expert_offsets=np.empty(E + 1, np.int32),
                sorted_ids=np.empty(cap, np.int32), block_expert=np.empty(cap // B, np.int32),
                inv_pos=np.empty(T * K, np.int32))
-    rc = lib().orc_align(_p(ids), T, K, E, B, cap, _p(out["expert_counts"]),
-                         _p(out["expert_offsets"]), _p(out["sorted_ids"]),
-                         _p(out["block_expert"]), _p(out["inv_pos"]))
+    rc = lib().orc_align_mode(_p(ids), T, K, E, B, cap, PAD_MODES[mode], _p(out["expert_counts"]),
+                              _p(out["expert_offsets"]), _p(out["sorted_ids"]),
+                              _p(out["block_expert"]), _p(out["inv_pos"]))
     if rc == -2:
         raise ValueError("orc_align: padded total exceeds capacity")
     if rc:

@@ -159,9 +159,12 @@ int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double
 }
 
 /*
- * Alignment of the T*K (token, slot) pairs p = t*K + k into expert buckets
- * with block-wise padding to a multiple of B:
- *   N_e = #{p : ids[p] = e},  P_e = ceil(N_e / B) * B,
+ * Alignment of the T*K (token, slot) pairs p = t*K + k into expert buckets,
+ * padded as in the padding model of the Serving-tax notes (Section 5.1):
+ *   N_e = #{p : ids[p] = e};
+ *   block-wise (mode 0): P_e = ceil(N_e / B) * B;
+ *   max (mode 1):        P_e = ceil(max_i N_i / B) * B for every expert, so
+ *                        the total is E * ceil(max_i N_i / B) * B;
  *   offsets[0] = 0, offsets[e+1] = offsets[e] + P_e, num_padded = offsets[E];
  *   bucket e holds its pairs in ascending p at rows offsets[e] ..
  *   offsets[e] + N_e - 1; every other row below cap holds the sentinel T*K;
@@ -170,10 +173,11 @@ int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double
  * cap must be a multiple of B.  Returns 0, -1 on bad arguments, -2 if the
  * padded total exceeds cap.
  */
-int orc_align(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, int32_t *counts,
-              int32_t *offsets, int32_t *sorted_ids, int32_t *block_expert, int32_t *inv_pos)
+int orc_align_mode(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, int mode,
+                   int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
+                   int32_t *block_expert, int32_t *inv_pos)
 {
-    if (T < 0 || K < 1 || E < 1 || B < 1 || cap < 0 || cap % B != 0)
+    if (T < 0 || K < 1 || E < 1 || B < 1 || cap < 0 || cap % B != 0 || mode < 0 || mode > 1)
         return -1;
     const int64_t TK = T * K;
     for (int e = 0; e < E; ++e)
@@ -183,13 +187,17 @@ int orc_align(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, i
             return -1;
         counts[ids[p]] += 1;
     }
+    int32_t maxn = 0;
+    for (int e = 0; e < E; ++e)
+        if (counts[e] > maxn)
+            maxn = counts[e];
     offsets[0] = 0;
     for (int e = 0; e < E; ++e) {
-        int64_t padded = (int64_t)(counts[e] + B - 1) / B * B;
+        int64_t padded = (int64_t)((mode == 1 ? maxn : counts[e]) + B - 1) / B * B;
+        if (offsets[e] + padded > cap)
+            return -2;
         offsets[e + 1] = (int32_t)(offsets[e] + padded);
     }
-    if (offsets[E] > cap)
-        return -2;
     for (int64_t r = 0; r < cap; ++r)
         sorted_ids[r] = (int32_t)TK;
     int32_t *fill = calloc((size_t)E, sizeof(int32_t));
@@ -207,6 +215,13 @@ int orc_align(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, i
         for (int64_t b = offsets[e] / B; b < offsets[e + 1] / B; ++b)
             block_expert[b] = e;
     return 0;
+}
+
+int orc_align(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, int32_t *counts,
+              int32_t *offsets, int32_t *sorted_ids, int32_t *block_expert, int32_t *inv_pos)
+{
+    return orc_align_mode(ids, T, K, E, B, cap, 0, counts, offsets, sorted_ids, block_expert,
+                          inv_pos);
 }
 
 /*

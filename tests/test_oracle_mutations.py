@@ -17,7 +17,9 @@ MUTANTS = {
     "ties_to_high_id": ("(best < 0 || l[e] > l[best])", "(best < 0 || l[e] >= l[best])"),
     "no_renormalise": ("w[t * K + j] = p[ids[t * K + j]] / s;", "w[t * K + j] = p[ids[t * K + j]];"),
     "shared_dropped": ("out[t * H + h] = acc + (s ? s[t * H + h] : 0.0);", "out[t * H + h] = acc;"),
-    "padding_off_by_one": ("(int64_t)(counts[e] + B - 1) / B * B", "(int64_t)(counts[e] + B) / B * B"),
+    "padding_off_by_one": ("((mode == 1 ? maxn : counts[e]) + B - 1) / B * B",
+                           "((mode == 1 ? maxn : counts[e]) + B) / B * B"),
+    "max_padding_uses_own_count": ("(mode == 1 ? maxn : counts[e])", "(counts[e])"),
     "bucket_descending": ("int64_t r = offsets[e] + fill[e];",
                           "int64_t r = offsets[e] + (counts[e] - 1 - fill[e]);"),
     "wrong_expert_weights": ("(size_t)ids[k] * 2 * I * H * esize", "(size_t)ids[(k + 1) % K] * 2 * I * H * esize"),

@@ -197,6 +197,60 @@ def test_align_degenerate_cases(orc):
         orc.align(np.arange(8, dtype=np.int32).reshape(4, 2), E=8, B=16, cap=64)
 
 
+def test_align_max_padding_hand_worked_example(orc):
+    # the same pairs as above with max padding: N = [2, 3, 0, 1], max N = 3, so every
+    # expert gets ceil(3/4)*4 = 4 rows, the empty expert e2 included
+    ids = np.array([[1, 0], [1, 3], [0, 1]], np.int32)
+    S = 6
+    a = orc.align(ids, E=4, B=4, cap=20, mode="max")
+    assert a["expert_counts"].tolist() == [2, 3, 0, 1]
+    assert a["expert_offsets"].tolist() == [0, 4, 8, 12, 16]
+    assert a["sorted_ids"].tolist() == [1, 4, S, S, 0, 2, 5, S, S, S, S, S, 3, S, S, S, S, S, S, S]
+    assert a["block_expert"].tolist() == [0, 1, 2, 3, -1]
+    assert a["inv_pos"].tolist() == [4, 0, 5, 12, 1, 6]
+
+
+@pytest.mark.parametrize("T,K,E,B", [(64, 2, 8, 16), (37, 8, 64, 16), (5, 8, 256, 128),
+                                     (100, 2, 8, 128), (1, 1, 4, 32), (33, 8, 64, 64)])
+@pytest.mark.parametrize("routing", ["uniform", "zipf"])
+def test_align_max_padding_invariants(orc, T, K, E, B, routing):
+    """Max padding (Section 5.1): P = E * ceil(max N_i / B) * B, every expert the
+    same slot, bucket contents those of block-wise padding, and never fewer rows."""
+    from mixture_experts_layer_30_amd import synth
+    ids, _ = orc.route(synth.router_logits(T, E, routing, seed=T + E), K)
+    TK = T * K
+    N = np.bincount(ids.reshape(-1), minlength=E)
+    slot = -(-int(N.max()) // B) * B
+    cap = E * -(-T // B) * B
+    a = orc.align(ids, E, B, cap, mode="max")
+    off = a["expert_offsets"].astype(np.int64)
+    assert off.tolist() == [e * slot for e in range(E + 1)]
+    assert off[-1] == E * (-(-int(N.max()) // B)) * B
+    blk_cap = -(-(TK + min(E, TK) * (B - 1)) // B) * B
+    b = orc.align(ids, E, B, blk_cap)
+    assert off[-1] >= b["expert_offsets"][-1]
+    srt, bs, bo = a["sorted_ids"], b["sorted_ids"], b["expert_offsets"]
+    for e in range(E):
+        assert srt[off[e]:off[e] + N[e]].tolist() == bs[bo[e]:bo[e] + N[e]].tolist()
+        assert (srt[off[e] + N[e]:off[e + 1]] == TK).all()
+    assert (srt[off[-1]:] == TK).all()
+    assert (srt[a["inv_pos"]] == np.arange(TK)).all()
+    be = a["block_expert"]
+    nb = int(off[-1]) // B
+    assert be[:nb].tolist() == [r * B // slot for r in range(nb)] if slot else True
+    assert (be[nb:] == -1).all()
+
+
+def test_align_max_padding_equals_block_when_loads_are_even():
+    """Every expert with the same count: the two paddings coincide."""
+    import oracle as orc
+    ids = np.array([[e, (e + 1) % 4] for e in range(4)] * 3, np.int32)   # N = 6 each
+    a = orc.align(ids, 4, 4, 48, mode="max")
+    b = orc.align(ids, 4, 4, 48)
+    for k in a:
+        assert (a[k] == b[k]).all(), k
+
+
 # --------------------------------------------------------------------------- expert FFN
 
 
