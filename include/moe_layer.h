@@ -104,6 +104,19 @@ const char *moe_status_string(moe_status s);
  */
 int64_t moe_align_capacity(int64_t T, int K, int E, int block_m);
 
+/* Padding schemes of the alignment (Serving-tax notes, "Padding model (Section 5.1)"). */
+typedef enum {
+    MOE_PAD_BLOCK = 0,   /* each expert on its own: P = sum_i ceil(N_i/B)*B */
+    MOE_PAD_MAX = 1      /* every expert the busiest one's slot: P = E*ceil(max_i N_i/B)*B */
+} moe_padding;
+
+/*
+ * Rows an alignment with padding `pad` may need: moe_align_capacity for
+ * MOE_PAD_BLOCK; E * ceil(T/B)*B for MOE_PAD_MAX (no expert holds more than T
+ * pairs, its tokens' K experts being distinct).  Returns -1 on bad arguments.
+ */
+int64_t moe_align_capacity_ex(int64_t T, int K, int E, int block_m, moe_padding pad);
+
 /* Workspace bytes moe_grouped_ffn needs: the SwiGLU activations, [cap][I] bf16. */
 int64_t moe_ffn_workspace_bytes(int64_t cap, int I);
 
@@ -138,6 +151,19 @@ moe_status moe_route(const float *logits, int64_t T, int E, int K, int32_t *topk
  */
 moe_status moe_align(const int32_t *topk_ids, int64_t T, int K, int E, const moe_plan *plan,
                      void *stream);
+
+/*
+ * moe_align with a choice of padding scheme (Section 5.1 of the Serving-tax
+ * notes): MOE_PAD_BLOCK is moe_align; MOE_PAD_MAX gives every expert, empty
+ * ones included, ceil(max_i N_i/B)*B rows (offsets[e] = e times that), the
+ * layout of a grouped GEMM with one fixed-size slot per expert.  Buckets hold
+ * the same pairs in the same order as with block-wise padding.  plan->cap must
+ * be at least moe_align_capacity_ex(T, K, E, block_m, pad).  Every grouped-FFN
+ * schedule reads either layout.
+ * Errors: as moe_align; MOE_EINVAL for an unknown scheme.
+ */
+moe_status moe_align_ex(const int32_t *topk_ids, int64_t T, int K, int E, const moe_plan *plan,
+                        moe_padding pad, void *stream);
 
 /*
  * Grouped expert FFN (Serving-tax notes, Table 1 row "GroupGEMM": the batch

@@ -15,11 +15,13 @@ LIB_PATH = os.path.join(_HERE, "libmoe_layer.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 SCHED_AUTO, SCHED_STREAM, SCHED_TILE, SCHED_RING = 0, 1, 2, 3
+PAD_BLOCK, PAD_MAX = 0, 1
 
 # every function the C header declares
-EXPORTS = ["moe_last_error", "moe_status_string", "moe_align_capacity", "moe_ffn_workspace_bytes",
-           "dense_ffn_workspace_bytes", "moe_route", "moe_align", "moe_grouped_ffn",
-           "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "dense_ffn_fa"]
+EXPORTS = ["moe_last_error", "moe_status_string", "moe_align_capacity", "moe_align_capacity_ex",
+           "moe_ffn_workspace_bytes", "dense_ffn_workspace_bytes", "moe_route", "moe_align",
+           "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
+           "moe_combine", "dense_ffn_fa"]
 
 
 class MoEError(RuntimeError):
@@ -51,6 +53,8 @@ def lib():
         L.moe_status_string.argtypes = [i32]
         L.moe_align_capacity.restype = i64
         L.moe_align_capacity.argtypes = [i64, i32, i32, i32]
+        L.moe_align_capacity_ex.restype = i64
+        L.moe_align_capacity_ex.argtypes = [i64, i32, i32, i32, i32]
         L.moe_ffn_workspace_bytes.restype = i64
         L.moe_ffn_workspace_bytes.argtypes = [i64, i32]
         L.dense_ffn_workspace_bytes.restype = i64
@@ -59,6 +63,8 @@ def lib():
         L.moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         L.moe_align.restype = i32
         L.moe_align.argtypes = [vp, i64, i32, i32, P, vp]
+        L.moe_align_ex.restype = i32
+        L.moe_align_ex.argtypes = [vp, i64, i32, i32, P, i32, vp]
         L.moe_grouped_ffn.restype = i32
         L.moe_grouped_ffn.argtypes = [vp, i32, i64, i32, i32, i32, i32, vp, vp, P, vp, i64, vp, vp]
         L.moe_grouped_gate_up.restype = i32
@@ -100,6 +106,10 @@ def moe_align_capacity(T, K, E, block_m):
     return lib().moe_align_capacity(T, K, E, block_m)
 
 
+def moe_align_capacity_ex(T, K, E, block_m, pad):
+    return lib().moe_align_capacity_ex(T, K, E, block_m, pad)
+
+
 def moe_ffn_workspace_bytes(cap, I):
     return lib().moe_ffn_workspace_bytes(cap, I)
 
@@ -111,9 +121,9 @@ def dense_ffn_workspace_bytes(T, H, I):
 class Plan:
     """Device arrays of one alignment (see moe_plan in include/moe_layer.h)."""
 
-    def __init__(self, T, K, E, block_m, device, cap=None):
-        self.T, self.K, self.E, self.block_m = T, K, E, block_m
-        self.cap = moe_align_capacity(T, K, E, block_m) if cap is None else cap
+    def __init__(self, T, K, E, block_m, device, cap=None, pad=PAD_BLOCK):
+        self.T, self.K, self.E, self.block_m, self.pad = T, K, E, block_m, pad
+        self.cap = moe_align_capacity_ex(T, K, E, block_m, pad) if cap is None else cap
         i32 = torch.int32
         self.expert_counts = torch.empty(E, dtype=i32, device=device)
         self.expert_offsets = torch.empty(E + 1, dtype=i32, device=device)
@@ -138,6 +148,11 @@ def moe_route(logits, K, topk_ids, topk_w, stream=None):
 def moe_align(topk_ids, E, plan, stream=None):
     T, K = topk_ids.shape
     _check(lib().moe_align(_ptr(topk_ids), T, K, E, ctypes.byref(plan.c), _stream(stream)))
+
+
+def moe_align_ex(topk_ids, E, plan, pad, stream=None):
+    T, K = topk_ids.shape
+    _check(lib().moe_align_ex(_ptr(topk_ids), T, K, E, ctypes.byref(plan.c), pad, _stream(stream)))
 
 
 def moe_grouped_ffn(x, w13, w2, K, plan, workspace, y_pairs, stream=None):

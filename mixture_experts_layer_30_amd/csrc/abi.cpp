@@ -48,7 +48,8 @@ moe_status check_route_shape(int64_t T, int E, int K) {
   return MOE_OK;
 }
 
-moe_status check_plan(const moe_plan* plan, int64_t T, int K, int E) {
+moe_status check_plan(const moe_plan* plan, int64_t T, int K, int E,
+                      moe_padding pad = MOE_PAD_BLOCK) {
   if (!plan) return fail(MOE_EINVAL, "plan is NULL");
   if (plan->block_m < 1 || plan->block_m > 1024)
     return fail(MOE_EUNSUPPORTED, "block_m = %d outside 1..1024", plan->block_m);
@@ -62,7 +63,7 @@ moe_status check_plan(const moe_plan* plan, int64_t T, int K, int E) {
   if (plan->cap % plan->block_m != 0)
     return fail(MOE_EINVAL, "plan->cap = %lld is not a multiple of block_m = %d",
                 (long long)plan->cap, plan->block_m);
-  const int64_t need = moe_align_capacity(T, K, E, plan->block_m);
+  const int64_t need = moe_align_capacity_ex(T, K, E, plan->block_m, pad);
   if (plan->cap < need)
     return fail(MOE_ECAPACITY, "plan->cap = %lld < %lld required", (long long)plan->cap,
                 (long long)need);
@@ -216,6 +217,12 @@ int64_t moe_align_capacity(int64_t T, int K, int E, int block_m) {
   return round_up(TK + active * (block_m - 1), block_m);
 }
 
+int64_t moe_align_capacity_ex(int64_t T, int K, int E, int block_m, moe_padding pad) {
+  if (pad == MOE_PAD_BLOCK) return moe_align_capacity(T, K, E, block_m);
+  if (pad != MOE_PAD_MAX || T < 0 || K < 1 || E < 1 || block_m < 1) return -1;
+  return (int64_t)E * round_up(T, block_m);
+}
+
 int64_t moe_ffn_workspace_bytes(int64_t cap, int I) {
   if (cap < 0 || I < 0) return -1;
   return cap * (int64_t)I * 2;
@@ -241,19 +248,26 @@ moe_status moe_route(const float* logits, int64_t T, int E, int K, int32_t* topk
                     "moe_route");
 }
 
-moe_status moe_align(const int32_t* topk_ids, int64_t T, int K, int E, const moe_plan* plan,
-                     void* stream) {
+moe_status moe_align_ex(const int32_t* topk_ids, int64_t T, int K, int E, const moe_plan* plan,
+                        moe_padding pad, void* stream) {
   moe_status st = check_route_shape(T, E, K);
   if (st) return st;
+  if (pad != MOE_PAD_BLOCK && pad != MOE_PAD_MAX)
+    return fail(MOE_EINVAL, "moe_align_ex: padding scheme %d", (int)pad);
   if (T > 0 && (!topk_ids || !aligned(topk_ids, 4)))
     return fail(MOE_EINVAL, "moe_align: topk_ids NULL or misaligned");
-  st = check_plan(plan, T, K, E);
+  st = check_plan(plan, T, K, E, pad);
   if (st) return st;
   return hip_status(moe::launch_align(topk_ids, T, K, E, plan->block_m, plan->cap,
-                                      plan->expert_counts, plan->expert_offsets,
-                                      plan->sorted_ids, plan->block_expert, plan->inv_pos,
-                                      (hipStream_t)stream),
+                                      pad == MOE_PAD_MAX ? 1 : 0, plan->expert_counts,
+                                      plan->expert_offsets, plan->sorted_ids, plan->block_expert,
+                                      plan->inv_pos, (hipStream_t)stream),
                     "moe_align");
+}
+
+moe_status moe_align(const int32_t* topk_ids, int64_t T, int K, int E, const moe_plan* plan,
+                     void* stream) {
+  return moe_align_ex(topk_ids, T, K, E, plan, MOE_PAD_BLOCK, stream);
 }
 
 static moe_status check_grouped(const void* x, moe_dtype dt, int64_t T, int H, int I, int E, int K,

@@ -1,8 +1,9 @@
-// Token-to-expert alignment with block-wise padding on gfx950.
+// Token-to-expert alignment with block-wise or max padding on gfx950.
 //
-// Serving-tax notes, "Padding model (Section 5.1)": each expert's token count
-// N_i is rounded up on its own to a multiple of the block B, so the grouped
-// GEMM computes P = sum_i ceil(N_i/B)*B rows.  The kernel produces the
+// Serving-tax notes, "Padding model (Section 5.1)": block-wise padding rounds
+// each expert's token count N_i up on its own to a multiple of the block B, so
+// the grouped GEMM computes P = sum_i ceil(N_i/B)*B rows; max padding gives
+// every expert the slot of the busiest one, P = E * ceil(max_i N_i/B)*B.  The kernel produces the
 // grouping that the grouped GEMM reads: per-expert counts and padded offsets,
 // the pair index of every row (buckets in ascending pair order, sentinel T*K
 // in padding rows), the expert of every B-row block and the inverse map.
@@ -11,7 +12,8 @@
 // thousands of pairs, so the pass is a few microseconds:
 //  1. histogram of the expert ids in LDS (atomics only on counts, so the
 //     result does not depend on their order);
-//  2. one wavefront scans the padded counts (E <= 256, four per lane);
+//  2. one wavefront scans the padded counts (E <= 256, four per lane; for max
+//     padding after a max-reduction of the counts);
 //  3. padding rows get the sentinel and every block its expert, each row
 //     finding its bucket by binary search over the LDS offsets;
 //  4. a stable scatter in rounds of 1024 consecutive pairs: inside a
@@ -30,7 +32,7 @@ constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kMaxExperts = 256;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int64_t TK, int E, int B, int64_t cap,
+    const int32_t* __restrict__ ids, int64_t TK, int E, int B, int64_t cap, int max_pad,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ inv_pos) {
   __shared__ int s_cnt[kMaxExperts];
@@ -58,6 +60,18 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 
   // 2. exclusive prefix sum of the padded counts, one wavefront
   if (wave == 0) {
+    int slot = 0;   // max padding: every expert's padded size
+    if (max_pad) {
+      int mx = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane * 4 + j;
+        mx = max(mx, e < E ? s_cnt[e] : 0);
+      }
+#pragma unroll
+      for (int d = kWave / 2; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d));
+      slot = (mx + B - 1) / B * B;
+    }
     int loc[4];
     int run = 0;
 #pragma unroll
@@ -65,7 +79,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       const int e = lane * 4 + j;
       const int n = e < E ? s_cnt[e] : 0;
       loc[j] = run;
-      run += (n + B - 1) / B * B;
+      run += e < E ? (max_pad ? slot : (n + B - 1) / B * B) : 0;
     }
     int incl = run;
 #pragma unroll
@@ -148,10 +162,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 }
 
 hipError_t launch_align(const int32_t* ids, int64_t T, int K, int E, int B, int64_t cap,
-                        int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                        int max_pad, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* inv_pos, hipStream_t s) {
   hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, T * K, E, B, cap,
-                     counts, offsets, sorted_ids, block_expert, inv_pos);
+                     max_pad, counts, offsets, sorted_ids, block_expert, inv_pos);
   return hipGetLastError();
 }
 

@@ -12,8 +12,9 @@ constexpr int kDtBF16 = 1;
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
                         hipStream_t s);
 
+// max_pad: 0 block-wise padding, 1 max padding (every expert ceil(max N / B) * B rows)
 hipError_t launch_align(const int32_t* ids, int64_t T, int K, int E, int B, int64_t cap,
-                        int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                        int max_pad, int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* inv_pos, hipStream_t s);
 
 hipError_t launch_combine(const void* y, int ydt, const float* w, const void* shared, int sdt,

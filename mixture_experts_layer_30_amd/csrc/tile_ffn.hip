@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
     const int jj = j < nvalid ? j : 0;  // rows past the bucket reuse its first row
     const int row = row0 + jj;
     if (kGateUp) {
-      sm.tok[j] = dense ? row : rm.sorted_ids[row] / rm.K;
+      // (a block of padding rows only, as max padding makes, reads token 0)
+      sm.tok[j] = dense ? row : (nvalid > 0 ? rm.sorted_ids[row] / rm.K : 0);
     } else {
       sm.tok[j] = row;
       sm.dst[j] = dense ? row : rm.sorted_ids[row];
@@ -306,10 +307,11 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   const int m = lane & 15, g = lane >> 4;
 
   for (int j = tid; j < BN; j += NT) {
-    const int jj = j < nvalid ? j : 0;
+    const int jj = j < nvalid ? j : 0;  // rows past the bucket reuse its first row
     const int row = row0 + jj;
     if (kGateUp) {
-      sm.tok[j] = dense ? row : rm.sorted_ids[row] / rm.K;
+      // (a block of padding rows only, as max padding makes, reads token 0)
+      sm.tok[j] = dense ? row : (nvalid > 0 ? rm.sorted_ids[row] / rm.K : 0);
     } else {
       sm.tok[j] = row;
       sm.dst[j] = dense ? row : rm.sorted_ids[row];

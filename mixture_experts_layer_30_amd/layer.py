@@ -25,7 +25,8 @@ def default_block_m(T, K, E):
 
 
 class MoELayer:
-    def __init__(self, shape, inputs, block_m=None, sched=B.SCHED_AUTO, out_dtype=None):
+    def __init__(self, shape, inputs, block_m=None, sched=B.SCHED_AUTO, out_dtype=None,
+                 pad=B.PAD_BLOCK):
         x = inputs["x"]
         self.shape, self.inputs, self.sched = shape, inputs, sched
         self.T = T = x.shape[0]
@@ -34,7 +35,8 @@ class MoELayer:
         self.block_m = block_m or default_block_m(T, K, E)
         self.topk_ids = torch.empty(T, K, dtype=torch.int32, device=dev)
         self.topk_w = torch.empty(T, K, dtype=torch.float32, device=dev)
-        self.plan = B.Plan(T, K, E, self.block_m, dev)
+        self.pad = pad
+        self.plan = B.Plan(T, K, E, self.block_m, dev, pad=pad)
         ws = B.moe_ffn_workspace_bytes(self.plan.cap, I)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.y_pairs = torch.empty(max(T * K, 1), H, dtype=x.dtype, device=dev)
@@ -58,7 +60,10 @@ class MoELayer:
         B.moe_route(self.inputs["logits"], self.shape.topk, self.topk_ids, self.topk_w)
 
     def align(self):
-        B.moe_align(self.topk_ids, self.shape.experts, self.plan)
+        if self.pad == B.PAD_BLOCK:
+            B.moe_align(self.topk_ids, self.shape.experts, self.plan)
+        else:
+            B.moe_align_ex(self.topk_ids, self.shape.experts, self.plan, self.pad)
 
     def gate_up(self):
         B.moe_grouped_gate_up(self.inputs["x"], self.inputs["w13"], self.shape.topk, self.plan,

@@ -50,6 +50,10 @@ def test_align_capacity_bound(L):
     assert B.moe_align_capacity(0, 2, 8, 16) == 0
     assert B.moe_align_capacity(-1, 2, 8, 16) == -1
     assert B.moe_ffn_workspace_bytes(4864, 2048) == 4864 * 2048 * 2
+    # max padding: E slots of ceil(T/B)*B rows (no expert holds more than T pairs)
+    assert B.moe_align_capacity_ex(128, 8, 256, 16, B.PAD_BLOCK) == B.moe_align_capacity(128, 8, 256, 16)
+    assert B.moe_align_capacity_ex(100, 2, 8, 64, B.PAD_MAX) == 8 * 128
+    assert B.moe_align_capacity_ex(100, 2, 8, 64, 7) == -1
     # activations (128-row rounded) plus split-K partial sums
     assert B.dense_ffn_workspace_bytes(1, 128, 512) >= 128 * 512 * 2
     assert B.dense_ffn_workspace_bytes(1, 100, 512) == -1
@@ -88,6 +92,11 @@ def test_align_argument_checks(L):
     assert st(L.moe_align(FAKE, 128, 8, 256, None, None)) == B.MOE_EINVAL
     bad_b = plan(block_m=0)
     assert st(L.moe_align(FAKE, 128, 8, 256, ctypes.byref(bad_b), None)) == B.MOE_EUNSUPPORTED
+    # max padding needs E * ceil(T/B)*B rows; an unknown scheme is refused
+    assert st(L.moe_align_ex(FAKE, 128, 8, 256, ctypes.byref(plan(cap=4864)), B.PAD_MAX,
+                             None)) == B.MOE_ECAPACITY
+    assert st(L.moe_align_ex(FAKE, 128, 8, 256, ctypes.byref(plan(cap=4864)), 5,
+                             None)) == B.MOE_EINVAL
 
 
 def test_grouped_ffn_argument_checks(L):

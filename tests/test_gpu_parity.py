@@ -101,20 +101,23 @@ def test_route_empty_batch_is_a_noop():
     assert (ids.cpu() == -7).all()
 
 
-def run_align(ids_np, E, block_m):
+def run_align(ids_np, E, block_m, pad=B.PAD_BLOCK):
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(DEV)
     T, K = ids_np.shape
-    plan = B.Plan(T, K, E, block_m, DEV)
+    plan = B.Plan(T, K, E, block_m, DEV, pad=pad)
     for t in plan.arrays().values():
         t.fill_(-12345)
-    B.moe_align(ids, E, plan)
+    if pad == B.PAD_BLOCK:
+        B.moe_align(ids, E, plan)
+    else:
+        B.moe_align_ex(ids, E, plan, pad)
     torch.cuda.synchronize()
     return plan.cap, {k: v.cpu().numpy() for k, v in plan.arrays().items()}
 
 
-def assert_align_equal(ids_np, E, block_m):
-    cap, got = run_align(ids_np, E, block_m)
-    ref = oracle.align(ids_np, E, block_m, cap)
+def assert_align_equal(ids_np, E, block_m, pad=B.PAD_BLOCK):
+    cap, got = run_align(ids_np, E, block_m, pad)
+    ref = oracle.align(ids_np, E, block_m, cap, mode="max" if pad == B.PAD_MAX else "block")
     for k in ref:
         assert got[k].shape == ref[k].shape, k
         assert (got[k] == ref[k]).all(), k
@@ -142,6 +145,21 @@ def test_align_adversarial(block_m):
     # many rounds of the scatter: 32768 pairs
     ids, _ = oracle.route(synth.router_logits(4096, 64, "zipf", seed=1), 8)
     assert_align_equal(ids, 64, block_m)
+
+
+@pytest.mark.parametrize("T,E,K,routing", ROUTE_CASES)
+@pytest.mark.parametrize("block_m", [16, 128])
+def test_align_max_padding_parity(T, E, K, routing, block_m):
+    """Max padding (every expert the busiest one's slot), bit-exact."""
+    logits = synth.router_logits(T, E, routing, seed=T + E)
+    ids, _ = oracle.route(logits, K)
+    assert_align_equal(ids, E, block_m, pad=B.PAD_MAX)
+
+
+def test_align_max_padding_adversarial():
+    assert_align_equal(np.zeros((300, 1), np.int32), 8, 64, pad=B.PAD_MAX)        # one hot expert
+    assert_align_equal(np.full((5, 1), 255, np.int32), 256, 16, pad=B.PAD_MAX)    # 255 empty slots
+    assert_align_equal(np.tile(np.arange(16, dtype=np.int32), (37, 1)), 16, 32, pad=B.PAD_MAX)
 
 
 def test_align_empty_batch():
@@ -402,6 +420,32 @@ def test_dense_pa_parity(T):
     torch.cuda.synchronize()
     assert dev["wpa13"].shape[0] == 2 * shape.dense_pa_inter
     assert rel_err(out, oracle.dense_ffn(d["x"], d["wpa13"], d["wpa2"])) <= TOL
+
+
+MAXPAD_SHAPES = [
+    # (shape, T, routing, block_m, sched): skewed loads leave whole padding blocks and empty
+    # experts' slots, which the tiled schedule reads and the streaming schedules skip
+    (LayerShape("maxpad_tile", 256, 256, 16, 2, 128, "bf16", (300,), ("zipf",)), 300, "zipf", 64, B.SCHED_TILE),
+    (LayerShape("maxpad_tile128", 512, 384, 8, 2, 0, "bf16", (500,), ("zipf",)), 500, "zipf", 128, B.SCHED_TILE),
+    (LayerShape("maxpad_ring", 256, 256, 16, 2, 0, "bf16", (40,), ("zipf",)), 40, "zipf", 16, B.SCHED_RING),
+    (LayerShape("maxpad_stream", 256, 192, 16, 4, 0, "bf16", (60,), ("uniform",)), 60, "uniform", 16, B.SCHED_STREAM),
+]
+
+
+@pytest.mark.parametrize("shape,T,routing,block_m,sched", MAXPAD_SHAPES,
+                         ids=[s[0].name for s in MAXPAD_SHAPES])
+def test_layer_parity_max_padding(shape, T, routing, block_m, sched):
+    d, dev = layer_case(shape, T, routing, seed=13)
+    layer = MoELayer(shape, dev, block_m=block_m, sched=sched, pad=B.PAD_MAX)
+    out = layer.forward().clone()
+    torch.cuda.synchronize()
+    ref, rids, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], shape.topk,
+                                    d["ws13"], d["ws2"])
+    got = {k: v.cpu().numpy() for k, v in layer.plan.arrays().items()}
+    ra = oracle.align(rids, shape.experts, block_m, layer.plan.cap, mode="max")
+    for k in ra:
+        assert (got[k] == ra[k]).all(), k
+    assert rel_err(out, ref) <= TOL
 
 
 def test_tile_schedule_rejects_unsupported_block():
