@@ -341,6 +341,48 @@ def run_only(name, T, routing, what, steps):
                       "dense_fa_algorithmic_flops": alg["fa_flops"]}))
 
 
+def padding_sweep(steps):
+    """Padding model of the Serving-tax notes (Section 5.1): the padded rows P
+    and the padding factor eta = P / (T*K) of block-wise and max padding for
+    B in 16..256, and the tiled gate/up kernel's time against P (B = 64, 128)
+    with a least-squares line per B; one JSON line per point, then the fits."""
+    from mixture_experts_layer_30_amd import binding as B
+    shape = configs.CONFIGS["qwen2"]
+    E, K = shape.experts, shape.topk
+    points = []
+    for T in (256, 512, 1024, 2048):
+        for routing in ("uniform", "zipf"):
+            d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=False)
+            for bm in (16, 32, 64, 128, 256):
+                for pad, pname in ((B.PAD_BLOCK, "block"), (B.PAD_MAX, "max")):
+                    tiled = bm in (64, 128)
+                    layer = MoELayer(shape, d, block_m=bm, pad=pad,
+                                     sched=B.SCHED_TILE if tiled else B.SCHED_STREAM)
+                    layer.route()
+                    layer.align()
+                    torch.cuda.synchronize()
+                    P = int(layer.plan.expert_offsets[-1].item())
+                    rec = {"padding_sweep": f"qwen2 T={T} {routing}", "block_m": bm, "padding": pname,
+                           "P_rows": P, "eta": round(P / (T * K), 4)}
+                    if tiled:
+                        us, _, _ = time_steps(layer.gate_up, steps, 2)
+                        rec["gate_up_us"] = round(us * 1e3, 2)
+                        points.append((bm, P, us * 1e3))
+                    print(json.dumps(rec), flush=True)
+                    del layer
+            del d
+            torch.cuda.empty_cache()
+    for bm in (64, 128):
+        xs = np.array([p for b, p, _ in points if b == bm], dtype=np.float64)
+        ys = np.array([t for b, _, t in points if b == bm], dtype=np.float64)
+        slope, icpt = np.polyfit(xs, ys, 1)
+        pred = slope * xs + icpt
+        r2 = 1.0 - ((ys - pred) ** 2).sum() / ((ys - ys.mean()) ** 2).sum()
+        print(json.dumps({"padding_fit": f"tiled gate/up time vs padded rows, qwen2 shape, block_m={bm}",
+                          "points": len(xs), "us_per_row": round(slope, 6),
+                          "intercept_us": round(icpt, 2), "r2": round(float(r2), 5)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +395,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["gate_up", "down", "dense_fa", "layer", "copy"],
                     help="run one piece `--steps` times, untimed (for counter runs)")
+    ap.add_argument("--padding-sweep", action="store_true",
+                    help="padded rows, eta and tiled gate/up time vs padded rows (Section 5.1)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
@@ -361,6 +405,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.padding_sweep:
+        padding_sweep(args.steps)
+        return
     if args.only:
         shape = configs.CONFIGS[args.config or "mixtral"]
         run_only(args.config or "mixtral", args.T or shape.tokens[0],
