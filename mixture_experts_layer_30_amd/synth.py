@@ -72,6 +72,30 @@ def swiglu_weights(n_out_inter, H, dtype="bf16", seed=0, device="cpu", prefix="w
     return w13, w2
 
 
+FP8_MAX = 448.0   # largest finite FP8 E4M3 value
+
+
+def quantize_fp8_rows(w, chunk_rows=8192):
+    """FP8 E4M3 weight codes and fp32 row scales for a [..., rows, cols] matrix:
+    scale = max |w[row]| / 448 (1 for an all-zero row), code = w / scale rounded
+    to the nearest E4M3 value (torch's float8_e4m3fn conversion).  Returns
+    (uint8 codes of w's shape, float32 scales of shape [..., rows]).  An input
+    transform (weight quantization, the notes' decode-phase remedy); the layer
+    consumes codes and scales as given."""
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    sc = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    flat_w = w.reshape(-1, w.shape[-1])
+    flat_q = q.view(-1, w.shape[-1])
+    flat_s = sc.view(-1)
+    for r0 in range(0, flat_w.shape[0], chunk_rows):
+        blk = flat_w[r0:r0 + chunk_rows].float()
+        amax = blk.abs().amax(dim=1)
+        s_ = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+        flat_s[r0:r0 + chunk_rows] = s_
+        flat_q[r0:r0 + chunk_rows] = (blk / s_[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q, sc
+
+
 def layer_inputs(shape, T, routing=None, seed=0, device="cpu", dense=True, moe=True,
                  densepa=False):
     """All inputs of one MoE layer pass (and its DenseFA / DensePA baselines) for a LayerShape."""

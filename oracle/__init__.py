@@ -5,8 +5,9 @@ import this package.  The library's compute path never calls it; it shares no
 code with the HIP kernels (the C source is compiled with gcc on its own).
 
 Thin ctypes marshalling around ``moe_oracle.c``; every step of the arithmetic
-is in that file.  Inputs are torch CPU tensors or numpy arrays, fp32 or bf16;
-results are float64 numpy arrays (routing ids and alignment arrays int32).
+is in that file.  Inputs are torch CPU tensors or numpy arrays, fp32 or bf16
+(weights also FP8 E4M3 codes as uint8 with fp32 row scales); results are
+float64 numpy arrays (routing ids and alignment arrays int32).
 """
 import ctypes
 import os
@@ -18,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "moe_oracle.c")
 LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 _lib = None
 
 
@@ -48,11 +49,18 @@ def lib():
         L.orc_align_mode.restype = i32
         L.orc_swiglu.argtypes = [vp, i32, i64, i32, i32, vp, vp, i32, dp]
         L.orc_swiglu.restype = None
+        L.orc_swiglu_s.argtypes = [vp, i32, i64, i32, i32, vp, vp, i32, vp, vp, dp]
+        L.orc_swiglu_s.restype = None
+        L.orc_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        L.orc_fp8_e4m3.restype = ctypes.c_double
         L.orc_combine.argtypes = [dp, dp, dp, i64, i32, i32, dp]
         L.orc_combine.restype = None
         L.orc_moe_layer.argtypes = [vp, i32, vp, i64, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp,
                                     vp, dp, dp]
         L.orc_moe_layer.restype = i32
+        L.orc_moe_layer_s.argtypes = [vp, i32, vp, i64, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32,
+                                      vp, vp, vp, vp, vp, dp, dp]
+        L.orc_moe_layer_s.restype = i32
         L.orc_set_threads.argtypes = [i32]
         L.orc_max_threads.restype = i32
         _lib = L
@@ -69,6 +77,8 @@ def _arr(t):
             return a, F32
         if a.dtype == np.uint16:
             return a, BF16
+        if a.dtype == np.uint8:
+            return a, FP8
         raise TypeError(f"unsupported numpy dtype {a.dtype}")
     import torch
     t = t.detach().to("cpu").contiguous()
@@ -76,7 +86,19 @@ def _arr(t):
         return t.numpy(), F32
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16), BF16
+    if t.dtype == torch.uint8:
+        return t.numpy(), FP8
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _scales(t):
+    """fp32 row scales as a contiguous numpy array (or None)."""
+    if t is None:
+        return None
+    if not isinstance(t, np.ndarray):
+        t = t.detach().to("cpu").contiguous().numpy()
+    a = np.ascontiguousarray(t, dtype=np.float32)
+    return a
 
 
 def _p(a):
@@ -140,6 +162,56 @@ def swiglu(x, w13, w2):
 
 
 dense_ffn = swiglu
+
+
+def fp8_e4m3(code):
+    """Value of one FP8 E4M3 code (0..255)."""
+    return lib().orc_fp8_e4m3(int(code))
+
+
+def swiglu_fp8(x, q13, s13, q2, s2):
+    """SwiGLU with FP8 E4M3 weights (uint8 codes) times fp32 row scales:
+    W13 = q13 * s13[:, None] ([2I,H], [2I]), W2 = q2 * s2[:, None] ([H,I], [H])."""
+    xa, xdt = _arr(x)
+    a13, wdt = _arr(q13)
+    a2, wdt2 = _arr(q2)
+    assert wdt == FP8 and wdt2 == FP8
+    n, H = xa.shape
+    I = a13.shape[0] // 2
+    sc13, sc2 = _scales(s13), _scales(s2)
+    assert a13.shape == (2 * I, H) and a2.shape == (H, I) and sc13.shape == (2 * I,) and sc2.shape == (H,)
+    y = np.empty((n, H), np.float64)
+    lib().orc_swiglu_s(_p(xa), xdt, n, H, I, _p(a13), _p(a2), wdt, _p(sc13), _p(sc2), _p(y))
+    return y
+
+
+def moe_layer_fp8(x, logits, q13, s13, q2, s2, K, qs13=None, ss13=None, qs2=None, ss2=None):
+    """Whole layer with FP8 E4M3 weights and fp32 row scales (routed experts
+    q13 [E,2I,H] / s13 [E,2I], q2 [E,H,I] / s2 [E,H]; shared experts likewise);
+    returns (out float64 [T,H], ids int32 [T,K], w float64 [T,K])."""
+    xa, xdt = _arr(x)
+    la, _ = _arr(logits)
+    a13, wdt = _arr(q13)
+    a2, _ = _arr(q2)
+    assert wdt == FP8
+    T, H = xa.shape
+    E = a13.shape[0]
+    I = a13.shape[1] // 2
+    sc13, sc2 = _scales(s13), _scales(s2)
+    assert a13.shape == (E, 2 * I, H) and a2.shape == (E, H, I) and la.shape == (T, E)
+    assert sc13.shape == (E, 2 * I) and sc2.shape == (E, H)
+    b13, _ = _arr(qs13)
+    b2, _ = _arr(qs2)
+    Is = 0 if b13 is None else b13.shape[0] // 2
+    out = np.empty((T, H), np.float64)
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float64)
+    rc = lib().orc_moe_layer_s(_p(xa), xdt, _p(la), T, H, I, E, K, _p(a13), _p(a2), wdt, _p(sc13),
+                               _p(sc2), Is, _p(b13), _p(b2), _p(_scales(ss13)), _p(_scales(ss2)),
+                               _p(ids), _p(w), _p(out))
+    if rc:
+        raise ValueError("orc_moe_layer: bad arguments")
+    return out, ids, w
 
 
 def combine(y, w, s=None):

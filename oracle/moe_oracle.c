@@ -7,7 +7,11 @@
  *
  * Plain loops, one token and one expert at a time, float64 accumulation.
  * Inputs are fp32 or bf16 bit patterns; bf16 is decoded exactly (its 16 bits
- * are the top half of an fp32).  Where the pages leave a step open the reading
+ * are the top half of an fp32).  Weights may also be FP8 E4M3 codes (the OCP
+ * 8-bit float: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN) with one fp32 scale per matrix row, the
+ * weight being code value * row scale -- weight quantization, the decode-phase
+ * remedy of the notes ("量子化").  Where the pages leave a step open the reading
  * taken is stated at the function.
  *
  * What it computes, and where the pages define it:
@@ -33,32 +37,53 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
 
-/* Element i of an fp32 or bf16 array, as a double (exact in both cases). */
+static size_t elem_size(int dt) { return dt == ORC_F32 ? 4 : dt == ORC_BF16 ? 2 : 1; }
+
+/* Value of an FP8 E4M3 code, from the format's definition. */
+double orc_fp8_e4m3(uint8_t b)
+{
+    const int sgn = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);           /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sgn ? -v : v;
+}
+
+/* Element i of an fp32, bf16 or FP8 array, as a double (exact in every case). */
 static double elem(const void *p, int dt, int64_t i)
 {
     if (dt == ORC_F32)
         return (double)((const float *)p)[i];
+    if (dt == ORC_FP8)
+        return orc_fp8_e4m3(((const uint8_t *)p)[i]);
     uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
 }
 
-/* Row `row` (length n) of a row-major matrix, decoded to doubles. */
-static void decode_row(const void *m, int dt, int64_t row, int64_t n, double *dst)
+/* Row `row` (length n) of a row-major matrix, decoded to doubles; with a
+ * per-row scale (quantized weights) each element is code value * scale[row]. */
+static void decode_row(const void *m, int dt, int64_t row, int64_t n, double *dst,
+                       const float *scale)
 {
+    const double sc = scale ? (double)scale[row] : 1.0;
     for (int64_t c = 0; c < n; ++c)
-        dst[c] = elem(m, dt, row * n + c);
+        dst[c] = elem(m, dt, row * n + c) * sc;
 }
 
 /* out[j] = sum_c M[row0 + j][c] * v[c] over c ascending, for j < nrows. */
-static void matvec(const void *m, int dt, int64_t row0, int64_t nrows, int64_t ncols,
-                   const double *v, double *rowbuf, double *out)
+static void matvec(const void *m, int dt, const float *scale, int64_t row0, int64_t nrows,
+                   int64_t ncols, const double *v, double *rowbuf, double *out)
 {
     for (int64_t j = 0; j < nrows; ++j) {
-        decode_row(m, dt, row0 + j, ncols, rowbuf);
+        decode_row(m, dt, row0 + j, ncols, rowbuf, scale);
         double s = 0.0;
         for (int64_t c = 0; c < ncols; ++c)
             s += rowbuf[c] * v[c];
@@ -73,18 +98,19 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  *   g_i = sum_h W1[i][h] x[h],  u_i = sum_h W3[i][h] x[h]   (W1 = rows 0..I-1
  *   of w13, W3 = rows I..2I-1), a_i = silu(g_i) * u_i,
  *   y_h = sum_i W2[h][i] a_i   (w2 is [H][I], out x in, row-major).
- * w13/w2 point at this expert's matrices.  scratch holds 3*I + max(H,I) doubles.
+ * w13/w2 point at this expert's matrices; s13 [2I] / s2 [H] are their row
+ * scales (NULL for fp32/bf16 weights).  scratch holds 3*I + max(H,I) doubles.
  */
 static void swiglu_token(const double *xv, int H, int I, const void *w13, const void *w2, int wdt,
-                         double *scratch, double *y)
+                         const float *s13, const float *s2, double *scratch, double *y)
 {
     double *g = scratch, *u = scratch + I, *a = scratch + 2 * (int64_t)I;
     double *rowbuf = scratch + 3 * (int64_t)I;
-    matvec(w13, wdt, 0, I, H, xv, rowbuf, g);
-    matvec(w13, wdt, I, I, H, xv, rowbuf, u);
+    matvec(w13, wdt, s13, 0, I, H, xv, rowbuf, g);
+    matvec(w13, wdt, s13, I, I, H, xv, rowbuf, u);
     for (int i = 0; i < I; ++i)
         a[i] = silu(g[i]) * u[i];
-    matvec(w2, wdt, 0, H, I, a, rowbuf, y);
+    matvec(w2, wdt, s2, 0, H, I, a, rowbuf, y);
 }
 
 static size_t swiglu_scratch(int H, int I) { return 3 * (size_t)I + (size_t)(H > I ? H : I); }
@@ -229,8 +255,8 @@ int orc_align(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, i
  * (w13 [2I][H] gate rows then up rows, w2 [H][I]).  Serves a single expert,
  * the shared experts and DenseFA.  Parallel over rows.
  */
-void orc_swiglu(const void *x, int xdt, int64_t n, int H, int I, const void *w13, const void *w2,
-                int wdt, double *y)
+void orc_swiglu_s(const void *x, int xdt, int64_t n, int H, int I, const void *w13,
+                  const void *w2, int wdt, const float *s13, const float *s2, double *y)
 {
 #pragma omp parallel
     {
@@ -238,12 +264,18 @@ void orc_swiglu(const void *x, int xdt, int64_t n, int H, int I, const void *w13
         double *scratch = malloc(sizeof(double) * swiglu_scratch(H, I));
 #pragma omp for schedule(dynamic, 1)
         for (int64_t r = 0; r < n; ++r) {
-            decode_row(x, xdt, r, H, xv);
-            swiglu_token(xv, H, I, w13, w2, wdt, scratch, y + r * H);
+            decode_row(x, xdt, r, H, xv, NULL);
+            swiglu_token(xv, H, I, w13, w2, wdt, s13, s2, scratch, y + r * H);
         }
         free(xv);
         free(scratch);
     }
+}
+
+void orc_swiglu(const void *x, int xdt, int64_t n, int H, int I, const void *w13, const void *w2,
+                int wdt, double *y)
+{
+    orc_swiglu_s(x, xdt, n, H, I, w13, w2, wdt, NULL, NULL, y);
 }
 
 /*
@@ -264,16 +296,19 @@ void orc_combine(const double *y, const double *w, const double *s, int64_t T, i
 /*
  * The whole layer for T tokens, one token at a time: route the token, run
  * each of its K experts on it, add the shared experts (weight 1, width Is;
- * Is = 0 for none), and combine.  w13 is [E][2I][H], w2 is [E][H][I].
- * ids_out/w_out (nullable) receive the routing.  Returns 0 or the route error.
+ * Is = 0 for none), and combine.  w13 is [E][2I][H], w2 is [E][H][I]; for FP8
+ * weights s13 [E][2I], s2 [E][H], ss13 [2Is], ss2 [H] are the row scales
+ * (NULL otherwise).  ids_out/w_out (nullable) receive the routing.  Returns 0
+ * or the route error.
  */
-int orc_moe_layer(const void *x, int xdt, const float *logits, int64_t T, int H, int I, int E,
-                  int K, const void *w13, const void *w2, int wdt, int Is, const void *ws13,
-                  const void *ws2, int32_t *ids_out, double *w_out, double *out)
+int orc_moe_layer_s(const void *x, int xdt, const float *logits, int64_t T, int H, int I, int E,
+                    int K, const void *w13, const void *w2, int wdt, const float *s13,
+                    const float *s2, int Is, const void *ws13, const void *ws2, const float *ss13,
+                    const float *ss2, int32_t *ids_out, double *w_out, double *out)
 {
     if (E < 1 || K < 1 || K > E || T < 0)
         return -1;
-    const size_t esize = wdt == ORC_F32 ? 4 : 2;
+    const size_t esize = elem_size(wdt);
     int rc = 0;
 #pragma omp parallel
     {
@@ -289,16 +324,18 @@ int orc_moe_layer(const void *x, int xdt, const float *logits, int64_t T, int H,
                 rc = -1;
                 continue;
             }
-            decode_row(x, xdt, t, H, xv);
+            decode_row(x, xdt, t, H, xv, NULL);
             for (int k = 0; k < K; ++k) {
                 const char *e13 = (const char *)w13 + (size_t)ids[k] * 2 * I * H * esize;
                 const char *e2 = (const char *)w2 + (size_t)ids[k] * H * I * esize;
-                swiglu_token(xv, H, I, e13, e2, wdt, scratch, y + (size_t)k * H);
+                const float *es13 = s13 ? s13 + (size_t)ids[k] * 2 * I : NULL;
+                const float *es2 = s2 ? s2 + (size_t)ids[k] * H : NULL;
+                swiglu_token(xv, H, I, e13, e2, wdt, es13, es2, scratch, y + (size_t)k * H);
             }
             double *s = NULL;
             if (Is > 0) {
                 s = y + (size_t)K * H;
-                swiglu_token(xv, H, Is, ws13, ws2, wdt, scratch, s);
+                swiglu_token(xv, H, Is, ws13, ws2, wdt, ss13, ss2, scratch, s);
             }
             orc_combine(y, w, s, 1, K, H, out + t * H);
             if (ids_out)
@@ -313,4 +350,12 @@ int orc_moe_layer(const void *x, int xdt, const float *logits, int64_t T, int H,
         free(w);
     }
     return rc;
+}
+
+int orc_moe_layer(const void *x, int xdt, const float *logits, int64_t T, int H, int I, int E,
+                  int K, const void *w13, const void *w2, int wdt, int Is, const void *ws13,
+                  const void *ws2, int32_t *ids_out, double *w_out, double *out)
+{
+    return orc_moe_layer_s(x, xdt, logits, T, H, I, E, K, w13, w2, wdt, NULL, NULL, Is, ws13, ws2,
+                           NULL, NULL, ids_out, w_out, out);
 }

@@ -11,8 +11,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 
 MUTANTS = {
-    "gate_up_swapped": ("matvec(w13, wdt, 0, I, H, xv, rowbuf, g);\n    matvec(w13, wdt, I, I, H, xv, rowbuf, u);",
-                        "matvec(w13, wdt, I, I, H, xv, rowbuf, g);\n    matvec(w13, wdt, 0, I, H, xv, rowbuf, u);"),
+    "gate_up_swapped": ("matvec(w13, wdt, s13, 0, I, H, xv, rowbuf, g);\n    matvec(w13, wdt, s13, I, I, H, xv, rowbuf, u);",
+                        "matvec(w13, wdt, s13, I, I, H, xv, rowbuf, g);\n    matvec(w13, wdt, s13, 0, I, H, xv, rowbuf, u);"),
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "ties_to_high_id": ("(best < 0 || l[e] > l[best])", "(best < 0 || l[e] >= l[best])"),
     "no_renormalise": ("w[t * K + j] = p[ids[t * K + j]] / s;", "w[t * K + j] = p[ids[t * K + j]];"),
@@ -25,9 +25,13 @@ MUTANTS = {
     "wrong_expert_weights": ("(size_t)ids[k] * 2 * I * H * esize", "(size_t)ids[(k + 1) % K] * 2 * I * H * esize"),
     "combine_slot_mixup": ("acc += w[t * K + k] * y[(t * K + k) * H + h];",
                            "acc += w[t * K + (K - 1 - k)] * y[(t * K + k) * H + h];"),
-    "down_proj_transposed": ("matvec(w2, wdt, 0, H, I, a, rowbuf, y);",
+    "down_proj_transposed": ("matvec(w2, wdt, s2, 0, H, I, a, rowbuf, y);",
                              "for (int hh = 0; hh < H; ++hh) { double s2 = 0; for (int i = 0; i < I; ++i) "
                              "s2 += elem(w2, wdt, (int64_t)i * H + hh) * a[i]; y[hh] = s2; }"),
+    "fp8_exponent_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 9)"),
+    "fp8_subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "fp8_row_scale_ignored": ("const double sc = scale ? (double)scale[row] : 1.0;",
+                              "const double sc = 1.0;"),
     "block_map_overrun": ("for (int64_t b = offsets[e] / B; b < offsets[e + 1] / B; ++b)",
                           "for (int64_t b = offsets[e] / B; b <= offsets[e + 1] / B && b < cap / B; ++b)"),
 }
