@@ -222,6 +222,36 @@ moe_status dense_ffn_fa(const void *x, moe_dtype dt, int64_t T, int H, int I_fa,
                         const void *w2, void *workspace, int64_t workspace_bytes, void *out,
                         moe_dtype odt, moe_schedule sched, void *stream);
 
+/*
+ * FP8 weights: weight quantization, the notes' decode-phase remedy (Serving-tax
+ * notes, "デコード最適化": it cuts the bytes that weight amplification makes the
+ * step read).  Weights are OCP FP8 E4M3 codes (1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN) with one fp32
+ * scale per matrix row: W[r][c] = value(code[r][c]) * scale[r].  x, the
+ * activations and y_pairs are bf16; the codes are expanded to bf16 exactly,
+ * multiplied on bf16 MFMA with fp32 accumulation, and each row's scale is
+ * applied to its accumulators.  The LDS-ring weight-streaming schedule runs
+ * them with passes of up to 32 of an expert's tokens (64 for dense rows);
+ * busier experts take several passes: a decode-shape path.
+ * Shapes: H % 128 == 0 and I % 128 == 0.  Pointers: codes 16-byte aligned,
+ * scales 4-byte aligned.  Same plan and workspace as the bf16 calls.
+ *   moe_grouped_gate_up_fp8: w13 [E][2I][H] codes, w13_scale [E][2I] fp32
+ *   moe_grouped_down_fp8:    w2 [E][H][I] codes,  w2_scale [E][H] fp32
+ *   dense_ffn_fp8:           w13 [2I][H], w13_scale [2I], w2 [H][I], w2_scale [H]
+ * Errors: as their bf16 counterparts; MOE_EUNSUPPORTED for other shapes.
+ */
+moe_status moe_grouped_gate_up_fp8(const void *x, int64_t T, int H, int I, int E, int K,
+                                   const uint8_t *w13, const float *w13_scale,
+                                   const moe_plan *plan, void *workspace, int64_t workspace_bytes,
+                                   void *stream);
+moe_status moe_grouped_down_fp8(const uint8_t *w2, const float *w2_scale, int64_t T, int H, int I,
+                                int E, int K, const moe_plan *plan, const void *workspace,
+                                int64_t workspace_bytes, void *y_pairs, void *stream);
+moe_status dense_ffn_fp8(const void *x, int64_t T, int H, int I, const uint8_t *w13,
+                         const float *w13_scale, const uint8_t *w2, const float *w2_scale,
+                         void *workspace, int64_t workspace_bytes, void *out, moe_dtype odt,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ PAD_BLOCK, PAD_MAX = 0, 1
 EXPORTS = ["moe_last_error", "moe_status_string", "moe_align_capacity", "moe_align_capacity_ex",
            "moe_ffn_workspace_bytes", "dense_ffn_workspace_bytes", "moe_route", "moe_align",
            "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
-           "moe_combine", "dense_ffn_fa"]
+           "moe_combine", "dense_ffn_fa", "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8",
+           "dense_ffn_fp8"]
 
 
 class MoEError(RuntimeError):
@@ -75,6 +76,12 @@ def lib():
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i64, i32, i32, vp, i32, vp]
         L.dense_ffn_fa.restype = i32
         L.dense_ffn_fa.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp, i64, vp, i32, i32, vp]
+        L.moe_grouped_gate_up_fp8.restype = i32
+        L.moe_grouped_gate_up_fp8.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, P, vp, i64, vp]
+        L.moe_grouped_down_fp8.restype = i32
+        L.moe_grouped_down_fp8.argtypes = [vp, vp, i64, i32, i32, i32, i32, P, vp, i64, vp, vp]
+        L.dense_ffn_fp8.restype = i32
+        L.dense_ffn_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, i64, vp, i32, vp]
         _lib = L
     return _lib
 
@@ -192,3 +199,29 @@ def dense_ffn_fa(x, w13, w2, workspace, out, sched=SCHED_AUTO, stream=None):
     _check(lib().dense_ffn_fa(_ptr(x), _dt(x), T, H, I, _ptr(w13), _ptr(w2), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(out), _dt(out),
                               sched, _stream(stream)))
+
+
+def moe_grouped_gate_up_fp8(x, q13, s13, K, plan, workspace, stream=None):
+    """FP8 E4M3 expert weights: q13 uint8 [E,2I,H] codes, s13 fp32 [E,2I] row scales."""
+    T, H = x.shape
+    E, I2, _ = q13.shape
+    _check(lib().moe_grouped_gate_up_fp8(_ptr(x), T, H, I2 // 2, E, K, _ptr(q13), _ptr(s13),
+                                         ctypes.byref(plan.c), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_grouped_down_fp8(q2, s2, T, K, plan, workspace, y_pairs, stream=None):
+    """q2 uint8 [E,H,I] codes, s2 fp32 [E,H] row scales; y_pairs bf16."""
+    E, H, I = q2.shape
+    _check(lib().moe_grouped_down_fp8(_ptr(q2), _ptr(s2), T, H, I, E, K, ctypes.byref(plan.c),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _ptr(y_pairs), _stream(stream)))
+
+
+def dense_ffn_fp8(x, q13, s13, q2, s2, workspace, out, stream=None):
+    T, H = x.shape
+    I = q2.shape[1]
+    _check(lib().dense_ffn_fp8(_ptr(x), T, H, I, _ptr(q13), _ptr(s13), _ptr(q2), _ptr(s2),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _ptr(out), _dt(out), _stream(stream)))
+

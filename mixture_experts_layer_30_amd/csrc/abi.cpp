@@ -131,7 +131,7 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   p.tile_split = 1;
   if (tile2) {
     const int64_t items = (int64_t)(H / 256) * ((T + p.tile_block - 1) / p.tile_block);
-    if (items < 256) {
+    if (items > 0 && items < 256) {
       // one 512-thread workgroup per CU: aim at 256, keeping >= 8 contraction steps a slice
       const int64_t most = I / 64 / 8 > 1 ? I / 64 / 8 : 1;
       const int64_t want = (256 + items - 1) / items;
@@ -327,7 +327,8 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
     moe::RowMap cold = rm, hot = rm;
     cold.max_rows = 16 * nb;
     hot.min_rows = 16 * nb + 1;
-    e = moe::launch_ring_gate_up(x, w13, cold, E, H, I, T, nb, 1, (uint16_t*)workspace, nullptr, s);
+    e = moe::launch_ring_gate_up(x, dt, w13, nullptr, cold, E, H, I, T, nb, 1, (uint16_t*)workspace,
+                                 nullptr, s);
     if (e == hipSuccess && T > 16 * nb)
       e = moe::launch_stream_gate_up(x, dt, w13, hot, E, H, I, stream_tok_blocks(T), 1,
                                      (uint16_t*)workspace, nullptr, s);
@@ -364,8 +365,8 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
     moe::RowMap cold = rm, hot = rm;
     cold.max_rows = 16 * nb;
     hot.min_rows = 16 * nb + 1;
-    e = moe::launch_ring_down(w2, (const uint16_t*)workspace, cold, E, H, I, T, nb, 1, y_pairs, dt,
-                              nullptr, s);
+    e = moe::launch_ring_down(w2, dt, nullptr, (const uint16_t*)workspace, cold, E, H, I, T, nb, 1,
+                              y_pairs, dt, nullptr, s);
     if (e == hipSuccess && T > 16 * nb)
       e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, hot, E, H, I,
                                   stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
@@ -455,17 +456,100 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   float* part = (float*)((char*)workspace + dp.act_bytes);
   hipError_t e =
       use_gu == MOE_SCHED_RING
-          ? moe::launch_ring_gate_up(x, w13, rm, 1, H, I_fa, T, dp.tok_blocks, dp.ring_split_gu,
-                                     act, part, s)
+          ? moe::launch_ring_gate_up(x, dt, w13, nullptr, rm, 1, H, I_fa, T, dp.tok_blocks,
+                                     dp.ring_split_gu, act, part, s)
           : moe::launch_stream_gate_up(x, dt, w13, rm, 1, H, I_fa, dp.tok_blocks, dp.split_gu, act,
                                        part, s);
   if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
   e = use_dn == MOE_SCHED_RING
-          ? moe::launch_ring_down(w2, act, rm, 1, H, I_fa, T, dp.tok_blocks, dp.ring_split_dn,
-                                  out, odt, part, s)
+          ? moe::launch_ring_down(w2, dt, nullptr, act, rm, 1, H, I_fa, T, dp.tok_blocks,
+                                  dp.ring_split_dn, out, odt, part, s)
           : moe::launch_stream_down(w2, dt, act, rm, 1, H, I_fa, dp.tok_blocks, dp.split_dn, out,
                                     odt, part, s);
   return hip_status(e, "dense_ffn_fa down");
+}
+
+static moe_status check_fp8_weights(const void* w, const float* scale, int H, int I,
+                                    const char* what) {
+  if (H % 128 != 0 || I % 128 != 0)
+    return fail(MOE_EUNSUPPORTED, "%s: FP8 weights need H %% 128 == 0 and I %% 128 == 0 "
+                "(H = %d, I = %d)", what, H, I);
+  if (!w || !aligned(w, 16) || !scale || !aligned(scale, 4))
+    return fail(MOE_EINVAL, "%s: NULL or misaligned weights or scales", what);
+  return MOE_OK;
+}
+
+moe_status moe_grouped_gate_up_fp8(const void* x, int64_t T, int H, int I, int E, int K,
+                                   const uint8_t* w13, const float* w13_scale,
+                                   const moe_plan* plan, void* workspace, int64_t workspace_bytes,
+                                   void* stream) {
+  moe_status st = check_grouped(x, MOE_BF16, T, H, I, E, K, plan, workspace_bytes);
+  if (st) return st;
+  st = check_fp8_weights(w13, w13_scale, H, I, "moe_grouped_gate_up_fp8");
+  if (st) return st;
+  if (T == 0) return ok();
+  if (!x || !workspace || !aligned(x, 16) || !aligned(workspace, 16))
+    return fail(MOE_EINVAL, "moe_grouped_gate_up_fp8: NULL or misaligned pointer");
+  const moe::RowMap rm = grouped_rows(plan, K);   // every expert in the ring, in passes
+  hipError_t e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T,
+                                          ring_tok_blocks(T, K, E), 1, (uint16_t*)workspace,
+                                          nullptr, (hipStream_t)stream);
+  return hip_status(e, "moe_grouped_gate_up_fp8");
+}
+
+moe_status moe_grouped_down_fp8(const uint8_t* w2, const float* w2_scale, int64_t T, int H, int I,
+                                int E, int K, const moe_plan* plan, const void* workspace,
+                                int64_t workspace_bytes, void* y_pairs, void* stream) {
+  moe_status st = check_grouped(w2, MOE_BF16, T, H, I, E, K, plan, workspace_bytes);
+  if (st) return st;
+  st = check_fp8_weights(w2, w2_scale, H, I, "moe_grouped_down_fp8");
+  if (st) return st;
+  if (T == 0) return ok();
+  if (!workspace || !y_pairs || !aligned(workspace, 16) || !aligned(y_pairs, 16))
+    return fail(MOE_EINVAL, "moe_grouped_down_fp8: NULL or misaligned pointer");
+  const moe::RowMap rm = grouped_rows(plan, K);
+  hipError_t e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, rm,
+                                       E, H, I, T, ring_tok_blocks(T, K, E), 1, y_pairs,
+                                       moe::kDtBF16, nullptr, (hipStream_t)stream);
+  return hip_status(e, "moe_grouped_down_fp8");
+}
+
+moe_status dense_ffn_fp8(const void* x, int64_t T, int H, int I, const uint8_t* w13,
+                         const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                         void* workspace, int64_t workspace_bytes, void* out, moe_dtype odt,
+                         void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "dense_ffn_fp8: T < 0");
+  if (T >= (int64_t)1 << 31) return fail(MOE_EUNSUPPORTED, "dense_ffn_fp8: T must be < 2^31");
+  if (!valid_dtype(odt)) return fail(MOE_EUNSUPPORTED, "dense_ffn_fp8: dtype");
+  moe_status st = check_ffn_dims(H, I);
+  if (st) return st;
+  st = check_fp8_weights(w13, w13_scale, H, I, "dense_ffn_fp8");
+  if (st) return st;
+  st = check_fp8_weights(w2, w2_scale, H, I, "dense_ffn_fp8");
+  if (st) return st;
+  if (workspace_bytes < dense_ffn_workspace_bytes(T, H, I))
+    return fail(MOE_ECAPACITY, "dense_ffn_fp8: workspace %lld bytes < %lld required",
+                (long long)workspace_bytes, (long long)dense_ffn_workspace_bytes(T, H, I));
+  if (T == 0) return ok();
+  if (!x || !workspace || !out || !aligned(x, 16) || !aligned(workspace, 16) || !aligned(out, 16))
+    return fail(MOE_EINVAL, "dense_ffn_fp8: NULL or misaligned pointer");
+  moe::RowMap rm;
+  memset(&rm, 0, sizeof rm);
+  rm.K = 1;
+  rm.dense_rows = T;
+  rm.block_m = 128;
+  rm.min_rows = 1;
+  rm.max_rows = INT32_MAX;
+  const DensePlan dp = dense_plan(T, H, I, MOE_BF16);
+  uint16_t* act = (uint16_t*)workspace;
+  float* part = (float*)((char*)workspace + dp.act_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, 1, H, I, T,
+                                          dp.tok_blocks, dp.ring_split_gu, act, part, s);
+  if (e != hipSuccess) return hip_status(e, "dense_ffn_fp8 gate/up");
+  e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, act, rm, 1, H, I, T, dp.tok_blocks,
+                            dp.ring_split_dn, out, odt, part, s);
+  return hip_status(e, "dense_ffn_fp8 down");
 }
 
 }  // extern "C"

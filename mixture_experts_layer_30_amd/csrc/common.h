@@ -15,6 +15,8 @@ constexpr int kWave = 64;
 // Storage element types of x and the weights.
 struct F32 { typedef float T; static constexpr int kBytes = 4; };
 struct BF16 { typedef uint16_t T; static constexpr int kBytes = 2; };
+// OCP FP8 E4M3 weight codes (with a per-row fp32 scale held separately)
+struct FP8 { typedef uint8_t T; static constexpr int kBytes = 1; };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

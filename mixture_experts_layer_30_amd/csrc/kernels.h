@@ -8,6 +8,7 @@ namespace moe {
 
 constexpr int kDtF32 = 0;
 constexpr int kDtBF16 = 1;
+constexpr int kDtFP8 = 2;   // weights only: OCP E4M3 codes with fp32 row scales
 
 hipError_t launch_route(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
                         hipStream_t s);
@@ -81,11 +82,12 @@ int ring_gate_up_splits(int64_t rows, int H, int I);
 int ring_down_splits(int64_t rows, int H, int I);
 // T bounds the rows of any expert; tok_blocks (1, 2, 4) is the 16-token blocks
 // per pass over the weights (an expert with more tokens takes more passes).
-hipError_t launch_ring_gate_up(const void* x, const void* w13, const RowMap& rm, int E, int H,
-                               int I, int64_t T, int tok_blocks, int splits, uint16_t* act,
-                               float* part, hipStream_t s);
-hipError_t launch_ring_down(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H,
-                            int I, int64_t T, int tok_blocks, int splits, void* y, int ydt,
-                            float* part, hipStream_t s);
+// wdt: kDtBF16, or kDtFP8 with the row scales w13_scale [E][2I] / w2_scale [E][H].
+hipError_t launch_ring_gate_up(const void* x, int wdt, const void* w13, const float* w13_scale,
+                               const RowMap& rm, int E, int H, int I, int64_t T, int tok_blocks,
+                               int splits, uint16_t* act, float* part, hipStream_t s);
+hipError_t launch_ring_down(const void* w2, int wdt, const float* w2_scale, const uint16_t* act,
+                            const RowMap& rm, int E, int H, int I, int64_t T, int tok_blocks,
+                            int splits, void* y, int ydt, float* part, hipStream_t s);
 
 }  // namespace moe

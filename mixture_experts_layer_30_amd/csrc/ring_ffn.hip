@@ -46,18 +46,26 @@ constexpr int kRWaves = 8;
 constexpr int kRThreads = kRWaves * kWave;
 constexpr int kRRows = 128;      // weight rows per slab
 constexpr int kRK = 128;         // contraction elements per stage
-constexpr int kRRowBytes = 256;  // bytes of one row per stage
-constexpr int kRWLoads = 4;      // direct loads per wavefront per stage for its 16 weight rows
+constexpr int kRRowBytes = 256;  // bytes of one bf16 row per stage (token rows, bf16 weights)
+constexpr int kRLds = 160 * 1024;
 
-// NB: token blocks of 16 per pass.  Stages and token loads per wavefront per
-// stage (every wavefront issues the same number, so one vmcnt bound serves all).
-template <int NB>
-constexpr int ring_stages() { return NB == 4 ? 3 : 4; }
-
+// SW: weight storage (BF16, or FP8 codes with row scales, whose stage rows are
+// 128 bytes).  NB: token blocks of 16 per pass.  A slot holds the slab's 128
+// weight rows and the pass's 16*NB token rows; as many stages as fit (at most
+// 8).  Every wavefront issues the same number of loads per stage, so one vmcnt
+// bound serves all.
+template <class SW>
+constexpr int ring_wrow_bytes() { return kRK * SW::kBytes; }
+template <class SW, int NB>
+constexpr int ring_slot_bytes() { return kRRows * ring_wrow_bytes<SW>() + 16 * NB * kRRowBytes; }
+template <class SW, int NB>
+constexpr int ring_stages() {
+  return kRLds / ring_slot_bytes<SW, NB>() > 8 ? 8 : kRLds / ring_slot_bytes<SW, NB>();
+}
+template <class SW>
+constexpr int ring_wloads() { return 16 * ring_wrow_bytes<SW>() / 1024; }
 template <int NB>
 constexpr int ring_tok_loads() { return NB == 4 ? 2 : 1; }
-template <int NB>
-constexpr int ring_slot_bytes() { return (kRRows + 16 * NB) * kRRowBytes; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -71,10 +79,27 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, kStream ? 2 : 0);
 }
 
-// Byte offset of 16-byte segment s of row r in a stage: segments are permuted
-// by the row's low 4 bits, so the 16 rows a fragment read touches hit 16
-// different 16-byte bank groups.
+// Byte offset of 16-byte segment s of row r in a region of 256-byte rows:
+// segments are permuted by the row's low 4 bits, so the 16 rows a fragment
+// read touches hit 16 different 16-byte bank groups.
 __device__ __forceinline__ int roff(int r, int s) { return r * kRRowBytes + ((s ^ (r & 15)) << 4); }
+
+// The same for 128-byte rows (FP8 weights): segments permuted by bits 1..3 of
+// the row, so the 16 rows of an 8-byte fragment read (two rows per 256 bytes)
+// cover all 64 banks.
+__device__ __forceinline__ int roff8(int r, int s) { return r * 128 + ((s ^ ((r >> 1) & 7)) << 4); }
+
+// 8 FP8 E4M3 codes (two dwords, code j in byte j) as 8 bf16, exactly: every
+// E4M3 value is a bf16 value (v_cvt_scalef32_pk_bf16_fp8 with scale 1; checked
+// against the format's definition for all 256 codes)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint2 v) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
+  return r;
+}
 
 __device__ __forceinline__ void barrier_nf() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -152,16 +177,24 @@ __device__ __forceinline__ void ring_next(RingIt& it, const RowMap& rm, const Ri
 // ids / counts / offsets are the plan's sorted_ids, expert_counts and
 // expert_offsets (unused for dense rows); passed as restrict-qualified
 // arguments, their wave-uniform reads compile to scalar loads.
-template <class SY, int NB, bool kGateUp, bool kDense>
+template <class SW, class SY, int NB, bool kGateUp, bool kDense>
 __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
-    const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
-    RingWork wk, uint16_t* __restrict__ act, typename SY::T* __restrict__ y,
-    float* __restrict__ part, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets) {
-  constexpr int ST = ring_stages<NB>();
-  constexpr int SB = ring_slot_bytes<NB>();
+    const typename SW::T* __restrict__ w, const float* __restrict__ wscale,
+    const uint16_t* __restrict__ xs, RowMap rm, int H, int I, RingWork wk,
+    uint16_t* __restrict__ act, typename SY::T* __restrict__ y, float* __restrict__ part,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets) {
+  constexpr bool kFP8 = SW::kBytes == 1;
+  constexpr int WB = ring_wrow_bytes<SW>();      // bytes of a weight row per stage
+  constexpr int WL = ring_wloads<SW>();          // direct loads per wavefront for its 16 rows
+  constexpr int WRPI = 1024 / WB;                // weight rows per direct load
+  constexpr int WSEG = WB / 16;                  // 16-byte segments per weight row
+  constexpr int TOK0 = kRRows * WB;              // byte offset of the token rows in a slot
+  constexpr int ST = ring_stages<SW, NB>();
+  constexpr int SB = ring_slot_bytes<SW, NB>();
   constexpr int TL = ring_tok_loads<NB>();
-  constexpr int L = kRWLoads + TL;  // vector loads per wavefront per stage
+  constexpr int L = WL + TL;  // vector loads per wavefront per stage
+  static_assert(ST >= 3 && (ST - 2) * L < 64, "stages");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[ST * SB];
 
   RingIt is;
@@ -193,17 +226,20 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
   };
 
   // ---- load side ----
-  // Lane's weight rows for its kRWLoads direct loads (4 rows x 256 B each) and
+  // Lane's weight rows for its WL direct loads (WRPI rows x WB bytes each) and
   // token rows for its TL loads, refreshed at the first stage of every pass.
-  const uint16_t* wsrc[kRWLoads];
+  const uint8_t* wsrc[WL];
   const uint16_t* tsrc[TL];
   auto refresh = [&](const RingIt& it) {
-    const uint16_t* wexp = w + (size_t)it.e * wrows * Kdim;
+    const uint8_t* wexp =
+        reinterpret_cast<const uint8_t*>(w) + (size_t)it.e * wrows * Kdim * SW::kBytes;
 #pragma unroll
-    for (int j = 0; j < kRWLoads; ++j) {
-      const int t = 4 * j + g;
-      const int seg = m ^ t;  // logical segment this lane fetches (row t & 15 == t)
-      wsrc[j] = wexp + (size_t)wrow(it.slab, t) * Kdim + seg * 8;
+    for (int j = 0; j < WL; ++j) {
+      const int t = WRPI * j + lane / WSEG;  // row within the wavefront's 16
+      const int slot = lane % WSEG;
+      // logical segment this lane fetches (the row's permuted slot `slot`)
+      const int seg = kFP8 ? (slot ^ ((t >> 1) & 7)) : (slot ^ t);
+      wsrc[j] = wexp + (size_t)wrow(it.slab, t) * Kdim * SW::kBytes + seg * 16;
     }
     // token rows: NB == 1: rows 2w, 2w+1 (lanes 0..31); NB == 2: rows 4w..4w+3;
     // NB == 4: rows 4w..4w+3 and 32+4w..32+4w+3.  Uniform per 16 lanes.
@@ -217,7 +253,7 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
         const int64_t ri = tok_row(it, rbase + i);
         tr = (g & (nr - 1)) == i ? ri : tr;
       }
-      const int r = kRRows + (NB == 1 ? rbase + (g & 1) : rbase + g);
+      const int r = NB == 1 ? rbase + (g & 1) : rbase + g;   // token row in the slot
       const int seg = m ^ (r & 15);
       tsrc[q] = xs + (size_t)tr * Kdim + seg * 8;
     }
@@ -226,13 +262,13 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
     uint8_t* sl = ring + slot * SB;
     const size_t k = (size_t)it.ks * kRK;
 #pragma unroll
-    for (int j = 0; j < kRWLoads; ++j)
-      load_lds16<true>(wsrc[j] + k, sl + (16 * wave + 4 * j) * kRRowBytes);
+    for (int j = 0; j < WL; ++j)
+      load_lds16<true>(wsrc[j] + k * SW::kBytes, sl + (16 * wave + WRPI * j) * WB);
 #pragma unroll
     for (int q = 0; q < TL; ++q) {
-      const int rbase = kRRows + (NB == 1 ? 2 * wave : 4 * wave + 32 * q);
+      const int rbase = NB == 1 ? 2 * wave : 4 * wave + 32 * q;
       if (NB > 1 || lane < 32)
-        load_lds16<false>(tsrc[q] + k, sl + rbase * kRRowBytes);
+        load_lds16<false>(tsrc[q] + k, sl + TOK0 + rbase * kRRowBytes);
     }
   };
 
@@ -321,11 +357,19 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
     const uint8_t* sl = ring + slot_c * SB;
 #pragma unroll
     for (int kk = 0; kk < kRK / 32; ++kk) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(sl + roff(16 * wave + m, 4 * kk + g));
+      u32x4 a;
+      if (kFP8) {  // 8 codes of row m at k = 32kk + 8g: half (g & 1) of segment 2kk + g/2
+        const uint2 q = *reinterpret_cast<const uint2*>(
+            sl + roff8(16 * wave + m, 2 * kk + (g >> 1)) + 8 * (g & 1));
+        a = fp8x8_to_bf16(q);
+      } else {
+        a = *reinterpret_cast<const u32x4*>(sl + roff(16 * wave + m, 4 * kk + g));
+      }
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
         if (tb < ntb) {
-          const u32x4 b = *reinterpret_cast<const u32x4*>(sl + roff(kRRows + 16 * tb + m, 4 * kk + g));
+          const u32x4 b =
+              *reinterpret_cast<const u32x4*>(sl + TOK0 + roff(16 * tb + m, 4 * kk + g));
           acc[tb] = mfma16x16x32(a, b, acc[tb]);
         }
       }
@@ -337,11 +381,27 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
       // epilogue of the pass: lane holds rows 4g..4g+3 of its tile for token m of each block
       const int base = ic.pass * 16 * NB;
       const int rows = kDense ? (int)rm.dense_rows : 0;
+      // FP8: the row scales of the lane's 4 rows (scalar loads of the wavefront's
+      // 16, then a per-lane pick), applied before the SwiGLU / the store
+      f32x4 rs = f32x4{1.f, 1.f, 1.f, 1.f};
+      if (kFP8) {
+        const float* se = wscale + (size_t)ic.e * wrows;
+        float sv[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) sv[t] = se[wrow(ic.slab, t)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v = sv[q];
+#pragma unroll
+          for (int gg = 1; gg < 4; ++gg) v = g == gg ? sv[4 * gg + q] : v;
+          rs[q] = v;
+        }
+      }
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
         if (tb < ntb) {
           const int j = base + 16 * tb + m;  // row of the pass within the expert
-          const f32x4 v = acc[tb];
+          const f32x4 v = acc[tb] * rs;
           if (kGateUp) {
             if (j < ic.n) {
               const int64_t row = (int64_t)ic.row0 + j;
@@ -426,9 +486,10 @@ int ring_splits(int nslabs, int nks, int64_t rows, int outdim, int G) {
   return best;
 }
 
-template <class SY, int NB, bool kGateUp, bool kDense>
-void ring_go(const void* w, const void* xs, const RowMap& rm, int E, int H, int I, int ksplit,
-             int64_t rows_bound, uint16_t* act, void* y, float* part, hipStream_t s) {
+template <class SW, class SY, int NB, bool kGateUp, bool kDense>
+void ring_go(const void* w, const float* wscale, const void* xs, const RowMap& rm, int E, int H,
+             int I, int ksplit, int64_t rows_bound, uint16_t* act, void* y, float* part,
+             hipStream_t s) {
   RingWork wk;
   wk.nslabs = kGateUp ? I / 64 : H / kRRows;
   wk.nexp = kDense ? 1 : E;
@@ -438,30 +499,77 @@ void ring_go(const void* w, const void* xs, const RowMap& rm, int E, int H, int 
   const int64_t most = (int64_t)wk.nexp * wk.nslabs * ksplit * ((rows_bound + 16 * NB - 1) / (16 * NB));
   const int G = (int)(most < num_cus() ? most : num_cus());
   if (G <= 0) return;
-  hipLaunchKernelGGL((ring_ffn_kernel<SY, NB, kGateUp, kDense>), dim3(G), dim3(kRThreads), 0, s,
-                     static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(xs), rm, H, I,
-                     wk, act, static_cast<typename SY::T*>(y), ksplit > 1 ? part : nullptr,
-                     rm.sorted_ids, rm.counts, rm.offsets);
+  hipLaunchKernelGGL((ring_ffn_kernel<SW, SY, NB, kGateUp, kDense>), dim3(G), dim3(kRThreads), 0,
+                     s, static_cast<const typename SW::T*>(w), wscale,
+                     static_cast<const uint16_t*>(xs), rm, H, I, wk, act,
+                     static_cast<typename SY::T*>(y), ksplit > 1 ? part : nullptr, rm.sorted_ids,
+                     rm.counts, rm.offsets);
 }
 
-template <class SY, bool kGateUp, bool kDense>
-void ring_nb(const void* w, const void* xs, const RowMap& rm, int E, int H, int I, int64_t T,
-             int tok_blocks, int ksplit, uint16_t* act, void* y, float* part, hipStream_t s) {
+template <class SW, class SY, bool kGateUp, bool kDense>
+void ring_nb(const void* w, const float* wscale, const void* xs, const RowMap& rm, int E, int H,
+             int I, int64_t T, int tok_blocks, int ksplit, uint16_t* act, void* y, float* part,
+             hipStream_t s) {
   if (tok_blocks <= 1)
-    ring_go<SY, 1, kGateUp, kDense>(w, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+    ring_go<SW, SY, 1, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
   else if (tok_blocks == 2)
-    ring_go<SY, 2, kGateUp, kDense>(w, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+    ring_go<SW, SY, 2, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
   else
-    ring_go<SY, 4, kGateUp, kDense>(w, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+    ring_go<SW, SY, 4, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+}
+
+template <class SW>
+hipError_t ring_gate_up(const void* x, const void* w13, const float* w13_scale, const RowMap& rm,
+                        int E, int H, int I, int64_t T, int tok_blocks, int splits, uint16_t* act,
+                        float* part, hipStream_t s) {
+  if (rm.counts == nullptr)
+    ring_nb<SW, BF16, true, true>(w13, w13_scale, x, rm, E, H, I, T, tok_blocks, splits, act,
+                                  nullptr, part, s);
+  else
+    ring_nb<SW, BF16, true, false>(w13, w13_scale, x, rm, E, H, I, T, tok_blocks, 1, act, nullptr,
+                                   nullptr, s);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && rm.counts == nullptr && splits > 1)
+    e = launch_finish_gate_up(part, splits, rm.dense_rows, I, act, s);
+  return e;
+}
+
+template <class SW>
+hipError_t ring_down(const void* w2, const float* w2_scale, const uint16_t* act, const RowMap& rm,
+                     int E, int H, int I, int64_t T, int tok_blocks, int splits, void* y, int ydt,
+                     float* part, hipStream_t s) {
+  const bool dense = rm.counts == nullptr;
+  if (!dense) splits = 1;
+  if (ydt == kDtF32) {
+    if (dense)
+      ring_nb<SW, F32, false, true>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, splits, nullptr,
+                                    y, part, s);
+    else
+      ring_nb<SW, F32, false, false>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y,
+                                     nullptr, s);
+  } else {
+    if (dense)
+      ring_nb<SW, BF16, false, true>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, splits,
+                                     nullptr, y, part, s);
+    else
+      ring_nb<SW, BF16, false, false>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y,
+                                      nullptr, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && splits > 1) e = launch_finish_down(part, splits, rm.dense_rows, H, y, ydt, s);
+  return e;
 }
 
 }  // namespace
 
 bool ring_gate_up_ok(int xdt, int wdt, int H, int I) {
-  return xdt == kDtBF16 && wdt == kDtBF16 && H % kRK == 0 && I % 64 == 0;
+  return xdt == kDtBF16 && (wdt == kDtBF16 || wdt == kDtFP8) && H % kRK == 0 &&
+         I % (wdt == kDtFP8 ? kRK : 64) == 0;
 }
 
-bool ring_down_ok(int wdt, int H, int I) { return wdt == kDtBF16 && H % kRRows == 0 && I % kRK == 0; }
+bool ring_down_ok(int wdt, int H, int I) {
+  return (wdt == kDtBF16 || wdt == kDtFP8) && H % kRRows == 0 && I % kRK == 0;
+}
 
 // (sized for 256 CUs, MI355X's count, so that workspace sizes do not depend on
 // the device queried)
@@ -469,34 +577,20 @@ int ring_gate_up_splits(int64_t rows, int H, int I) { return ring_splits(I / 64,
 
 int ring_down_splits(int64_t rows, int H, int I) { return ring_splits(H / kRRows, I / kRK, rows, H, 256); }
 
-hipError_t launch_ring_gate_up(const void* x, const void* w13, const RowMap& rm, int E, int H,
-                               int I, int64_t T, int tok_blocks, int splits, uint16_t* act,
-                               float* part, hipStream_t s) {
-  if (rm.counts == nullptr)
-    ring_nb<BF16, true, true>(w13, x, rm, E, H, I, T, tok_blocks, splits, act, nullptr, part, s);
-  else
-    ring_nb<BF16, true, false>(w13, x, rm, E, H, I, T, tok_blocks, 1, act, nullptr, nullptr, s);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && rm.counts == nullptr && splits > 1)
-    e = launch_finish_gate_up(part, splits, rm.dense_rows, I, act, s);
-  return e;
+hipError_t launch_ring_gate_up(const void* x, int wdt, const void* w13, const float* w13_scale,
+                               const RowMap& rm, int E, int H, int I, int64_t T, int tok_blocks,
+                               int splits, uint16_t* act, float* part, hipStream_t s) {
+  if (wdt == kDtFP8)
+    return ring_gate_up<FP8>(x, w13, w13_scale, rm, E, H, I, T, tok_blocks, splits, act, part, s);
+  return ring_gate_up<BF16>(x, w13, nullptr, rm, E, H, I, T, tok_blocks, splits, act, part, s);
 }
 
-hipError_t launch_ring_down(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H,
-                            int I, int64_t T, int tok_blocks, int splits, void* y, int ydt,
-                            float* part, hipStream_t s) {
-  const bool dense = rm.counts == nullptr;
-  if (!dense) splits = 1;
-  if (ydt == kDtF32) {
-    if (dense) ring_nb<F32, false, true>(w2, act, rm, E, H, I, T, tok_blocks, splits, nullptr, y, part, s);
-    else ring_nb<F32, false, false>(w2, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y, nullptr, s);
-  } else {
-    if (dense) ring_nb<BF16, false, true>(w2, act, rm, E, H, I, T, tok_blocks, splits, nullptr, y, part, s);
-    else ring_nb<BF16, false, false>(w2, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y, nullptr, s);
-  }
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && splits > 1) e = launch_finish_down(part, splits, rm.dense_rows, H, y, ydt, s);
-  return e;
+hipError_t launch_ring_down(const void* w2, int wdt, const float* w2_scale, const uint16_t* act,
+                            const RowMap& rm, int E, int H, int I, int64_t T, int tok_blocks,
+                            int splits, void* y, int ydt, float* part, hipStream_t s) {
+  if (wdt == kDtFP8)
+    return ring_down<FP8>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, splits, y, ydt, part, s);
+  return ring_down<BF16>(w2, nullptr, act, rm, E, H, I, T, tok_blocks, splits, y, ydt, part, s);
 }
 
 }  // namespace moe

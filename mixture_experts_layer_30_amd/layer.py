@@ -26,8 +26,12 @@ def default_block_m(T, K, E):
 
 class MoELayer:
     def __init__(self, shape, inputs, block_m=None, sched=B.SCHED_AUTO, out_dtype=None,
-                 pad=B.PAD_BLOCK):
+                 pad=B.PAD_BLOCK, fp8=False):
+        """fp8: run the experts, shared experts and DenseFA on the FP8 E4M3 codes
+        and row scales of the inputs (keys q13/s13, q2/s2, qs13/ss13, qs2/ss2,
+        qfa13/sfa13, qfa2/sfa2; see synth.add_fp8_weights)."""
         x = inputs["x"]
+        self.fp8 = fp8
         self.shape, self.inputs, self.sched = shape, inputs, sched
         self.T = T = x.shape[0]
         H, I, E, K = shape.hidden, shape.inter, shape.experts, shape.topk
@@ -41,12 +45,12 @@ class MoELayer:
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.y_pairs = torch.empty(max(T * K, 1), H, dtype=x.dtype, device=dev)
         self.out = torch.empty(T, H, dtype=out_dtype or x.dtype, device=dev)
-        self.has_shared = inputs.get("ws13") is not None
+        self.has_shared = inputs.get("qs13" if fp8 else "ws13") is not None
         if self.has_shared:
             self.shared_out = torch.empty(T, H, dtype=torch.float32, device=dev)
             self.shared_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, H, shape.shared_inter), 16),
                                          dtype=torch.uint8, device=dev)
-        if inputs.get("wfa13") is not None:
+        if inputs.get("qfa13" if fp8 else "wfa13") is not None:
             self.fa_out = torch.empty(T, H, dtype=out_dtype or x.dtype, device=dev)
             self.fa_ws = torch.empty(max(B.dense_ffn_workspace_bytes(T, H, shape.dense_fa_inter), 16),
                                      dtype=torch.uint8, device=dev)
@@ -66,17 +70,32 @@ class MoELayer:
             B.moe_align_ex(self.topk_ids, self.shape.experts, self.plan, self.pad)
 
     def gate_up(self):
-        B.moe_grouped_gate_up(self.inputs["x"], self.inputs["w13"], self.shape.topk, self.plan,
-                              self.workspace, self.sched)
+        d = self.inputs
+        if self.fp8:
+            B.moe_grouped_gate_up_fp8(d["x"], d["q13"], d["s13"], self.shape.topk, self.plan,
+                                      self.workspace)
+        else:
+            B.moe_grouped_gate_up(d["x"], d["w13"], self.shape.topk, self.plan, self.workspace,
+                                  self.sched)
 
     def down(self):
-        B.moe_grouped_down(self.inputs["w2"], self.T, self.shape.topk, self.plan, self.workspace,
-                           self.y_pairs, self.sched)
+        d = self.inputs
+        if self.fp8:
+            B.moe_grouped_down_fp8(d["q2"], d["s2"], self.T, self.shape.topk, self.plan,
+                                   self.workspace, self.y_pairs)
+        else:
+            B.moe_grouped_down(d["w2"], self.T, self.shape.topk, self.plan, self.workspace,
+                               self.y_pairs, self.sched)
 
     def shared(self):
         if self.has_shared:
-            B.dense_ffn_fa(self.inputs["x"], self.inputs["ws13"], self.inputs["ws2"], self.shared_ws,
-                           self.shared_out, self.sched)
+            d = self.inputs
+            if self.fp8:
+                B.dense_ffn_fp8(d["x"], d["qs13"], d["ss13"], d["qs2"], d["ss2"], self.shared_ws,
+                                self.shared_out)
+            else:
+                B.dense_ffn_fa(d["x"], d["ws13"], d["ws2"], self.shared_ws, self.shared_out,
+                               self.sched)
 
     def combine(self):
         B.moe_combine(self.y_pairs, self.topk_w, self.out,
@@ -92,8 +111,12 @@ class MoELayer:
         return self.out
 
     def dense_fa(self):
-        B.dense_ffn_fa(self.inputs["x"], self.inputs["wfa13"], self.inputs["wfa2"], self.fa_ws,
-                       self.fa_out, self.sched)
+        d = self.inputs
+        if self.fp8:
+            B.dense_ffn_fp8(d["x"], d["qfa13"], d["sfa13"], d["qfa2"], d["sfa2"], self.fa_ws,
+                            self.fa_out)
+        else:
+            B.dense_ffn_fa(d["x"], d["wfa13"], d["wfa2"], self.fa_ws, self.fa_out, self.sched)
         return self.fa_out
 
     def dense_pa(self):

@@ -118,3 +118,21 @@ def layer_inputs(shape, T, routing=None, seed=0, device="cpu", dense=True, moe=T
         d["wpa13"], d["wpa2"] = swiglu_weights(shape.dense_pa_inter, shape.hidden, shape.dtype, seed,
                                                device, "densepa_w")
     return d
+
+
+# weight tensors of layer_inputs and the keys of their FP8 codes and row scales
+FP8_KEYS = {"w13": ("q13", "s13"), "w2": ("q2", "s2"), "ws13": ("qs13", "ss13"),
+            "ws2": ("qs2", "ss2"), "wfa13": ("qfa13", "sfa13"), "wfa2": ("qfa2", "sfa2")}
+
+
+def add_fp8_weights(d, drop_bf16=False):
+    """Adds FP8 E4M3 codes and row scales of every weight tensor of layer_inputs'
+    dict d (see quantize_fp8_rows); with drop_bf16 the bf16 tensors are released."""
+    for k, (qk, sk) in FP8_KEYS.items():
+        if d.get(k) is not None:
+            d[qk], d[sk] = quantize_fp8_rows(d[k])
+            if drop_bf16:
+                d[k] = None
+        elif k in d:
+            d[qk] = d[sk] = None
+    return d

@@ -57,6 +57,7 @@ def test_align_capacity_bound(L):
     # activations (128-row rounded) plus split-K partial sums
     assert B.dense_ffn_workspace_bytes(1, 128, 512) >= 128 * 512 * 2
     assert B.dense_ffn_workspace_bytes(1, 100, 512) == -1
+    assert B.dense_ffn_workspace_bytes(0, 4096, 28672) >= 0   # empty batch
 
 
 def st(r):
@@ -116,6 +117,27 @@ def test_grouped_ffn_argument_checks(L):
     assert call(args(w13=FAKE + 8)) == B.MOE_EINVAL
     assert call(args(K=9, E=8)) == B.MOE_EINVAL
     assert call(args(T=0)) == B.MOE_OK
+
+
+def test_fp8_argument_checks(L):
+    p = plan(cap=4864)
+    ws = B.moe_ffn_workspace_bytes(4864, 2048)
+    # H not a multiple of 128
+    assert st(L.moe_grouped_gate_up_fp8(FAKE, 128, 192, 2048, 256, 8, FAKE, FAKE, ctypes.byref(p), FAKE,
+                                        ws, None)) == B.MOE_EUNSUPPORTED
+    # missing scales
+    assert st(L.moe_grouped_gate_up_fp8(FAKE, 128, 7168, 2048, 256, 8, FAKE, NULL, ctypes.byref(p), FAKE,
+                                        ws, None)) == B.MOE_EINVAL
+    assert st(L.moe_grouped_down_fp8(FAKE, NULL, 128, 7168, 2048, 256, 8, ctypes.byref(p), FAKE, ws, FAKE,
+                                     None)) == B.MOE_EINVAL
+    # workspace too small
+    assert st(L.moe_grouped_down_fp8(FAKE, FAKE, 128, 7168, 2048, 256, 8, ctypes.byref(p), FAKE, ws - 1,
+                                     FAKE, None)) == B.MOE_ECAPACITY
+    assert st(L.dense_ffn_fp8(FAKE, 4, 4096, 14400, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE,
+                              B.MOE_BF16, None)) == B.MOE_EUNSUPPORTED
+    # empty batch: no-op
+    assert st(L.dense_ffn_fp8(NULL, 0, 4096, 14336, FAKE, FAKE, FAKE, FAKE, NULL, 1 << 30, NULL,
+                              B.MOE_BF16, None)) == B.MOE_OK
 
 
 def test_combine_and_dense_argument_checks(L):

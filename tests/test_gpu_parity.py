@@ -550,3 +550,88 @@ def test_layer_parity_full_size_sampled(name, T, routing):
         assert rel_err(pa[tokens], ref_pa) <= TOL
     del dev, layer
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- FP8 weights
+
+
+def fp8_case(shape, T, routing, seed):
+    d = synth.layer_inputs(shape, T, routing, seed=seed, device="cpu", dense=True)
+    synth.add_fp8_weights(d)
+    dev = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in d.items()}
+    return d, dev
+
+
+FP8_SHAPES = [
+    # (shape, T, routing): one and two token blocks per pass, experts taking several
+    # passes, shared experts, dense contraction splits
+    (LayerShape("fp8_nb1", 256, 256, 8, 2, 128, "bf16", (6,), ("uniform",)), 6, "uniform"),
+    (LayerShape("fp8_nb2", 384, 128, 4, 2, 0, "bf16", (30,), ("zipf",)), 30, "zipf"),
+    (LayerShape("fp8_passes", 256, 256, 8, 2, 256, "bf16", (200,), ("zipf",)), 200, "zipf"),
+    (LayerShape("fp8_items", 128, 512, 64, 6, 0, "bf16", (50,), ("uniform",)), 50, "uniform"),
+]
+
+
+@pytest.mark.parametrize("shape,T,routing", FP8_SHAPES, ids=[s[0].name for s in FP8_SHAPES])
+def test_layer_parity_fp8(shape, T, routing):
+    d, dev = fp8_case(shape, T, routing, seed=17)
+    layer = MoELayer(shape, dev, fp8=True)
+    out = layer.forward().clone()
+    fa = layer.dense_fa().clone()
+    torch.cuda.synchronize()
+    ref, rids, _ = oracle.moe_layer_fp8(d["x"], d["logits"], d["q13"], d["s13"], d["q2"], d["s2"],
+                                        shape.topk, d["qs13"], d["ss13"], d["qs2"], d["ss2"])
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    assert rel_err(out, ref) <= TOL
+    ref_fa = oracle.swiglu_fp8(d["x"], d["qfa13"], d["sfa13"], d["qfa2"], d["sfa2"])
+    assert rel_err(fa, ref_fa) <= TOL
+    out2 = layer.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("T,H,I", [(1, 256, 4096), (40, 128, 1024), (100, 256, 512)])
+def test_dense_ffn_fp8_parity(T, H, I):
+    x = synth.tokens(T, H, "bf16", seed=I + 3)
+    w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T + 3)
+    q13, s13 = synth.quantize_fp8_rows(w13)
+    q2, s2 = synth.quantize_fp8_rows(w2)
+    ref = oracle.swiglu_fp8(x, q13, s13, q2, s2)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(T, H, I), dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    B.dense_ffn_fp8(x.to(DEV), q13.to(DEV), s13.to(DEV), q2.to(DEV), s2.to(DEV), ws, out)
+    torch.cuda.synchronize()
+    assert rel_err(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("name,T,routing", [("mixtral", 32, "uniform"), ("deepseek_v3", 128, "zipf")])
+def test_layer_parity_fp8_full_size_sampled(name, T, routing):
+    shape = configs.CONFIGS[name]
+    print(f"\n[fp8 full-size parity] {name} T={T} {routing}", flush=True)
+    dev = synth.layer_inputs(shape, T, routing, seed=0, device=DEV, dense=False)
+    synth.add_fp8_weights(dev, drop_bf16=True)
+    layer = MoELayer(shape, dev, fp8=True)
+    out = layer.forward()
+    torch.cuda.synchronize()
+    rids = layer.topk_ids.cpu().numpy()
+    counts = np.bincount(rids.ravel(), minlength=shape.experts)
+    hot = int(np.argwhere((rids == counts.argmax()).any(axis=1))[-1, 0])
+    tokens = sorted({0, T // 2, T - 1, hot})
+    used = np.unique(rids[tokens])
+    # only the experts the sampled tokens use are copied to the host
+    q13 = torch.zeros((shape.experts,) + tuple(dev["q13"].shape[1:]), dtype=torch.uint8)
+    q2 = torch.zeros((shape.experts,) + tuple(dev["q2"].shape[1:]), dtype=torch.uint8)
+    for e in used:
+        q13[e] = dev["q13"][e].cpu()
+        q2[e] = dev["q2"][e].cpu()
+    ref, ids, _ = oracle.moe_layer_fp8(dev["x"][tokens].cpu(), dev["logits"][tokens].cpu(), q13,
+                                       dev["s13"].cpu(), q2, dev["s2"].cpu(), shape.topk,
+                                       None if dev["qs13"] is None else dev["qs13"].cpu(),
+                                       None if dev["ss13"] is None else dev["ss13"].cpu(),
+                                       None if dev["qs2"] is None else dev["qs2"].cpu(),
+                                       None if dev["ss2"] is None else dev["ss2"].cpu())
+    assert (ids == rids[tokens]).all()
+    assert rel_err(out[tokens], ref) <= TOL
+    del dev, layer
+    torch.cuda.empty_cache()
+
