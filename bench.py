@@ -383,6 +383,63 @@ def padding_sweep(steps):
                           "intercept_us": round(icpt, 2), "r2": round(float(r2), 5)}), flush=True)
 
 
+def run_fp8(name, T, routing, steps, warmup):
+    """The same pass with FP8 E4M3 expert, shared and DenseFA weights (row scales,
+    bf16 activations): the notes' weight-quantization remedy for the decode tax.
+    Reports tokens/s, the gate/up kernel against the HBM roofline on the FP8
+    bytes, tau against the FP8 DenseFA, and the speed-up over the bf16 pass."""
+    shape = configs.CONFIGS[name]
+    d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=True)
+    bf = MoELayer(shape, d)
+    bf.forward()
+    torch.cuda.synchronize()
+    e_active = int(len(np.unique(bf.topk_ids.cpu().numpy())))
+    ms_bf, _, _ = time_steps(bf.forward, steps, warmup)
+    del bf
+    synth.add_fp8_weights(d, drop_bf16=True)
+    torch.cuda.empty_cache()
+    layer = MoELayer(shape, d, fp8=True)
+    layer.forward()
+    torch.cuda.synchronize()
+
+    def step(a=None, b=None, stream=None):
+        layer.route()
+        layer.align()
+        if a is not None:
+            a.record(stream)
+        layer.gate_up()
+        if b is not None:
+            b.record(stream)
+        layer.down()
+        layer.shared()
+        layer.combine()
+
+    ms, _, gu_ms = time_steps(step, steps, warmup, mid=True)
+    fa_ms, _, _ = time_steps(layer.dense_fa, steps, warmup)
+    H, I, K, Is = shape.hidden, shape.inter, shape.topk, shape.shared_inter
+    # FP8 bytes: codes (1 B) plus fp32 row scales; tokens and activations bf16
+    gu_bytes = e_active * 2 * I * H + e_active * 2 * I * 4 + T * H * 2 + T * K * I * 2
+    layer_bytes = (e_active * 3 * I * H + e_active * (2 * I + H) * 4 + 3 * H * Is + (2 * Is + H) * 4
+                   * (Is > 0) + 2 * T * H * 2 + T * shape.experts * 4)
+    fa_bytes = 3 * H * shape.dense_fa_inter + (2 * shape.dense_fa_inter + H) * 4 + 2 * T * H * 2
+    rec = {"metric": "MoE-layer tokens/s at 1 GPU with FP8 E4M3 weights", "value": round(T / (ms * 1e-3), 2),
+           "unit": "tokens/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+           "dtype": "fp8-e4m3 weights (fp32 row scales), bf16 activations, fp32 accumulation",
+           "config": {"workload": f"{name} T={T} {routing}", "e_active": e_active},
+           "roofline": {"bound": "hbm", "kernel": "ring_ffn_kernel<FP8, ...> (gate/up + SwiGLU)",
+                        "achieved": round(gu_bytes / (gu_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes": gu_bytes},
+           "layer": {"achieved_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "tau_fp8": round(ms / fa_ms, 4),
+           "dense_fa_fp8": {"ms": round(fa_ms, 4), "achieved_GBps": round(fa_bytes / (fa_ms * 1e-3) / 1e9, 1)},
+           "speedup_vs_bf16": round(ms_bf / ms, 4), "bf16_ms_per_step": round(ms_bf, 4)}
+    del d, layer
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,6 +452,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["gate_up", "down", "dense_fa", "layer", "copy"],
                     help="run one piece `--steps` times, untimed (for counter runs)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time the decode workloads with FP8 E4M3 weights (one line each)")
     ap.add_argument("--padding-sweep", action="store_true",
                     help="padded rows, eta and tiled gate/up time vs padded rows (Section 5.1)")
     args = ap.parse_args()
@@ -424,6 +483,13 @@ def main():
         rec = run_workload(name, T, routing, args.steps, args.warmup,
                            do_cpu=(not args.no_cpu) and (i == 0))
         print(json.dumps(rec), flush=True)
+    if args.fp8:
+        shapes = [(n, T, r) for n, T, r in work
+                  if configs.CONFIGS[n].dtype == "bf16" and configs.CONFIGS[n].hidden % 128 == 0
+                  and configs.CONFIGS[n].inter % 128 == 0 and T * configs.CONFIGS[n].topk
+                  < 24 * configs.CONFIGS[n].experts]
+        for name, T, routing in shapes:
+            print(json.dumps(run_fp8(name, T, routing, args.steps, args.warmup)), flush=True)
 
 
 if __name__ == "__main__":

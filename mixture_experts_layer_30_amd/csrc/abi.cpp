@@ -541,14 +541,22 @@ moe_status dense_ffn_fp8(const void* x, int64_t T, int H, int I, const uint8_t* 
   rm.min_rows = 1;
   rm.max_rows = INT32_MAX;
   const DensePlan dp = dense_plan(T, H, I, MOE_BF16);
+  // contraction splits at the FP8 stage length, within the bf16 plan's (which
+  // sized the workspace's partial sums)
+  const int ks_gu = moe::ring_stage_k(moe::kDtFP8, dp.tok_blocks, H);
+  const int ks_dn = moe::ring_stage_k(moe::kDtFP8, dp.tok_blocks, I);
+  int split_gu = moe::ring_gate_up_splits(T, H, I, ks_gu);
+  int split_dn = moe::ring_down_splits(T, H, I, ks_dn);
+  split_gu = split_gu < dp.ring_split_gu ? split_gu : dp.ring_split_gu;
+  split_dn = split_dn < dp.ring_split_dn ? split_dn : dp.ring_split_dn;
   uint16_t* act = (uint16_t*)workspace;
   float* part = (float*)((char*)workspace + dp.act_bytes);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, 1, H, I, T,
-                                          dp.tok_blocks, dp.ring_split_gu, act, part, s);
+                                          dp.tok_blocks, split_gu, act, part, s);
   if (e != hipSuccess) return hip_status(e, "dense_ffn_fp8 gate/up");
   e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, act, rm, 1, H, I, T, dp.tok_blocks,
-                            dp.ring_split_dn, out, odt, part, s);
+                            split_dn, out, odt, part, s);
   return hip_status(e, "dense_ffn_fp8 down");
 }
 

@@ -71,15 +71,19 @@ hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, in
 hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H, void* y,
                               int ydt, hipStream_t s);
 
-// LDS-ring variant of the weight-streaming schedule: bf16 weights and tokens,
-// 128-row weight slabs streamed in 128-k stages by persistent workgroups (one
-// per CU).  *_ok tells whether a shape qualifies; *_splits is the contraction
-// split it uses for `rows` dense rows (part holds [splits][rows][2I] resp.
-// [splits][rows][H] fp32); grouped rows never split.
+// LDS-ring variant of the weight-streaming schedule: bf16 tokens, bf16 or FP8
+// weights, 128-row weight slabs streamed in stages of ring_stage_k contraction
+// elements by persistent workgroups (one per CU).  *_ok tells whether a shape
+// qualifies; *_splits is the contraction split it uses for `rows` dense rows at
+// ks elements per stage (part holds [splits][rows][2I] resp. [splits][rows][H]
+// fp32); grouped rows never split.
 bool ring_gate_up_ok(int xdt, int wdt, int H, int I);
 bool ring_down_ok(int wdt, int H, int I);
-int ring_gate_up_splits(int64_t rows, int H, int I);
-int ring_down_splits(int64_t rows, int H, int I);
+int ring_gate_up_splits(int64_t rows, int H, int I, int ks = 128);
+int ring_down_splits(int64_t rows, int H, int I, int ks = 128);
+// contraction elements per stage for weights wdt, tok_blocks blocks per pass and
+// contraction length kdim: 128, or 256 for FP8 weights with at most 2 blocks
+int ring_stage_k(int wdt, int tok_blocks, int kdim);
 // T bounds the rows of any expert; tok_blocks (1, 2, 4) is the 16-token blocks
 // per pass over the weights (an expert with more tokens takes more passes).
 // wdt: kDtBF16, or kDtFP8 with the row scales w13_scale [E][2I] / w2_scale [E][H].

@@ -45,27 +45,30 @@ namespace moe {
 constexpr int kRWaves = 8;
 constexpr int kRThreads = kRWaves * kWave;
 constexpr int kRRows = 128;      // weight rows per slab
-constexpr int kRK = 128;         // contraction elements per stage
-constexpr int kRRowBytes = 256;  // bytes of one bf16 row per stage (token rows, bf16 weights)
+constexpr int kRK = 128;         // contraction elements per stage of bf16 weights
 constexpr int kRLds = 160 * 1024;
 
-// SW: weight storage (BF16, or FP8 codes with row scales, whose stage rows are
-// 128 bytes).  NB: token blocks of 16 per pass.  A slot holds the slab's 128
-// weight rows and the pass's 16*NB token rows; as many stages as fit (at most
-// 8).  Every wavefront issues the same number of loads per stage, so one vmcnt
+// SW: weight storage (BF16, or FP8 codes with row scales).  KS: contraction
+// elements per stage: 128 for bf16; 256 for FP8 where the token rows leave room
+// (the weight rows of a stage are then 256 contiguous bytes, as for bf16: HBM
+// serves 128-byte pieces of rows 4 KB apart at less than half the rate), else
+// 128.  NB: token blocks of 16 per pass.  A slot holds the slab's 128 weight
+// rows and the pass's 16*NB bf16 token rows; as many stages as fit (at most 8).
+// Every wavefront issues the same number of loads per stage, so one vmcnt
 // bound serves all.
-template <class SW>
-constexpr int ring_wrow_bytes() { return kRK * SW::kBytes; }
-template <class SW, int NB>
-constexpr int ring_slot_bytes() { return kRRows * ring_wrow_bytes<SW>() + 16 * NB * kRRowBytes; }
-template <class SW, int NB>
+template <class SW, int KS>
+constexpr int ring_wrow_bytes() { return KS * SW::kBytes; }
+template <class SW, int KS, int NB>
+constexpr int ring_slot_bytes() { return kRRows * ring_wrow_bytes<SW, KS>() + 16 * NB * 2 * KS; }
+template <class SW, int KS, int NB>
 constexpr int ring_stages() {
-  return kRLds / ring_slot_bytes<SW, NB>() > 8 ? 8 : kRLds / ring_slot_bytes<SW, NB>();
+  return kRLds / ring_slot_bytes<SW, KS, NB>() > 8 ? 8 : kRLds / ring_slot_bytes<SW, KS, NB>();
 }
-template <class SW>
-constexpr int ring_wloads() { return 16 * ring_wrow_bytes<SW>() / 1024; }
-template <int NB>
-constexpr int ring_tok_loads() { return NB == 4 ? 2 : 1; }
+// direct loads per wavefront per stage: its 16 weight rows, its 2*NB token rows
+template <class SW, int KS>
+constexpr int ring_wloads() { return 16 * ring_wrow_bytes<SW, KS>() / 1024; }
+template <int KS, int NB>
+constexpr int ring_tok_loads() { return (2 * NB * 2 * KS + 1023) / 1024; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -79,14 +82,15 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, kStream ? 2 : 0);
 }
 
-// Byte offset of 16-byte segment s of row r in a region of 256-byte rows:
-// segments are permuted by the row's low 4 bits, so the 16 rows a fragment
-// read touches hit 16 different 16-byte bank groups.
-__device__ __forceinline__ int roff(int r, int s) { return r * kRRowBytes + ((s ^ (r & 15)) << 4); }
+// Byte offset of 16-byte segment s of row r in a region of RB-byte rows (RB a
+// multiple of 256): segments are permuted by the row's low 4 bits, so the 16
+// rows a fragment read touches hit 16 different 16-byte bank groups.
+template <int RB>
+__device__ __forceinline__ int roff(int r, int s) { return r * RB + ((s ^ (r & 15)) << 4); }
 
-// The same for 128-byte rows (FP8 weights): segments permuted by bits 1..3 of
-// the row, so the 16 rows of an 8-byte fragment read (two rows per 256 bytes)
-// cover all 64 banks.
+// The same for 128-byte rows (FP8 weights at 128 k per stage): segments
+// permuted by bits 1..3 of the row, so the 16 rows of a fragment read (two rows
+// per 256 bytes) cover all 64 banks.
 __device__ __forceinline__ int roff8(int r, int s) { return r * 128 + ((s ^ ((r >> 1) & 7)) << 4); }
 
 // 8 FP8 E4M3 codes (two dwords, code j in byte j) as 8 bf16, exactly: every
@@ -177,7 +181,7 @@ __device__ __forceinline__ void ring_next(RingIt& it, const RowMap& rm, const Ri
 // ids / counts / offsets are the plan's sorted_ids, expert_counts and
 // expert_offsets (unused for dense rows); passed as restrict-qualified
 // arguments, their wave-uniform reads compile to scalar loads.
-template <class SW, class SY, int NB, bool kGateUp, bool kDense>
+template <class SW, class SY, int KS, int NB, bool kGateUp, bool kDense>
 __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
     const typename SW::T* __restrict__ w, const float* __restrict__ wscale,
     const uint16_t* __restrict__ xs, RowMap rm, int H, int I, RingWork wk,
@@ -185,15 +189,21 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets) {
   constexpr bool kFP8 = SW::kBytes == 1;
-  constexpr int WB = ring_wrow_bytes<SW>();      // bytes of a weight row per stage
-  constexpr int WL = ring_wloads<SW>();          // direct loads per wavefront for its 16 rows
+  constexpr int WB = ring_wrow_bytes<SW, KS>();  // bytes of a weight row per stage
+  constexpr int WL = ring_wloads<SW, KS>();      // direct loads per wavefront for its 16 rows
   constexpr int WRPI = 1024 / WB;                // weight rows per direct load
   constexpr int WSEG = WB / 16;                  // 16-byte segments per weight row
   constexpr int TOK0 = kRRows * WB;              // byte offset of the token rows in a slot
-  constexpr int ST = ring_stages<SW, NB>();
-  constexpr int SB = ring_slot_bytes<SW, NB>();
-  constexpr int TL = ring_tok_loads<NB>();
+  constexpr int TB = 2 * KS;                     // bytes of a token row per stage
+  constexpr int TSEG = TB / 16;                  // lanes per token row in a direct load
+  constexpr int TRPL = 64 / TSEG;                // token rows per direct load
+  constexpr int TRW = 2 * NB;                    // token rows each wavefront loads
+  constexpr int ST = ring_stages<SW, KS, NB>();
+  constexpr int SB = ring_slot_bytes<SW, KS, NB>();
+  constexpr int TL = ring_tok_loads<KS, NB>();
   constexpr int L = WL + TL;  // vector loads per wavefront per stage
+  static_assert(WB == 128 || WB == 256, "weight row bytes");
+  static_assert(TL * TRPL >= TRW && (TL - 1) * TRPL < TRW, "token loads");
   static_assert(ST >= 3 && (ST - 2) * L < 64, "stages");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[ST * SB];
 
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int m = lane & 15, g = lane >> 4;
   const int G = (int)gridDim.x;
-  const int Kdim = kGateUp ? H : I;      // contraction length
+  const int Kdim = kGateUp ? H : I;      // contraction length (a multiple of KS)
   const int64_t wrows = kGateUp ? 2 * (int64_t)I : H;  // weight rows per expert
 
   // Weight row of row t (0..15) of wavefront `wave`'s tile in slab `slab`.
@@ -238,37 +248,39 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
       const int t = WRPI * j + lane / WSEG;  // row within the wavefront's 16
       const int slot = lane % WSEG;
       // logical segment this lane fetches (the row's permuted slot `slot`)
-      const int seg = kFP8 ? (slot ^ ((t >> 1) & 7)) : (slot ^ t);
+      const int seg = WB == 128 ? (slot ^ ((t >> 1) & 7)) : (slot ^ t);
       wsrc[j] = wexp + (size_t)wrow(it.slab, t) * Kdim * SW::kBytes + seg * 16;
     }
-    // token rows: NB == 1: rows 2w, 2w+1 (lanes 0..31); NB == 2: rows 4w..4w+3;
-    // NB == 4: rows 4w..4w+3 and 32+4w..32+4w+3.  Uniform per 16 lanes.
+    // token rows TRW*w .. TRW*w + TRW - 1, TRPL of them per load (TSEG lanes
+    // each; lanes past the last row idle)
 #pragma unroll
     for (int q = 0; q < TL; ++q) {
-      const int rbase = NB == 1 ? 2 * wave : 4 * wave + 32 * q;
-      constexpr int nr = NB == 1 ? 2 : 4;  // rows of this load (lanes of row i: g == i)
+      const int rbase = TRW * wave + TRPL * q;
+      const int i = lane / TSEG;  // row of this load
       int64_t tr = 0;
 #pragma unroll
-      for (int i = 0; i < nr; ++i) {
-        const int64_t ri = tok_row(it, rbase + i);
-        tr = (g & (nr - 1)) == i ? ri : tr;
+      for (int ii = 0; ii < TRPL; ++ii) {
+        if (TRPL * q + ii < TRW) {
+          const int64_t ri = tok_row(it, rbase + ii);
+          tr = i == ii ? ri : tr;
+        }
       }
-      const int r = NB == 1 ? rbase + (g & 1) : rbase + g;   // token row in the slot
-      const int seg = m ^ (r & 15);
+      const int r = rbase + i;   // token row in the slot
+      const int seg = (lane % TSEG) ^ (r & 15);
       tsrc[q] = xs + (size_t)tr * Kdim + seg * 8;
     }
   };
   auto issue = [&](const RingIt& it, int slot) {
     uint8_t* sl = ring + slot * SB;
-    const size_t k = (size_t)it.ks * kRK;
+    const size_t k = (size_t)it.ks * KS;
 #pragma unroll
     for (int j = 0; j < WL; ++j)
       load_lds16<true>(wsrc[j] + k * SW::kBytes, sl + (16 * wave + WRPI * j) * WB);
 #pragma unroll
     for (int q = 0; q < TL; ++q) {
-      const int rbase = NB == 1 ? 2 * wave : 4 * wave + 32 * q;
-      if (NB > 1 || lane < 32)
-        load_lds16<false>(tsrc[q] + k, sl + TOK0 + rbase * kRRowBytes);
+      const int rbase = TRW * wave + TRPL * q;
+      if (TL * TRPL == TRW || TRPL * q + lane / TSEG < TRW)
+        load_lds16<false>(tsrc[q] + k, sl + TOK0 + rbase * TB);
     }
   };
 
@@ -355,22 +367,41 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
 
     const int ntb = min(NB, (ic.n - ic.pass * 16 * NB + 15) / 16);
     const uint8_t* sl = ring + slot_c * SB;
+    if (kFP8) {
+      // 64 k per step: lane reads 16 codes of row m at k = 64kk + 16g .. +15 and
+      // feeds the first 8 to one MFMA, the last 8 to a second one, with the
+      // token values of the same k (the MFMA's k order is immaterial as long as
+      // both operands follow it)
 #pragma unroll
-    for (int kk = 0; kk < kRK / 32; ++kk) {
-      u32x4 a;
-      if (kFP8) {  // 8 codes of row m at k = 32kk + 8g: half (g & 1) of segment 2kk + g/2
-        const uint2 q = *reinterpret_cast<const uint2*>(
-            sl + roff8(16 * wave + m, 2 * kk + (g >> 1)) + 8 * (g & 1));
-        a = fp8x8_to_bf16(q);
-      } else {
-        a = *reinterpret_cast<const u32x4*>(sl + roff(16 * wave + m, 4 * kk + g));
+      for (int kk = 0; kk < KS / 64; ++kk) {
+        const int r = 16 * wave + m;
+        const u32x4 q = *reinterpret_cast<const u32x4*>(
+            sl + (WB == 128 ? roff8(r, 4 * kk + g) : roff<WB>(r, 4 * kk + g)));
+        const u32x4 a0 = fp8x8_to_bf16(uint2{q.x, q.y});
+        const u32x4 a1 = fp8x8_to_bf16(uint2{q.z, q.w});
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          if (tb < ntb) {
+            const uint8_t* tr = sl + TOK0;
+            const u32x4 b0 = *reinterpret_cast<const u32x4*>(tr + roff<TB>(16 * tb + m, 8 * kk + 2 * g));
+            const u32x4 b1 =
+                *reinterpret_cast<const u32x4*>(tr + roff<TB>(16 * tb + m, 8 * kk + 2 * g + 1));
+            acc[tb] = mfma16x16x32(a0, b0, acc[tb]);
+            acc[tb] = mfma16x16x32(a1, b1, acc[tb]);
+          }
+        }
       }
+    } else {
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb) {
-        if (tb < ntb) {
-          const u32x4 b =
-              *reinterpret_cast<const u32x4*>(sl + TOK0 + roff(16 * tb + m, 4 * kk + g));
-          acc[tb] = mfma16x16x32(a, b, acc[tb]);
+      for (int kk = 0; kk < KS / 32; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + roff<WB>(16 * wave + m, 4 * kk + g));
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+          if (tb < ntb) {
+            const u32x4 b =
+                *reinterpret_cast<const u32x4*>(sl + TOK0 + roff<TB>(16 * tb + m, 4 * kk + g));
+            acc[tb] = mfma16x16x32(a, b, acc[tb]);
+          }
         }
       }
     }
@@ -469,11 +500,12 @@ int num_cus() {
 
 // Contraction slices for dense rows: the count minimising the stages on the
 // critical path (rounds of G slab slices x stages per slice) plus the fp32 partial
-// sums' round trip, in units of one stage of all G workgroups.
+// sums' round trip, in units of one stage of all G workgroups (256-byte weight
+// rows per stage).
 int ring_splits(int nslabs, int nks, int64_t rows, int outdim, int G) {
   int best = 1;
   double best_t = 1e30;
-  const double stage_bytes = (double)kRRows * kRRowBytes * G;
+  const double stage_bytes = (double)kRRows * 256 * G;
   for (int ks = 1; ks <= 16 && ks * 4 <= nks; ++ks) {
     const int64_t items = (int64_t)nslabs * ks;
     double t = (double)((items + G - 1) / G) * ((nks + ks - 1) / ks);
@@ -486,7 +518,7 @@ int ring_splits(int nslabs, int nks, int64_t rows, int outdim, int G) {
   return best;
 }
 
-template <class SW, class SY, int NB, bool kGateUp, bool kDense>
+template <class SW, class SY, int KS, int NB, bool kGateUp, bool kDense>
 void ring_go(const void* w, const float* wscale, const void* xs, const RowMap& rm, int E, int H,
              int I, int ksplit, int64_t rows_bound, uint16_t* act, void* y, float* part,
              hipStream_t s) {
@@ -494,12 +526,12 @@ void ring_go(const void* w, const float* wscale, const void* xs, const RowMap& r
   wk.nslabs = kGateUp ? I / 64 : H / kRRows;
   wk.nexp = kDense ? 1 : E;
   wk.ksplit = ksplit;
-  wk.nks = (kGateUp ? H : I) / kRK;
+  wk.nks = (kGateUp ? H : I) / KS;
   // units: at most every expert x slab x slice x pass of T tokens
   const int64_t most = (int64_t)wk.nexp * wk.nslabs * ksplit * ((rows_bound + 16 * NB - 1) / (16 * NB));
   const int G = (int)(most < num_cus() ? most : num_cus());
   if (G <= 0) return;
-  hipLaunchKernelGGL((ring_ffn_kernel<SW, SY, NB, kGateUp, kDense>), dim3(G), dim3(kRThreads), 0,
+  hipLaunchKernelGGL((ring_ffn_kernel<SW, SY, KS, NB, kGateUp, kDense>), dim3(G), dim3(kRThreads), 0,
                      s, static_cast<const typename SW::T*>(w), wscale,
                      static_cast<const uint16_t*>(xs), rm, H, I, wk, act,
                      static_cast<typename SY::T*>(y), ksplit > 1 ? part : nullptr, rm.sorted_ids,
@@ -510,12 +542,22 @@ template <class SW, class SY, bool kGateUp, bool kDense>
 void ring_nb(const void* w, const float* wscale, const void* xs, const RowMap& rm, int E, int H,
              int I, int64_t T, int tok_blocks, int ksplit, uint16_t* act, void* y, float* part,
              hipStream_t s) {
-  if (tok_blocks <= 1)
-    ring_go<SW, SY, 1, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
-  else if (tok_blocks == 2)
-    ring_go<SW, SY, 2, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
-  else
-    ring_go<SW, SY, 4, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+  if constexpr (SW::kBytes == 1) {
+    if (ring_stage_k(kDtFP8, tok_blocks, kGateUp ? H : I) == 256) {
+      if (tok_blocks <= 1)
+        ring_go<SW, SY, 256, 1, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+      else
+        ring_go<SW, SY, 256, 2, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+      return;
+    }
+  }
+  if (tok_blocks <= 1) {
+    ring_go<SW, SY, 128, 1, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+  } else if (tok_blocks == 2) {
+    ring_go<SW, SY, 128, 2, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+  } else {
+    ring_go<SW, SY, 128, 4, kGateUp, kDense>(w, wscale, xs, rm, E, H, I, ksplit, T, act, y, part, s);
+  }
 }
 
 template <class SW>
@@ -573,9 +615,17 @@ bool ring_down_ok(int wdt, int H, int I) {
 
 // (sized for 256 CUs, MI355X's count, so that workspace sizes do not depend on
 // the device queried)
-int ring_gate_up_splits(int64_t rows, int H, int I) { return ring_splits(I / 64, H / kRK, rows, 2 * I, 256); }
+int ring_gate_up_splits(int64_t rows, int H, int I, int ks) {
+  return ring_splits(I / 64, H / ks, rows, 2 * I, 256);
+}
 
-int ring_down_splits(int64_t rows, int H, int I) { return ring_splits(H / kRRows, I / kRK, rows, H, 256); }
+int ring_down_splits(int64_t rows, int H, int I, int ks) {
+  return ring_splits(H / kRRows, I / ks, rows, H, 256);
+}
+
+int ring_stage_k(int wdt, int tok_blocks, int kdim) {
+  return wdt == kDtFP8 && tok_blocks <= 2 && kdim % 256 == 0 ? 256 : kRK;
+}
 
 hipError_t launch_ring_gate_up(const void* x, int wdt, const void* w13, const float* w13_scale,
                                const RowMap& rm, int E, int H, int I, int64_t T, int tok_blocks,

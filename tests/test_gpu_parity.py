@@ -590,7 +590,9 @@ def test_layer_parity_fp8(shape, T, routing):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("T,H,I", [(1, 256, 4096), (40, 128, 1024), (100, 256, 512)])
+# stage lengths: 256 k (T <= 32, contraction a multiple of 256), 128 k with one
+# block (H, I not multiples of 256) and with four blocks (T > 32)
+@pytest.mark.parametrize("T,H,I", [(1, 256, 4096), (8, 384, 640), (40, 128, 1024), (100, 256, 512)])
 def test_dense_ffn_fp8_parity(T, H, I):
     x = synth.tokens(T, H, "bf16", seed=I + 3)
     w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T + 3)
