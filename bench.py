@@ -305,9 +305,10 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
     return rec
 
 
-def run_only(name, T, routing, what, steps):
+def run_only(name, T, routing, what, steps, fp8=False):
     """Runs one piece of the pass `steps` times with nothing else on the GPU in
-    between (for hardware-counter runs of a single kernel)."""
+    between (for hardware-counter runs of a single kernel); fp8: with FP8 E4M3
+    weights."""
     if what == "copy":
         # a plain device copy of known size, to calibrate the byte counters
         n = 1 << 30
@@ -322,7 +323,9 @@ def run_only(name, T, routing, what, steps):
         return
     shape = configs.CONFIGS[name]
     d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=(what == "dense_fa"))
-    layer = MoELayer(shape, d)
+    if fp8:
+        synth.add_fp8_weights(d, drop_bf16=True)
+    layer = MoELayer(shape, d, fp8=fp8)
     layer.route()
     layer.align()
     layer.gate_up()
@@ -335,8 +338,11 @@ def run_only(name, T, routing, what, steps):
         fn()
     torch.cuda.synchronize()
     alg = algorithmic(shape, T, e_active)
+    if fp8:  # 1-byte codes plus fp32 row scales
+        H, I, K = shape.hidden, shape.inter, shape.topk
+        alg["gu_bytes"] = e_active * 2 * I * (H + 4) + T * H * 2 + T * K * I * 2
     print(json.dumps({"only": what, "workload": f"{name} T={T} {routing}", "steps": steps,
-                      "e_active": e_active, "gate_up_algorithmic_bytes": alg["gu_bytes"],
+                      "fp8": fp8, "e_active": e_active, "gate_up_algorithmic_bytes": alg["gu_bytes"],
                       "gate_up_algorithmic_flops": alg["gu_flops"],
                       "dense_fa_algorithmic_flops": alg["fa_flops"]}))
 
@@ -429,7 +435,8 @@ def run_fp8(name, T, routing, steps, warmup):
            "roofline": {"bound": "hbm", "kernel": "ring_ffn_kernel<FP8, ...> (gate/up + SwiGLU)",
                         "achieved": round(gu_bytes / (gu_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes": gu_bytes},
+                        "avg_launch_us": round(gu_ms * 1e3, 2), "algorithmic_bytes": gu_bytes,
+                        "traffic": measured_traffic(f"{name} T={T} {routing} fp8")},
            "layer": {"achieved_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
            "tau_fp8": round(ms / fa_ms, 4),
@@ -470,7 +477,7 @@ def main():
     if args.only:
         shape = configs.CONFIGS[args.config or "mixtral"]
         run_only(args.config or "mixtral", args.T or shape.tokens[0],
-                 args.routing or shape.routing[0], args.only, args.steps)
+                 args.routing or shape.routing[0], args.only, args.steps, fp8=args.fp8)
         return
     if args.all:
         work = ALL
