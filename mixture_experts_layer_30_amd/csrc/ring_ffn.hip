@@ -30,8 +30,10 @@
 //
 // The token rows share the stage with the weights, so more token blocks per
 // pass leave fewer stages in flight; the library runs this kernel with one or
-// two blocks and hands experts with more tokens than a pass to the
-// register-streaming kernel (RowMap min_rows / max_rows).
+// two blocks and, for bf16, hands experts with more tokens than a pass to the
+// register-streaming kernel (RowMap min_rows / max_rows); FP8 experts take as
+// many passes as they need (measured faster than a second launch with four
+// blocks, whose 64 token rows every wavefront reads from LDS per stage).
 //
 // Rows of the alignment (token ids, output rows) and the experts' counts are
 // read with scalar loads, which complete on a different counter than the
@@ -49,11 +51,11 @@ constexpr int kRK = 128;         // contraction elements per stage of bf16 weigh
 constexpr int kRLds = 160 * 1024;
 
 // SW: weight storage (BF16, or FP8 codes with row scales).  KS: contraction
-// elements per stage: 128 for bf16; 256 for FP8 where the token rows leave room
-// (the weight rows of a stage are then 256 contiguous bytes, as for bf16: HBM
+// elements per stage: 128 for bf16; 256 for FP8 with at most two token blocks
+// where the contraction allows (the weight rows of a stage are then 256 contiguous bytes, as for bf16: HBM
 // serves 128-byte pieces of rows 4 KB apart at less than half the rate), else
 // 128.  NB: token blocks of 16 per pass.  A slot holds the slab's 128 weight
-// rows and the pass's 16*NB bf16 token rows; as many stages as fit (at most 8).
+// rows and the pass's 16*NB bf16 token rows; as many stages as fit (3 to 8).
 // Every wavefront issues the same number of loads per stage, so one vmcnt
 // bound serves all.
 template <class SW, int KS>
@@ -166,12 +168,12 @@ __device__ __forceinline__ void ring_next(RingIt& it, const RowMap& rm, const Ri
   ring_slice(it, wk);
   if (++it.slab < wk.nslabs) return;
   it.slab = 0;
-  // next expert with units: tokens, and no more than max_rows of them
+  // next expert with units: tokens, min_rows to max_rows of them
   int n;
   do {
     ++it.e;
     n = kDense ? (int)rm.dense_rows : counts[it.e];
-  } while (it.e < wk.nexp - 1 && (n == 0 || (!kDense && n > rm.max_rows)));
+  } while (it.e < wk.nexp - 1 && (n == 0 || (!kDense && (n > rm.max_rows || n < rm.min_rows))));
   ring_expert<NB, kDense>(it, rm, counts, offsets);
 }
 
@@ -293,7 +295,8 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
     int u = 0;
     if (t < wk.nexp) {
       const int n = kDense ? (int)rm.dense_rows : counts[t];
-      if (kDense || n <= rm.max_rows) u = (n + 16 * NB - 1) / (16 * NB) * wk.nslabs * wk.ksplit;
+      if (kDense || (n >= rm.min_rows && n <= rm.max_rows))
+        u = (n + 16 * NB - 1) / (16 * NB) * wk.nslabs * wk.ksplit;
     }
     int incl = u;  // inclusive scan within the wavefront
 #pragma unroll
@@ -623,6 +626,8 @@ int ring_down_splits(int64_t rows, int H, int I, int ks) {
   return ring_splits(H / kRRows, I / ks, rows, H, 256);
 }
 
+// (four token blocks of 256 k would leave two stages; measured slower than 128 k
+// with five)
 int ring_stage_k(int wdt, int tok_blocks, int kdim) {
   return wdt == kDtFP8 && tok_blocks <= 2 && kdim % 256 == 0 ? 256 : kRK;
 }

@@ -569,6 +569,8 @@ FP8_SHAPES = [
     (LayerShape("fp8_nb2", 384, 128, 4, 2, 0, "bf16", (30,), ("zipf",)), 30, "zipf"),
     (LayerShape("fp8_passes", 256, 256, 8, 2, 256, "bf16", (200,), ("zipf",)), 200, "zipf"),
     (LayerShape("fp8_items", 128, 512, 64, 6, 0, "bf16", (50,), ("uniform",)), 50, "uniform"),
+    # busy experts in several passes at 128 k per stage (H, I not multiples of 256)
+    (LayerShape("fp8_hot128", 384, 384, 8, 2, 0, "bf16", (120,), ("zipf",)), 120, "zipf"),
 ]
 
 
