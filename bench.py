@@ -389,6 +389,66 @@ def padding_sweep(steps):
                           "intercept_us": round(icpt, 2), "r2": round(float(r2), 5)}), flush=True)
 
 
+# expert shapes of the cost profile and the replica counts swept (up to the
+# experts a GPU holds at 8-way expert parallelism, and at most the layer's E)
+COST_REPLICAS = {"mixtral": [1, 2, 4, 8], "qwen2": [1, 2, 4, 8], "deepseek_v3": [1, 2, 4, 8, 16, 32]}
+COST_TOKENS = [1, 2, 4, 8, 16, 32, 48, 64, 96, 128, 160, 192, 224, 256, 320, 384, 512, 768, 1024]
+
+
+def cost_profile(names, steps):
+    """Per-expert cost profile of the TEMPO page (section "Dwa reżimy, jeden
+    próg"): the time of the grouped expert FFN (gate/up + down, the library's
+    automatic schedule) for N tokens shared evenly by G replicas of one expert
+    (distinct weight copies, so each replica streams its own weights), cache
+    flushed before every call; then the max-affine fit t = max(a + bG, c + beta*N)
+    and the threshold n*(G).  One JSON line per expert shape."""
+    import dataclasses
+    from mixture_experts_layer_30_amd.costprofile import fit_max_affine
+    for name in names:
+        base = configs.CONFIGS[name]
+        gs = COST_REPLICAS[name]
+        shp = dataclasses.replace(base, experts=max(gs), topk=1, shared_inter=0)
+        d = synth.layer_inputs(shp, max(COST_TOKENS), "uniform", seed=0, device="cuda", dense=False)
+        pts = []
+        for G in gs:
+            sg = dataclasses.replace(shp, experts=G)
+            row = []
+            for N in COST_TOKENS:
+                if N < G:
+                    continue
+                logits = torch.zeros(N, G, dtype=torch.float32, device="cuda")
+                logits[torch.arange(N), torch.arange(N) % G] = 1.0   # token n -> replica n mod G
+                inp = {"x": d["x"][:N], "logits": logits, "w13": d["w13"][:G], "w2": d["w2"][:G],
+                       "ws13": None, "ws2": None}
+                layer = MoELayer(sg, inp)
+                layer.route()
+                layer.align()
+
+                def fn():
+                    layer.gate_up()
+                    layer.down()
+
+                us = time_flushed(fn, steps)["median_ms"] * 1e3
+                pts.append((G, N, round(us, 2), layer.block_m))
+                row.append(f"{N}:{us:.0f}")
+            print(f"[cost profile] {name} G={G}: " + " ".join(row), file=sys.stderr, flush=True)
+        G, N, t = (np.array([p[i] for p in pts], dtype=np.float64) for i in range(3))
+        f = fit_max_affine(G, N, t)
+        rec = {"cost_profile": name, "hidden": base.hidden, "inter": base.inter, "dtype": base.dtype,
+               "unit": "us", "steps": steps,
+               "fit": {"a": round(f.a, 3), "b": round(f.b, 3), "c": round(f.c, 3), "beta": round(f.beta, 5),
+                       "r2": round(f.r2, 5), "max_rel_err": round(f.max_rel_err, 4),
+                       "points_memory": f.n_memory, "points_compute": f.n_compute},
+               "n_star": {str(g): (None if f.n_star(g) is None else round(f.n_star(g), 1)) for g in gs},
+               "n_star_per_replica": {str(g): (None if f.n_star(g) is None else round(f.n_star(g) / g, 1))
+                                      for g in gs},
+               "expert_weight_bytes": 3 * base.hidden * base.inter * 2,
+               "points": [list(p) for p in pts]}
+        print(json.dumps(rec), flush=True)
+        del d
+        torch.cuda.empty_cache()
+
+
 def run_fp8(name, T, routing, steps, warmup):
     """The same pass with FP8 E4M3 expert, shared and DenseFA weights (row scales,
     bf16 activations): the notes' weight-quantization remedy for the decode tax.
@@ -461,6 +521,8 @@ def main():
                     help="run one piece `--steps` times, untimed (for counter runs)")
     ap.add_argument("--fp8", action="store_true",
                     help="also time the decode workloads with FP8 E4M3 weights (one line each)")
+    ap.add_argument("--cost-profile", action="store_true",
+                    help="per-expert time vs tokens and replicas, max-affine fit and n* (TEMPO page)")
     ap.add_argument("--padding-sweep", action="store_true",
                     help="padded rows, eta and tiled gate/up time vs padded rows (Section 5.1)")
     args = ap.parse_args()
@@ -473,6 +535,9 @@ def main():
         sys.exit(1)
     if args.padding_sweep:
         padding_sweep(args.steps)
+        return
+    if args.cost_profile:
+        cost_profile([args.config] if args.config else list(COST_REPLICAS), args.steps)
         return
     if args.only:
         shape = configs.CONFIGS[args.config or "mixtral"]

@@ -120,6 +120,18 @@ int64_t moe_align_capacity_ex(int64_t T, int K, int E, int block_m, moe_padding 
 /* Workspace bytes moe_grouped_ffn needs: the SwiGLU activations, [cap][I] bf16. */
 int64_t moe_ffn_workspace_bytes(int64_t cap, int I);
 
+/*
+ * Workspace bytes with which moe_grouped_ffn (and its halves, bf16 and FP8)
+ * may also split the contraction of a weight-streaming launch across
+ * workgroups when few experts can be active (T*K or E small: their weight
+ * slabs alone would leave compute units idle): the activations, then fp32
+ * partial sums per pair added in a fixed order by a second kernel.  A
+ * workspace of at least this size selects the split wherever it applies; one
+ * of moe_ffn_workspace_bytes never splits.  The two give results that differ
+ * only in fp32 rounding; each is deterministic.  Returns -1 on bad arguments.
+ */
+int64_t moe_ffn_workspace_bytes_ex(int64_t cap, int64_t T, int K, int E, int H, int I);
+
 /* Workspace bytes dense_ffn_fa needs: the activations of T tokens (bf16) and,
  * when the contraction is split across workgroups, the fp32 partial sums.
  * Returns -1 on unsupported sizes. */
@@ -175,7 +187,8 @@ moe_status moe_align_ex(const int32_t *topk_ids, int64_t T, int K, int E, const 
  * w13      [E][2I][H]   dtype dt; rows 0..I-1 of each expert are W1 (gate),
  *                       rows I..2I-1 are W3 (up)
  * w2       [E][H][I]    dtype dt (down projection, out x in)
- * workspace            >= moe_ffn_workspace_bytes(plan->cap, I) bytes
+ * workspace            >= moe_ffn_workspace_bytes(plan->cap, I) bytes (the
+ *                      _ex size also allows a contraction split, see there)
  * y_pairs  [T*K][H]     dtype dt (out), row p = t*K + k
  * Rows of experts with no tokens are never read: an unused expert's weights
  * cost no HBM traffic.
@@ -192,9 +205,11 @@ moe_status moe_grouped_gate_up(const void *x, moe_dtype dt, int64_t T, int H, in
                                const void *w13, const moe_plan *plan, void *workspace,
                                int64_t workspace_bytes, moe_schedule sched, void *stream);
 
-/* Second half of moe_grouped_ffn: y_pairs[sorted_ids[r]] = W2_e a_r for every valid row r. */
+/* Second half of moe_grouped_ffn: y_pairs[sorted_ids[r]] = W2_e a_r for every valid row r.
+ * Reads the activations from the workspace; with a workspace of the _ex size
+ * it may write partial sums past them. */
 moe_status moe_grouped_down(const void *w2, moe_dtype dt, int64_t T, int H, int I, int E, int K,
-                            const moe_plan *plan, const void *workspace, int64_t workspace_bytes,
+                            const moe_plan *plan, void *workspace, int64_t workspace_bytes,
                             void *y_pairs, moe_schedule sched, void *stream);
 
 /*
@@ -245,7 +260,7 @@ moe_status moe_grouped_gate_up_fp8(const void *x, int64_t T, int H, int I, int E
                                    const moe_plan *plan, void *workspace, int64_t workspace_bytes,
                                    void *stream);
 moe_status moe_grouped_down_fp8(const uint8_t *w2, const float *w2_scale, int64_t T, int H, int I,
-                                int E, int K, const moe_plan *plan, const void *workspace,
+                                int E, int K, const moe_plan *plan, void *workspace,
                                 int64_t workspace_bytes, void *y_pairs, void *stream);
 moe_status dense_ffn_fp8(const void *x, int64_t T, int H, int I, const uint8_t *w13,
                          const float *w13_scale, const uint8_t *w2, const float *w2_scale,

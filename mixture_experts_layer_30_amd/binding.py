@@ -19,8 +19,8 @@ PAD_BLOCK, PAD_MAX = 0, 1
 
 # every function the C header declares
 EXPORTS = ["moe_last_error", "moe_status_string", "moe_align_capacity", "moe_align_capacity_ex",
-           "moe_ffn_workspace_bytes", "dense_ffn_workspace_bytes", "moe_route", "moe_align",
-           "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
+           "moe_ffn_workspace_bytes", "moe_ffn_workspace_bytes_ex", "dense_ffn_workspace_bytes",
+           "moe_route", "moe_align", "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
            "moe_combine", "dense_ffn_fa", "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8",
            "dense_ffn_fp8"]
 
@@ -58,6 +58,8 @@ def lib():
         L.moe_align_capacity_ex.argtypes = [i64, i32, i32, i32, i32]
         L.moe_ffn_workspace_bytes.restype = i64
         L.moe_ffn_workspace_bytes.argtypes = [i64, i32]
+        L.moe_ffn_workspace_bytes_ex.restype = i64
+        L.moe_ffn_workspace_bytes_ex.argtypes = [i64, i64, i32, i32, i32, i32]
         L.dense_ffn_workspace_bytes.restype = i64
         L.dense_ffn_workspace_bytes.argtypes = [i64, i32, i32]
         L.moe_route.restype = i32
@@ -119,6 +121,10 @@ def moe_align_capacity_ex(T, K, E, block_m, pad):
 
 def moe_ffn_workspace_bytes(cap, I):
     return lib().moe_ffn_workspace_bytes(cap, I)
+
+
+def moe_ffn_workspace_bytes_ex(cap, T, K, E, H, I):
+    return lib().moe_ffn_workspace_bytes_ex(cap, T, K, E, H, I)
 
 
 def dense_ffn_workspace_bytes(T, H, I):

@@ -99,6 +99,46 @@ int ring_tok_blocks(int64_t T, int K, int E) {
   return stream_tok_blocks(want < 32 ? want : 32);
 }
 
+// Contraction split of the grouped ring launches: only while every expert fits
+// one pass (no busy experts handed to the register kernel) and the slabs of
+// the experts that can have tokens, min(E, T*K), leave compute units idle.
+// The fp32 partial sums, [split][T*K][2I] resp. [split][T*K][H], follow the
+// activations in the workspace.
+struct GroupedSplit {
+  int gu, dn;
+  int64_t part_bytes;
+};
+
+GroupedSplit grouped_split(int64_t T, int K, int E, int H, int I, int ks) {
+  GroupedSplit g{1, 1, 0};
+  const int nb = ring_tok_blocks(T, K, E);
+  if (T <= 0 || T > 16 * nb || H % 128 || I % 128) return g;
+  const int64_t pairs = T * K;
+  const int64_t experts = pairs < E ? pairs : E;
+  g.gu = moe::ring_grouped_splits(pairs, experts, H, I, true, ks);
+  g.dn = moe::ring_grouped_splits(pairs, experts, H, I, false, ks);
+  const int64_t a = g.gu > 1 ? g.gu * pairs * 2 * I * 4 : 0, b = g.dn > 1 ? g.dn * pairs * H * 4 : 0;
+  g.part_bytes = a > b ? a : b;
+  return g;
+}
+
+int64_t grouped_part_offset(int64_t cap, int I) { return round_up(cap * (int64_t)I * 2, 256); }
+
+// The split a grouped call uses: the plan's (at the weights' stage length ks,
+// at most the bf16 plan's, which sized the workspace), or none when the
+// caller's workspace has no room for the partial sums.
+GroupedSplit grouped_split_for(int64_t T, int K, int E, int H, int I, int ks, int64_t cap,
+                               int64_t workspace_bytes) {
+  GroupedSplit g = grouped_split(T, K, E, H, I, 128);
+  if (workspace_bytes < grouped_part_offset(cap, I) + g.part_bytes) return GroupedSplit{1, 1, 0};
+  if (ks != 128) {
+    const GroupedSplit f = grouped_split(T, K, E, H, I, ks);
+    g.gu = f.gu < g.gu ? f.gu : g.gu;
+    g.dn = f.dn < g.dn ? f.dn : g.dn;
+  }
+  return g;
+}
+
 // Dense FFN plan: workgroups per streaming launch are slabs x splits; the
 // contraction is split (deterministically, partial sums added in slice order)
 // until about 1024 workgroups exist, keeping at least 2 chunks per wavefront.
@@ -228,6 +268,12 @@ int64_t moe_ffn_workspace_bytes(int64_t cap, int I) {
   return cap * (int64_t)I * 2;
 }
 
+int64_t moe_ffn_workspace_bytes_ex(int64_t cap, int64_t T, int K, int E, int H, int I) {
+  if (cap < 0 || T < 0 || K < 1 || E < 1 || H < 1 || I < 1) return -1;
+  const GroupedSplit g = grouped_split(T, K, E, H, I, 128);
+  return grouped_part_offset(cap, I) + g.part_bytes;
+}
+
 int64_t dense_ffn_workspace_bytes(int64_t T, int H, int I_fa) {
   if (T < 0 || H < 64 || I_fa < 64 || H % 64 || I_fa % 64) return -1;
   // sized for the larger of the two storage dtypes' plans
@@ -294,6 +340,7 @@ static moe::RowMap grouped_rows(const moe_plan* plan, int K) {
   rm.block_expert = plan->block_expert;
   rm.K = K;
   rm.dense_rows = 0;
+  rm.inv_pos = plan->inv_pos;
   rm.block_m = plan->block_m;
   rm.min_rows = 1;
   rm.max_rows = INT32_MAX;
@@ -327,8 +374,10 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
     moe::RowMap cold = rm, hot = rm;
     cold.max_rows = 16 * nb;
     hot.min_rows = 16 * nb + 1;
-    e = moe::launch_ring_gate_up(x, dt, w13, nullptr, cold, E, H, I, T, nb, 1, (uint16_t*)workspace,
-                                 nullptr, s);
+    const GroupedSplit g = grouped_split_for(T, K, E, H, I, 128, plan->cap, workspace_bytes);
+    float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
+    e = moe::launch_ring_gate_up(x, dt, w13, nullptr, cold, E, H, I, T, nb, g.gu,
+                                 (uint16_t*)workspace, part, s);
     if (e == hipSuccess && T > 16 * nb)
       e = moe::launch_stream_gate_up(x, dt, w13, hot, E, H, I, stream_tok_blocks(T), 1,
                                      (uint16_t*)workspace, nullptr, s);
@@ -340,7 +389,7 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
 }
 
 moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int I, int E, int K,
-                            const moe_plan* plan, const void* workspace, int64_t workspace_bytes,
+                            const moe_plan* plan, void* workspace, int64_t workspace_bytes,
                             void* y_pairs, moe_schedule sched, void* stream) {
   moe_status st = check_grouped(w2, dt, T, H, I, E, K, plan, workspace_bytes);
   if (st) return st;
@@ -365,8 +414,10 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
     moe::RowMap cold = rm, hot = rm;
     cold.max_rows = 16 * nb;
     hot.min_rows = 16 * nb + 1;
-    e = moe::launch_ring_down(w2, dt, nullptr, (const uint16_t*)workspace, cold, E, H, I, T, nb, 1,
-                              y_pairs, dt, nullptr, s);
+    const GroupedSplit g = grouped_split_for(T, K, E, H, I, 128, plan->cap, workspace_bytes);
+    float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
+    e = moe::launch_ring_down(w2, dt, nullptr, (const uint16_t*)workspace, cold, E, H, I, T, nb,
+                              g.dn, y_pairs, dt, part, s);
     if (e == hipSuccess && T > 16 * nb)
       e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, hot, E, H, I,
                                   stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
@@ -493,14 +544,17 @@ moe_status moe_grouped_gate_up_fp8(const void* x, int64_t T, int H, int I, int E
   // every expert in the ring, busy ones in several passes (measured faster than
   // passes of 64 tokens for them)
   const moe::RowMap rm = grouped_rows(plan, K);
-  hipError_t e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T,
-                                          ring_tok_blocks(T, K, E), 1, (uint16_t*)workspace,
-                                          nullptr, (hipStream_t)stream);
+  const int nb = ring_tok_blocks(T, K, E);
+  const GroupedSplit g = grouped_split_for(T, K, E, H, I, moe::ring_stage_k(moe::kDtFP8, nb, H),
+                                           plan->cap, workspace_bytes);
+  float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
+  hipError_t e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T, nb, g.gu,
+                                          (uint16_t*)workspace, part, (hipStream_t)stream);
   return hip_status(e, "moe_grouped_gate_up_fp8");
 }
 
 moe_status moe_grouped_down_fp8(const uint8_t* w2, const float* w2_scale, int64_t T, int H, int I,
-                                int E, int K, const moe_plan* plan, const void* workspace,
+                                int E, int K, const moe_plan* plan, void* workspace,
                                 int64_t workspace_bytes, void* y_pairs, void* stream) {
   moe_status st = check_grouped(w2, MOE_BF16, T, H, I, E, K, plan, workspace_bytes);
   if (st) return st;
@@ -510,9 +564,13 @@ moe_status moe_grouped_down_fp8(const uint8_t* w2, const float* w2_scale, int64_
   if (!workspace || !y_pairs || !aligned(workspace, 16) || !aligned(y_pairs, 16))
     return fail(MOE_EINVAL, "moe_grouped_down_fp8: NULL or misaligned pointer");
   const moe::RowMap rm = grouped_rows(plan, K);
+  const int nb = ring_tok_blocks(T, K, E);
+  const GroupedSplit g = grouped_split_for(T, K, E, H, I, moe::ring_stage_k(moe::kDtFP8, nb, I),
+                                           plan->cap, workspace_bytes);
+  float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
   hipError_t e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, rm,
-                                       E, H, I, T, ring_tok_blocks(T, K, E), 1, y_pairs,
-                                       moe::kDtBF16, nullptr, (hipStream_t)stream);
+                                       E, H, I, T, nb, g.dn, y_pairs, moe::kDtBF16, part,
+                                       (hipStream_t)stream);
   return hip_status(e, "moe_grouped_down_fp8");
 }
 

@@ -35,6 +35,7 @@ struct RowMap {
   const int32_t* offsets;
   const int32_t* sorted_ids;
   const int32_t* block_expert;
+  const int32_t* inv_pos;   // grouped: alignment row of each pair (-1: pair unused)
   int K;
   int64_t dense_rows;
   int block_m;
@@ -62,14 +63,16 @@ hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const 
                             int64_t nblocks, int H, int I, void* y, int ydt, int ksplit,
                             float* part, hipStream_t s);
 
-// act[r][i] = silu(g) * u with g, u the in-order sums over z < splits of
-// part[z][r][i] and part[z][r][I + i].
+// act[o][i] = silu(g) * u with g, u the in-order sums over z < splits of
+// part[z][r][i] and part[z][r][I + i], o = out_row[r] (r when out_row is null;
+// rows with out_row[r] < 0 are skipped).
 hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, int I,
-                                 uint16_t* act, hipStream_t s);
+                                 uint16_t* act, hipStream_t s, const int32_t* out_row = nullptr);
 
-// y[r][h] = sum over z < splits (in order) of part[z][r][h], rounded to ydt.
+// y[r][h] = sum over z < splits (in order) of part[z][r][h], rounded to ydt
+// (rows with skip[r] < 0 left untouched when skip is not null).
 hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H, void* y,
-                              int ydt, hipStream_t s);
+                              int ydt, hipStream_t s, const int32_t* skip = nullptr);
 
 // LDS-ring variant of the weight-streaming schedule: bf16 tokens, bf16 or FP8
 // weights, 128-row weight slabs streamed in stages of ring_stage_k contraction
@@ -81,6 +84,9 @@ bool ring_gate_up_ok(int xdt, int wdt, int H, int I);
 bool ring_down_ok(int wdt, int H, int I);
 int ring_gate_up_splits(int64_t rows, int H, int I, int ks = 128);
 int ring_down_splits(int64_t rows, int H, int I, int ks = 128);
+// the same for grouped rows: `pairs` partial-sum rows, at most `experts`
+// experts with tokens (each within one pass)
+int ring_grouped_splits(int64_t pairs, int64_t experts, int H, int I, bool gate_up, int ks = 128);
 // contraction elements per stage for weights wdt, tok_blocks blocks per pass and
 // contraction length kdim: 128, or 256 for FP8 weights with at most 2 blocks
 int ring_stage_k(int wdt, int tok_blocks, int kdim);

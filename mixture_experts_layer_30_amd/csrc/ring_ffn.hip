@@ -116,10 +116,11 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 struct RingWork {
-  int nslabs;   // 128-row slabs per expert
-  int nexp;     // experts (1 for dense rows)
-  int ksplit;   // contraction slices (dense rows only)
-  int nks;      // stages over the whole contraction (Kdim / 128)
+  int nslabs;     // 128-row slabs per expert
+  int nexp;       // experts (1 for dense rows)
+  int ksplit;     // contraction slices
+  int nks;        // stages over the whole contraction (Kdim / KS)
+  int64_t prows;  // rows of one slice of partial sums: dense rows, or T*K pairs
 };
 
 // Position in the workgroup's run of work units.  A unit is one pass of up to
@@ -178,8 +179,10 @@ __device__ __forceinline__ void ring_next(RingIt& it, const RowMap& rm, const Ri
 }
 
 // kGateUp: w = w13 [E][2I][H], xs = x [T][H], writes act [rows][I] (or fp32 gate/up
-// sums to part [ksplit][rows][2I]).  Down: w = w2 [E][H][I], xs = act, writes
-// y [pairs][H] at the pair of each row (or fp32 sums to part [ksplit][rows][H]).
+// sums to part [ksplit][prows][2I]).  Down: w = w2 [E][H][I], xs = act, writes
+// y [pairs][H] at the pair of each row (or fp32 sums to part [ksplit][prows][H]).
+// Partial sums of grouped rows are indexed by pair, so that a finish kernel
+// can add them without the alignment.
 // ids / counts / offsets are the plan's sorted_ids, expert_counts and
 // expert_offsets (unused for dense rows); passed as restrict-qualified
 // arguments, their wave-uniform reads compile to scalar loads.
@@ -414,7 +417,7 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
     if (ic.ks + 1 == ic.ks1) {
       // epilogue of the pass: lane holds rows 4g..4g+3 of its tile for token m of each block
       const int base = ic.pass * 16 * NB;
-      const int rows = kDense ? (int)rm.dense_rows : 0;
+      const int64_t prows = wk.prows;
       // FP8: the row scales of the lane's 4 rows (scalar loads of the wavefront's
       // 16, then a per-lane pick), applied before the SwiGLU / the store
       f32x4 rs = f32x4{1.f, 1.f, 1.f, 1.f};
@@ -436,12 +439,26 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
         if (tb < ntb) {
           const int j = base + 16 * tb + m;  // row of the pass within the expert
           const f32x4 v = acc[tb] * rs;
+          // pair of each token column (grouped down, and grouped partial sums):
+          // scalar loads of the block's 16 alignment rows, then a per-lane pick
+          int64_t pair = j;
+          if (!kDense && (!kGateUp || part)) {
+            const int jb = base + 16 * tb;
+            const int last = ic.n - 1 - jb;  // last valid column of this block
+            int d = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int di = ids[ic.row0 + jb + (i < last ? i : last)];
+              d = m == i ? di : d;
+            }
+            pair = d;
+          }
           if (kGateUp) {
             if (j < ic.n) {
               const int64_t row = (int64_t)ic.row0 + j;
               const int c = ic.slab * 64 + 8 * wave + 2 * g;
               if (part) {
-                float* pr = part + ((size_t)ic.z * rows + row) * (2 * (size_t)I);
+                float* pr = part + ((size_t)ic.z * prows + pair) * (2 * (size_t)I);
                 pr[c] = v.x;
                 pr[c + 1] = v.y;
                 pr[I + c] = v.z;
@@ -452,25 +469,11 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
               }
             }
           } else {
-            // output row of each token column (pair index for grouped rows)
-            int64_t dst;
-            if (kDense) {
-              dst = j;
-            } else {
-              const int jb = base + 16 * tb;
-              const int last = ic.n - 1 - jb;  // last valid column of this block
-              int d = 0;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int di = ids[ic.row0 + jb + (i < last ? i : last)];
-                d = m == i ? di : d;
-              }
-              dst = d;
-            }
+            const int64_t dst = pair;  // output row: the token (dense) or the pair
             if (j < ic.n) {
               const int h = ic.slab * kRRows + 16 * wave + 4 * g;
               if (part) {
-                *reinterpret_cast<f32x4*>(part + ((size_t)ic.z * rows + dst) * H + h) = v;
+                *reinterpret_cast<f32x4*>(part + ((size_t)ic.z * prows + dst) * H + h) = v;
               } else {
                 typename SY::T* o = y + (size_t)dst * H + h;
                 store_out<SY>(o + 0, v.x);
@@ -530,6 +533,7 @@ void ring_go(const void* w, const float* wscale, const void* xs, const RowMap& r
   wk.nexp = kDense ? 1 : E;
   wk.ksplit = ksplit;
   wk.nks = (kGateUp ? H : I) / KS;
+  wk.prows = kDense ? rm.dense_rows : rows_bound * rm.K;
   // units: at most every expert x slab x slice x pass of T tokens
   const int64_t most = (int64_t)wk.nexp * wk.nslabs * ksplit * ((rows_bound + 16 * NB - 1) / (16 * NB));
   const int G = (int)(most < num_cus() ? most : num_cus());
@@ -567,15 +571,18 @@ template <class SW>
 hipError_t ring_gate_up(const void* x, const void* w13, const float* w13_scale, const RowMap& rm,
                         int E, int H, int I, int64_t T, int tok_blocks, int splits, uint16_t* act,
                         float* part, hipStream_t s) {
-  if (rm.counts == nullptr)
+  const bool dense = rm.counts == nullptr;
+  if (dense)
     ring_nb<SW, BF16, true, true>(w13, w13_scale, x, rm, E, H, I, T, tok_blocks, splits, act,
                                   nullptr, part, s);
   else
-    ring_nb<SW, BF16, true, false>(w13, w13_scale, x, rm, E, H, I, T, tok_blocks, 1, act, nullptr,
-                                   nullptr, s);
+    ring_nb<SW, BF16, true, false>(w13, w13_scale, x, rm, E, H, I, T, tok_blocks, splits, act,
+                                   nullptr, part, s);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && rm.counts == nullptr && splits > 1)
-    e = launch_finish_gate_up(part, splits, rm.dense_rows, I, act, s);
+  // grouped partial sums are per pair: the finish writes each to its alignment row
+  if (e == hipSuccess && splits > 1)
+    e = dense ? launch_finish_gate_up(part, splits, rm.dense_rows, I, act, s)
+              : launch_finish_gate_up(part, splits, T * rm.K, I, act, s, rm.inv_pos);
   return e;
 }
 
@@ -584,24 +591,25 @@ hipError_t ring_down(const void* w2, const float* w2_scale, const uint16_t* act,
                      int E, int H, int I, int64_t T, int tok_blocks, int splits, void* y, int ydt,
                      float* part, hipStream_t s) {
   const bool dense = rm.counts == nullptr;
-  if (!dense) splits = 1;
   if (ydt == kDtF32) {
     if (dense)
       ring_nb<SW, F32, false, true>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, splits, nullptr,
                                     y, part, s);
     else
-      ring_nb<SW, F32, false, false>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y,
-                                     nullptr, s);
+      ring_nb<SW, F32, false, false>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, splits,
+                                     nullptr, y, part, s);
   } else {
     if (dense)
       ring_nb<SW, BF16, false, true>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, splits,
                                      nullptr, y, part, s);
     else
-      ring_nb<SW, BF16, false, false>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, 1, nullptr, y,
-                                      nullptr, s);
+      ring_nb<SW, BF16, false, false>(w2, w2_scale, act, rm, E, H, I, T, tok_blocks, splits,
+                                      nullptr, y, part, s);
   }
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && splits > 1) e = launch_finish_down(part, splits, rm.dense_rows, H, y, ydt, s);
+  if (e == hipSuccess && splits > 1)
+    e = dense ? launch_finish_down(part, splits, rm.dense_rows, H, y, ydt, s)
+              : launch_finish_down(part, splits, T * rm.K, H, y, ydt, s, rm.inv_pos);
   return e;
 }
 
@@ -624,6 +632,12 @@ int ring_gate_up_splits(int64_t rows, int H, int I, int ks) {
 
 int ring_down_splits(int64_t rows, int H, int I, int ks) {
   return ring_splits(H / kRRows, I / ks, rows, H, 256);
+}
+
+int ring_grouped_splits(int64_t pairs, int64_t experts, int H, int I, bool gate_up, int ks) {
+  const int64_t slabs = experts * (gate_up ? I / 64 : H / kRRows);
+  if (slabs >= 256) return 1;
+  return ring_splits((int)slabs, (gate_up ? H : I) / ks, pairs, gate_up ? 2 * I : H, 256);
 }
 
 // (four token blocks of 256 k would leave two stages; measured slower than 128 k

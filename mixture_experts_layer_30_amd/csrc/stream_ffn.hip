@@ -314,26 +314,31 @@ __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void str
 // Split-K finish (dense rows only): sums the gridDim.z slices in slice order.
 __global__ __launch_bounds__(256) void finish_gate_up_kernel(const float* __restrict__ part,
                                                              int splits, int64_t rows, int I,
-                                                             uint16_t* __restrict__ act) {
+                                                             uint16_t* __restrict__ act,
+                                                             const int32_t* __restrict__ out_row) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * I) return;
   const int64_t r = idx / I;
   const int i = (int)(idx % I);
+  const int64_t o = out_row ? out_row[r] : r;
+  if (o < 0) return;
   float g = 0.f, u = 0.f;
   for (int z = 0; z < splits; ++z) {
     const float* pr = part + ((size_t)z * rows + r) * (2 * (size_t)I);
     g += pr[i];
     u += pr[I + i];
   }
-  act[r * I + i] = f32_to_bf16(silu(g) * u);
+  act[o * I + i] = f32_to_bf16(silu(g) * u);
 }
 
 template <class SY>
 __global__ __launch_bounds__(256) void finish_down_kernel(const float* __restrict__ part,
                                                           int splits, int64_t rows, int H,
-                                                          typename SY::T* __restrict__ y) {
+                                                          typename SY::T* __restrict__ y,
+                                                          const int32_t* __restrict__ skip) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * H) return;
+  if (skip && skip[idx / H] < 0) return;
   float s = 0.f;
   for (int z = 0; z < splits; ++z) s += part[(size_t)z * rows * H + idx];
   store_out<SY>(y + idx, s);
@@ -407,23 +412,25 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
 }
 
 hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, int I,
-                                 uint16_t* act, hipStream_t s) {
+                                 uint16_t* act, hipStream_t s, const int32_t* out_row) {
   const int64_t n = rows * I;
+  if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(finish_gate_up_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     part, splits, rows, I, act);
+                     part, splits, rows, I, act, out_row);
   return hipGetLastError();
 }
 
 hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H, void* y,
-                              int ydt, hipStream_t s) {
+                              int ydt, hipStream_t s, const int32_t* skip) {
   const int64_t n = rows * H;
+  if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (ydt == kDtF32)
     hipLaunchKernelGGL(finish_down_kernel<F32>, dim3(blocks), dim3(256), 0, s, part, splits, rows,
-                       H, static_cast<float*>(y));
+                       H, static_cast<float*>(y), skip);
   else
     hipLaunchKernelGGL(finish_down_kernel<BF16>, dim3(blocks), dim3(256), 0, s, part, splits,
-                       rows, H, static_cast<uint16_t*>(y));
+                       rows, H, static_cast<uint16_t*>(y), skip);
   return hipGetLastError();
 }
 

@@ -41,7 +41,8 @@ class MoELayer:
         self.topk_w = torch.empty(T, K, dtype=torch.float32, device=dev)
         self.pad = pad
         self.plan = B.Plan(T, K, E, self.block_m, dev, pad=pad)
-        ws = B.moe_ffn_workspace_bytes(self.plan.cap, I)
+        # with room for the contraction split of few-expert decode launches
+        ws = B.moe_ffn_workspace_bytes_ex(self.plan.cap, T, K, E, H, I)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
         self.y_pairs = torch.empty(max(T * K, 1), H, dtype=x.dtype, device=dev)
         self.out = torch.empty(T, H, dtype=out_dtype or x.dtype, device=dev)

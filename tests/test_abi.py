@@ -54,6 +54,20 @@ def test_align_capacity_bound(L):
     assert B.moe_align_capacity_ex(128, 8, 256, 16, B.PAD_BLOCK) == B.moe_align_capacity(128, 8, 256, 16)
     assert B.moe_align_capacity_ex(100, 2, 8, 64, B.PAD_MAX) == 8 * 128
     assert B.moe_align_capacity_ex(100, 2, 8, 64, 7) == -1
+    # grouped FFN with room for a contraction split: the activations (256-byte
+    # rounded) plus fp32 partial sums per pair, only where few experts can have
+    # tokens (Mixtral at one token: 2 experts x 32 down slabs) ...
+    cap = B.moe_align_capacity(1, 2, 8, 16)
+    ex = B.moe_ffn_workspace_bytes_ex(cap, 1, 2, 8, 4096, 14336)
+    assert ex > B.moe_ffn_workspace_bytes(cap, 14336)
+    assert (ex - cap * 14336 * 2) % (2 * 4096 * 4) == 0   # whole [split][pairs][H] fp32 slices
+    # ... and not once the experts' slabs fill the GPU or a pass cannot hold the tokens
+    cap = B.moe_align_capacity(32, 2, 8, 16)
+    assert B.moe_ffn_workspace_bytes_ex(cap, 32, 2, 8, 4096, 14336) == cap * 14336 * 2
+    cap = B.moe_align_capacity(2048, 8, 64, 128)
+    assert B.moe_ffn_workspace_bytes_ex(cap, 2048, 8, 64, 3584, 2560) == cap * 2560 * 2
+    assert B.moe_ffn_workspace_bytes_ex(cap, 2048, 0, 64, 3584, 2560) == -1
+    assert B.moe_ffn_workspace_bytes_ex(-1, 1, 2, 8, 4096, 14336) == -1
     # activations (128-row rounded) plus split-K partial sums
     assert B.dense_ffn_workspace_bytes(1, 128, 512) >= 128 * 512 * 2
     assert B.dense_ffn_workspace_bytes(1, 100, 512) == -1

@@ -369,6 +369,34 @@ def test_layer_parity_ring(shape, T, routing, block_m):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("T,routing", [(1, "uniform"), (3, "zipf"), (17, "uniform")])
+def test_grouped_split_parity(T, routing, fp8):
+    """Few experts with tokens: with the _ex workspace the ring launches split
+    their contraction (partial sums per pair, added by the finish kernels);
+    with the minimal workspace they do not.  Both match the oracle, and the
+    split pass repeats bit for bit."""
+    shape = LayerShape("split", 2048, 1024, 4, 2, 0, "bf16", (T,), (routing,))
+    d, dev = (fp8_case if fp8 else layer_case)(shape, T, routing, seed=23)
+    layer = MoELayer(shape, dev, fp8=fp8)
+    ws_min = B.moe_ffn_workspace_bytes(layer.plan.cap, shape.inter)
+    assert layer.workspace.numel() > ws_min          # a split is planned
+    out = layer.forward().clone()
+    out_rep = layer.forward().clone()
+    layer.workspace = torch.empty(ws_min, dtype=torch.uint8, device=DEV)
+    out_min = layer.forward().clone()
+    torch.cuda.synchronize()
+    if fp8:
+        ref, rids, _ = oracle.moe_layer_fp8(d["x"], d["logits"], d["q13"], d["s13"], d["q2"], d["s2"],
+                                            shape.topk)
+    else:
+        ref, rids, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], shape.topk)
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    assert rel_err(out, ref) <= TOL
+    assert rel_err(out_min, ref) <= TOL
+    assert torch.equal(out, out_rep)
+
+
 DENSE_RING_CASES = [
     # (T, H, I): down projection split 8 ways (32 stages, 2 slabs); several token
     # blocks; a ragged last block; two passes of four blocks
@@ -503,6 +531,7 @@ def oracle_rows(dev, shape, tokens, hw):
 
 
 FULL_CASES = [
+    ("mixtral", 1, "uniform"),     # two experts: the down projection splits its contraction
     ("mixtral", 32, "uniform"),
     ("mixtral", 1024, "uniform"),
     ("qwen2", 1, "zipf"),
@@ -608,7 +637,8 @@ def test_dense_ffn_fp8_parity(T, H, I):
     assert rel_err(out, ref) <= TOL
 
 
-@pytest.mark.parametrize("name,T,routing", [("mixtral", 32, "uniform"), ("deepseek_v3", 128, "zipf")])
+@pytest.mark.parametrize("name,T,routing", [("mixtral", 1, "uniform"), ("mixtral", 32, "uniform"),
+                                            ("deepseek_v3", 128, "zipf")])
 def test_layer_parity_fp8_full_size_sampled(name, T, routing):
     shape = configs.CONFIGS[name]
     print(f"\n[fp8 full-size parity] {name} T={T} {routing}", flush=True)
