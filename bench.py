@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from mixture_experts_layer_30_amd import configs, synth, taxmodel  # noqa: E402
+from mixture_experts_layer_30_amd import binding as B  # noqa: E402
 from mixture_experts_layer_30_amd.layer import MoELayer  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
@@ -66,13 +67,17 @@ def measured_traffic(workload):
 
 
 def gate_up_kernel(shape, T, block_m):
-    """The kernel the library's automatic schedule runs for the gate/up half
+    """The kernel(s) the library's automatic schedule runs for the gate/up half
     (mirrors the choice made in the C ABI; for the record only)."""
     H, I, K, E = shape.hidden, shape.inter, shape.topk, shape.experts
-    if block_m in (64, 128) and H % 128 == 0 and T * K >= 24 * E:
+    tile = block_m in (64, 128) and H % 128 == 0
+    if tile and T * K >= 24 * E:
         return "tile2_ffn_kernel (MFMA tiles through an LDS ring)"
     if shape.dtype == "bf16" and H % 128 == 0 and I % 64 == 0:
-        return "ring_ffn_kernel (LDS-ring weight streaming, gate/up + SwiGLU)"
+        if T <= 32:
+            return "ring_ffn_kernel (LDS-ring weight streaming, gate/up + SwiGLU)"
+        return ("ring_ffn_kernel (experts within a ring pass) + "
+                + ("tile2_ffn_kernel" if tile else "stream_gate_up_kernel") + " (busier experts)")
     return "stream_gate_up_kernel (register weight streaming, gate/up + SwiGLU)"
 
 
@@ -352,7 +357,6 @@ def padding_sweep(steps):
     and the padding factor eta = P / (T*K) of block-wise and max padding for
     B in 16..256, and the tiled gate/up kernel's time against P (B = 64, 128)
     with a least-squares line per B; one JSON line per point, then the fits."""
-    from mixture_experts_layer_30_amd import binding as B
     shape = configs.CONFIGS["qwen2"]
     E, K = shape.experts, shape.topk
     points = []
@@ -420,30 +424,43 @@ def cost_profile(names, steps):
                 logits[torch.arange(N), torch.arange(N) % G] = 1.0   # token n -> replica n mod G
                 inp = {"x": d["x"][:N], "logits": logits, "w13": d["w13"][:G], "w2": d["w2"][:G],
                        "ws13": None, "ws2": None}
-                layer = MoELayer(sg, inp)
-                layer.route()
-                layer.align()
+                # the automatic schedule, then the weight-streaming and the tiled
+                # schedules forced (the tile needs 64- or 128-row blocks)
+                us = {}
+                for key, kw in (("auto", {}), ("stream", {"sched": B.SCHED_RING}),
+                                ("tile", {"sched": B.SCHED_TILE,
+                                          "block_m": 128 if N >= 128 * G else 64})):
+                    layer = MoELayer(sg, inp, **kw)
+                    layer.route()
+                    layer.align()
 
-                def fn():
-                    layer.gate_up()
-                    layer.down()
+                    def fn():
+                        layer.gate_up()
+                        layer.down()
 
-                us = time_flushed(fn, steps)["median_ms"] * 1e3
-                pts.append((G, N, round(us, 2), layer.block_m))
-                row.append(f"{N}:{us:.0f}")
-            print(f"[cost profile] {name} G={G}: " + " ".join(row), file=sys.stderr, flush=True)
-        G, N, t = (np.array([p[i] for p in pts], dtype=np.float64) for i in range(3))
-        f = fit_max_affine(G, N, t)
+                    us[key] = round(time_flushed(fn, steps)["median_ms"] * 1e3, 2)
+                pts.append((G, N, us["auto"], us["stream"], us["tile"]))
+                row.append(f"{N}:{us['auto']:.0f}/{us['stream']:.0f}/{us['tile']:.0f}")
+            print(f"[cost profile] {name} G={G} (auto/stream/tile us): " + " ".join(row),
+                  file=sys.stderr, flush=True)
+        G, N, t_auto, t_str, t_tile = (np.array([p[i] for p in pts], dtype=np.float64)
+                                       for i in range(5))
+
+        def fit_rec(t):
+            f = fit_max_affine(G, N, t)
+            return {"a": round(f.a, 3), "b": round(f.b, 3), "c": round(f.c, 3), "beta": round(f.beta, 5),
+                    "r2": round(f.r2, 5), "max_rel_err": round(f.max_rel_err, 4),
+                    "points_memory": f.n_memory, "points_compute": f.n_compute,
+                    "n_star": {str(g): (None if f.n_star(g) is None else round(f.n_star(g), 1))
+                               for g in gs}}
+
         rec = {"cost_profile": name, "hidden": base.hidden, "inter": base.inter, "dtype": base.dtype,
                "unit": "us", "steps": steps,
-               "fit": {"a": round(f.a, 3), "b": round(f.b, 3), "c": round(f.c, 3), "beta": round(f.beta, 5),
-                       "r2": round(f.r2, 5), "max_rel_err": round(f.max_rel_err, 4),
-                       "points_memory": f.n_memory, "points_compute": f.n_compute},
-               "n_star": {str(g): (None if f.n_star(g) is None else round(f.n_star(g), 1)) for g in gs},
-               "n_star_per_replica": {str(g): (None if f.n_star(g) is None else round(f.n_star(g) / g, 1))
-                                      for g in gs},
+               "fit_auto": fit_rec(t_auto),
+               "fit_best": fit_rec(np.minimum(t_str, t_tile)),
                "expert_weight_bytes": 3 * base.hidden * base.inter * 2,
-               "points": [list(p) for p in pts]}
+               "points": {"columns": ["G", "N", "auto_us", "stream_us", "tile_us"],
+                          "rows": [list(p) for p in pts]}}
         print(json.dumps(rec), flush=True)
         del d
         torch.cuda.empty_cache()

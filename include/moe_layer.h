@@ -55,9 +55,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Schedules of the grouped FFN (and of the dense FFN). */
 typedef enum {
-    MOE_SCHED_AUTO = 0,    /* chosen from the shape: TILE once experts average 24 tokens
-                              (T*K >= 24*E) and block_m allows it, else RING where it
-                              applies, else STREAM; dense rows: TILE above 32 tokens */
+    MOE_SCHED_AUTO = 0,    /* TILE once experts average 24 tokens (T*K >= 24*E) and
+                              block_m allows it; below that RING where it applies,
+                              chosen per expert on the device (two regimes per expert,
+                              TEMPO page): experts whose tokens fit a ring pass (16 or 32)
+                              streamed, busier ones tiled when block_m allows it, else
+                              streamed by STREAM; else STREAM; dense rows: TILE above 32
+                              tokens */
     MOE_SCHED_STREAM = 1,  /* weight-streaming: each active expert's weights read once per
                               pass of up to 64 tokens, straight into MFMA operand registers;
                               any supported shape and dtype; for HBM-bound (decode) shapes */

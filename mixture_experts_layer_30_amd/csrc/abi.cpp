@@ -361,6 +361,11 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
   const bool ring = moe::ring_gate_up_ok(dt, dt, H, I);
   st = pick_stream(sched, ring, ring, "moe_grouped_gate_up", &use);
   if (st) return st;
+  // automatic below kTileFrom tokens per expert: experts that fit a ring pass
+  // are streamed, busier ones tiled where the plan's block allows (two regimes
+  // per expert, TEMPO page).  From kTileFrom on every expert is tiled: two
+  // launches that each leave part of the GPU idle measured slower.
+  const bool hot_tiled = sched == MOE_SCHED_AUTO && tile_ok(plan->block_m, H);
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -379,8 +384,10 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
     e = moe::launch_ring_gate_up(x, dt, w13, nullptr, cold, E, H, I, T, nb, g.gu,
                                  (uint16_t*)workspace, part, s);
     if (e == hipSuccess && T > 16 * nb)
-      e = moe::launch_stream_gate_up(x, dt, w13, hot, E, H, I, stream_tok_blocks(T), 1,
-                                     (uint16_t*)workspace, nullptr, s);
+      e = hot_tiled ? moe::launch_tile_gate_up(x, dt, w13, hot, plan->cap / plan->block_m, H, I,
+                                               (uint16_t*)workspace, s)
+                    : moe::launch_stream_gate_up(x, dt, w13, hot, E, H, I, stream_tok_blocks(T), 1,
+                                                 (uint16_t*)workspace, nullptr, s);
   }
   else
     e = moe::launch_stream_gate_up(x, dt, w13, rm, E, H, I, stream_tok_blocks(T), 1,
@@ -403,6 +410,7 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   const bool ring = moe::ring_down_ok(dt, H, I);
   st = pick_stream(sched, ring, ring, "moe_grouped_down", &use);
   if (st) return st;
+  const bool hot_tiled = sched == MOE_SCHED_AUTO && tile_ok(plan->block_m, H);
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -419,8 +427,11 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
     e = moe::launch_ring_down(w2, dt, nullptr, (const uint16_t*)workspace, cold, E, H, I, T, nb,
                               g.dn, y_pairs, dt, part, s);
     if (e == hipSuccess && T > 16 * nb)
-      e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, hot, E, H, I,
-                                  stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
+      e = hot_tiled ? moe::launch_tile_down(w2, dt, (const uint16_t*)workspace, hot,
+                                            plan->cap / plan->block_m, H, I, y_pairs, dt, 1,
+                                            nullptr, s)
+                    : moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, hot, E, H, I,
+                                              stream_tok_blocks(T), 1, y_pairs, dt, nullptr, s);
   }
   else
     e = moe::launch_stream_down(w2, dt, (const uint16_t*)workspace, rm, E, H, I,

@@ -26,10 +26,10 @@ hipError_t launch_combine(const void* y, int ydt, const float* w, const void* sh
 // sorted_ids[r], i.e. token sorted_ids[r] / K.  Dense (counts == nullptr): one
 // "expert" whose row r is token r, for r < dense_rows.
 //
-// min_rows / max_rows (grouped rows; 1 and INT32_MAX by default) restrict the
-// weight-streaming kernels to the experts with min_rows <= count <= max_rows:
-// the LDS-ring kernel takes the experts whose tokens fit its passes and the
-// register-streaming kernel the rest.
+// min_rows / max_rows (grouped rows; 1 and INT32_MAX by default) restrict every
+// grouped kernel to the experts with min_rows <= count <= max_rows: the LDS-ring
+// kernel takes the experts whose tokens fit its passes and the register-
+// streaming or the tiled kernel the rest.
 struct RowMap {
   const int32_t* counts;
   const int32_t* offsets;

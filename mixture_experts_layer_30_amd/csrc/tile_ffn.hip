@@ -59,6 +59,8 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
   } else {
     e = rm.block_expert[blk];
     if (e < 0) return;  // past the padded total
+    // experts outside min_rows..max_rows are another launch's (or have no tokens)
+    if (rm.counts[e] < rm.min_rows || rm.counts[e] > rm.max_rows) return;
     row0 = blk * BN;
     nvalid = min(BN, rm.offsets[e] + rm.counts[e] - row0);
   }
@@ -296,6 +298,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   } else {
     e = rm.block_expert[blk];
     if (e < 0) return;
+    if (rm.counts[e] < rm.min_rows || rm.counts[e] > rm.max_rows) return;
     row0 = blk * BN;
     nvalid = min(BN, rm.offsets[e] + rm.counts[e] - row0);
   }

@@ -16,12 +16,13 @@ from . import binding as B
 
 
 def default_block_m(T, K, E):
-    """Padding block: 16 (one MFMA token block) for the streaming schedules,
-    64 or 128 (the tile's token block) once experts average 24 tokens, the
-    tiled schedule's range; 128 from 96 tokens on average (measured crossover)."""
+    """Padding block: 16 (one MFMA token block) while every expert fits a pass
+    of the streaming schedules (T <= 32); else 64 or 128, the tile's token
+    block, so that the busy experts can be tiled: 128 once experts average 96
+    tokens (measured crossover)."""
     if T * K >= 96 * E:
         return 128
-    return 64 if T * K >= 24 * E else 16
+    return 64 if T > 32 or T * K >= 24 * E else 16
 
 
 class MoELayer:

@@ -369,6 +369,26 @@ def test_layer_parity_ring(shape, T, routing, block_m):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("block_m", [16, 64, 128])
+def test_layer_parity_per_expert_schedule(block_m):
+    """Automatic schedule with cold and busy experts in one batch (Zipf routing):
+    experts within a ring pass go to the ring kernel, busier ones to the tiled
+    kernel (block 64 or 128) or the register-streaming kernel (block 16); each
+    launch skips the other's experts."""
+    # experts average under 24 tokens (T*K < 24*E), the range of the per-expert choice
+    shape = LayerShape("per_expert", 256, 512, 64, 2, 128, "bf16", (300,), ("zipf",))
+    d, dev = layer_case(shape, 300, "zipf", seed=29)
+    layer = MoELayer(shape, dev, block_m=block_m)
+    out = layer.forward().clone()
+    torch.cuda.synchronize()
+    counts = layer.plan.expert_counts.cpu().numpy()
+    assert (counts > 32).any() and ((counts > 0) & (counts <= 32)).any()
+    ref, rids, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], shape.topk,
+                                    d["ws13"], d["ws2"])
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    assert rel_err(out, ref) <= TOL
+
+
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
 @pytest.mark.parametrize("T,routing", [(1, "uniform"), (3, "zipf"), (17, "uniform")])
 def test_grouped_split_parity(T, routing, fp8):
