@@ -43,6 +43,8 @@ def lib():
         vp, i64, i32, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         L.orc_route.argtypes = [vp, i64, i32, i32, vp, vp]
         L.orc_route.restype = i32
+        L.orc_route_var.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.orc_route_var.restype = i32
         L.orc_align.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp]
         L.orc_align.restype = i32
         L.orc_align_mode.argtypes = [vp, i64, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp]
@@ -61,6 +63,9 @@ def lib():
         L.orc_moe_layer_s.argtypes = [vp, i32, vp, i64, i32, i32, i32, i32, vp, vp, i32, vp, vp, i32,
                                       vp, vp, vp, vp, vp, dp, dp]
         L.orc_moe_layer_s.restype = i32
+        L.orc_moe_layer_k.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, i32, vp, vp, i32, vp, vp,
+                                      i32, vp, vp, vp, vp, vp, dp, dp]
+        L.orc_moe_layer_k.restype = i32
         L.orc_set_threads.argtypes = [i32]
         L.orc_max_threads.restype = i32
         _lib = L
@@ -123,6 +128,28 @@ def route(logits, K):
     rc = lib().orc_route(_p(l), T, E, K, _p(ids), _p(w))
     if rc:
         raise ValueError(f"orc_route: bad arguments (E={E}, K={K})")
+    return ids, w
+
+
+def _budget(k_tok, T):
+    k = np.ascontiguousarray(np.asarray(k_tok, dtype=np.int32).reshape(-1))
+    assert k.shape == (T,), "one budget per token"
+    return k
+
+
+def route_var(logits, Kmax, k_tok):
+    """Routing with a per-token budget k_t (clamped to [0, Kmax]): token t's
+    first k_t slots as route(..., K=k_t), the rest id -1 and weight 0; returns
+    (ids int32 [T,Kmax], w float64 [T,Kmax])."""
+    l, dt = _arr(logits)
+    assert dt == F32, "router logits are fp32"
+    T, E = l.shape
+    k = _budget(k_tok, T)
+    ids = np.empty((T, Kmax), np.int32)
+    w = np.empty((T, Kmax), np.float64)
+    rc = lib().orc_route_var(_p(l), T, E, Kmax, _p(k), _p(ids), _p(w))
+    if rc:
+        raise ValueError(f"orc_route_var: bad arguments (E={E}, Kmax={Kmax})")
     return ids, w
 
 
@@ -215,7 +242,7 @@ def moe_layer_fp8(x, logits, q13, s13, q2, s2, K, qs13=None, ss13=None, qs2=None
 
 
 def combine(y, w, s=None):
-    """out[t] = sum_k w[t,k] y[t*K+k] (+ s[t])."""
+    """out[t] = sum_k w[t,k] y[t*K+k] (+ s[t]); slots of weight 0 skipped."""
     w = np.ascontiguousarray(w, dtype=np.float64)
     T, K = w.shape
     y = np.ascontiguousarray(y, dtype=np.float64).reshape(T * K, -1)
@@ -224,6 +251,31 @@ def combine(y, w, s=None):
     out = np.empty((T, H), np.float64)
     lib().orc_combine(_p(y), _p(w), _p(s), T, K, H, _p(out))
     return out
+
+
+def moe_layer_var(x, logits, w13, w2, Kmax, k_tok, ws13=None, ws2=None):
+    """Whole layer with a per-token routing budget k_tok [T] (see route_var);
+    returns (out float64 [T,H], ids int32 [T,Kmax], w float64 [T,Kmax])."""
+    xa, xdt = _arr(x)
+    la, _ = _arr(logits)
+    a13, wdt = _arr(w13)
+    a2, _ = _arr(w2)
+    T, H = xa.shape
+    E = a13.shape[0]
+    I = a13.shape[1] // 2
+    assert a13.shape == (E, 2 * I, H) and a2.shape == (E, H, I) and la.shape == (T, E)
+    k = _budget(k_tok, T)
+    s13, _ = _arr(ws13)
+    s2, _ = _arr(ws2)
+    Is = 0 if s13 is None else s13.shape[0] // 2
+    out = np.empty((T, H), np.float64)
+    ids = np.empty((T, Kmax), np.int32)
+    w = np.empty((T, Kmax), np.float64)
+    rc = lib().orc_moe_layer_k(_p(xa), xdt, _p(la), _p(k), T, H, I, E, Kmax, _p(a13), _p(a2), wdt,
+                               None, None, Is, _p(s13), _p(s2), None, None, _p(ids), _p(w), _p(out))
+    if rc:
+        raise ValueError("orc_moe_layer_k: bad arguments")
+    return out, ids, w
 
 
 def moe_layer(x, logits, w13, w2, K, ws13=None, ws2=None):

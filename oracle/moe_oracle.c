@@ -28,6 +28,11 @@
  *  - combine ("local sum", finding 5): out_t = sum_k w[t,k] y[t,k] (+ shared).
  *  - DenseFA (section "定義"): the same SwiGLU with the intermediate size
  *    scaled by top-K (plus the shared width), applied to every token.
+ *  - per-token routing budget: the MoE-Prism page treats the routing top-k
+ *    as a runtime knob chosen per request, so one batch mixes budgets.  The
+ *    reading: token t routes exactly as above with K = k_t (its request's
+ *    budget, 0 <= k_t <= Kmax), its unused slots k_t..Kmax-1 hold no expert
+ *    (id -1, weight 0) and are left out of the alignment and the combine.
  */
 #include <math.h>
 #include <stdint.h>
@@ -145,6 +150,31 @@ int orc_max_threads(void)
  * equal logits go to the lower expert id (IEEE comparison, -0 == +0).
  * Returns 0, or -1 if K is outside [1, E].
  */
+int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double *w);
+
+/*
+ * Routing with a per-token budget: token t takes k_t = k_tok[t], clamped to
+ * [0, Kmax], experts, selected and renormalised as by orc_route with K = k_t;
+ * slots k_t .. Kmax-1 of its row hold id -1 and weight 0.  ids and w are
+ * [T][Kmax].  Returns 0, or -1 if Kmax is outside [1, E].
+ */
+int orc_route_var(const float *logits, int64_t T, int E, int Kmax, const int32_t *k_tok,
+                  int32_t *ids, double *w)
+{
+    if (E < 1 || Kmax < 1 || Kmax > E || T < 0)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        int k = k_tok[t] < 0 ? 0 : (k_tok[t] > Kmax ? Kmax : k_tok[t]);
+        if (k > 0)
+            orc_route(logits + t * E, 1, E, k, ids + t * Kmax, w + t * Kmax);
+        for (int j = k; j < Kmax; ++j) {
+            ids[t * Kmax + j] = -1;
+            w[t * Kmax + j] = 0.0;
+        }
+    }
+    return 0;
+}
+
 int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double *w)
 {
     if (E < 1 || K < 1 || K > E || T < 0)
@@ -196,8 +226,10 @@ int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double
  *   offsets[e] + N_e - 1; every other row below cap holds the sentinel T*K;
  *   block_expert[b] = e for the blocks of bucket e and -1 past num_padded;
  *   inv_pos[p] = the row that holds p.
- * cap must be a multiple of B.  Returns 0, -1 on bad arguments, -2 if the
- * padded total exceeds cap.
+ * A pair with a negative id is an unused slot (per-token budget): it is in no
+ * bucket and inv_pos[p] = -1.
+ * cap must be a multiple of B.  Returns 0, -1 on bad arguments (an id >= E
+ * among them), -2 if the padded total exceeds cap.
  */
 int orc_align_mode(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, int mode,
                    int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
@@ -209,9 +241,10 @@ int orc_align_mode(const int32_t *ids, int64_t T, int K, int E, int B, int64_t c
     for (int e = 0; e < E; ++e)
         counts[e] = 0;
     for (int64_t p = 0; p < TK; ++p) {
-        if (ids[p] < 0 || ids[p] >= E)
+        if (ids[p] >= E)
             return -1;
-        counts[ids[p]] += 1;
+        if (ids[p] >= 0)
+            counts[ids[p]] += 1;
     }
     int32_t maxn = 0;
     for (int e = 0; e < E; ++e)
@@ -229,6 +262,10 @@ int orc_align_mode(const int32_t *ids, int64_t T, int K, int E, int B, int64_t c
     int32_t *fill = calloc((size_t)E, sizeof(int32_t));
     for (int64_t p = 0; p < TK; ++p) {
         int e = ids[p];
+        if (e < 0) {
+            inv_pos[p] = -1;
+            continue;
+        }
         int64_t r = offsets[e] + fill[e];
         fill[e] += 1;
         sorted_ids[r] = (int32_t)p;
@@ -279,7 +316,9 @@ void orc_swiglu(const void *x, int xdt, int64_t n, int H, int I, const void *w13
 }
 
 /*
- * out[t][h] = sum_{k ascending} w[t][k] * y[t*K + k][h]  (+ s[t][h] if s).
+ * out[t][h] = sum_{k ascending} w[t][k] * y[t*K + k][h]  (+ s[t][h] if s);
+ * slots of weight 0 (unused slots of a per-token budget) are skipped, their
+ * rows of y never read.
  */
 void orc_combine(const double *y, const double *w, const double *s, int64_t T, int K, int H,
                  double *out)
@@ -288,7 +327,8 @@ void orc_combine(const double *y, const double *w, const double *s, int64_t T, i
         for (int h = 0; h < H; ++h) {
             double acc = 0.0;
             for (int k = 0; k < K; ++k)
-                acc += w[t * K + k] * y[(t * K + k) * H + h];
+                if (w[t * K + k] != 0.0)
+                    acc += w[t * K + k] * y[(t * K + k) * H + h];
             out[t * H + h] = acc + (s ? s[t * H + h] : 0.0);
         }
 }
@@ -301,10 +341,31 @@ void orc_combine(const double *y, const double *w, const double *s, int64_t T, i
  * (NULL otherwise).  ids_out/w_out (nullable) receive the routing.  Returns 0
  * or the route error.
  */
+int orc_moe_layer_k(const void *x, int xdt, const float *logits, const int32_t *k_tok, int64_t T,
+                    int H, int I, int E, int K, const void *w13, const void *w2, int wdt,
+                    const float *s13, const float *s2, int Is, const void *ws13, const void *ws2,
+                    const float *ss13, const float *ss2, int32_t *ids_out, double *w_out,
+                    double *out);
+
 int orc_moe_layer_s(const void *x, int xdt, const float *logits, int64_t T, int H, int I, int E,
                     int K, const void *w13, const void *w2, int wdt, const float *s13,
                     const float *s2, int Is, const void *ws13, const void *ws2, const float *ss13,
                     const float *ss2, int32_t *ids_out, double *w_out, double *out)
+{
+    return orc_moe_layer_k(x, xdt, logits, NULL, T, H, I, E, K, w13, w2, wdt, s13, s2, Is, ws13,
+                           ws2, ss13, ss2, ids_out, w_out, out);
+}
+
+/*
+ * orc_moe_layer_s with a per-token budget k_tok [T] (NULL: K for every
+ * token): token t is routed with orc_route_var (K = Kmax) and combines only
+ * its k_t experts; ids_out / w_out rows carry -1 / 0 in the unused slots.
+ */
+int orc_moe_layer_k(const void *x, int xdt, const float *logits, const int32_t *k_tok, int64_t T,
+                    int H, int I, int E, int K, const void *w13, const void *w2, int wdt,
+                    const float *s13, const float *s2, int Is, const void *ws13, const void *ws2,
+                    const float *ss13, const float *ss2, int32_t *ids_out, double *w_out,
+                    double *out)
 {
     if (E < 1 || K < 1 || K > E || T < 0)
         return -1;
@@ -320,12 +381,15 @@ int orc_moe_layer_s(const void *x, int xdt, const float *logits, int64_t T, int 
         double *w = malloc(sizeof(double) * (size_t)K);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < T; ++t) {
-            if (orc_route(logits + t * E, 1, E, K, ids, w) != 0) {
+            const int32_t kt = k_tok ? k_tok[t] : K;
+            if (orc_route_var(logits + t * E, 1, E, K, &kt, ids, w) != 0) {
                 rc = -1;
                 continue;
             }
             decode_row(x, xdt, t, H, xv, NULL);
             for (int k = 0; k < K; ++k) {
+                if (ids[k] < 0)
+                    continue;   /* an unused slot of the token's budget */
                 const char *e13 = (const char *)w13 + (size_t)ids[k] * 2 * I * H * esize;
                 const char *e2 = (const char *)w2 + (size_t)ids[k] * H * I * esize;
                 const float *es13 = s13 ? s13 + (size_t)ids[k] * 2 * I : NULL;

@@ -552,3 +552,82 @@ def test_fp8_quantizer_roundtrip():
     big = np.abs(wf) >= 2.0 ** -6 * s.numpy()[:, None]   # normal range of the codes
     assert (np.abs(dec - wf)[big] <= np.abs(wf)[big] * 2.0 ** -4).all()
 
+
+
+# ------------------------------------------------- per-token routing budget (MoE-Prism page)
+
+
+def test_route_var_matches_brute_force_per_budget(orc):
+    """Token t takes the top k_t experts (k_t clamped to [0, Kmax]) with the
+    softmax renormalised over those k_t; the other slots hold -1 and 0."""
+    rng = np.random.default_rng(41)
+    T, E, Kmax = 36, 10, 4
+    l = np.round(rng.normal(size=(T, E)), 1).astype(np.float32)   # ties occur
+    k_tok = np.array([(t % 6) for t in range(T)], np.int32)        # 0..5, 5 > Kmax
+    k_tok[3] = -2
+    ids, w = orc.route_var(l, Kmax, k_tok)
+    for t in range(T):
+        k = min(max(int(k_tok[t]), 0), Kmax)
+        sel = _brute_topk(l[t], k) if k > 0 else []
+        assert list(ids[t, :k]) == sel and (ids[t, k:] == -1).all(), t
+        assert (w[t, k:] == 0.0).all()
+        if k:
+            ex = [math.exp(float(l[t, e]) - float(l[t, sel[0]])) for e in sel]
+            z = math.fsum(ex)
+            assert np.allclose(w[t, :k], [v / z for v in ex], rtol=0, atol=1e-14), t
+
+
+def test_align_skips_unused_slots_hand_worked(orc):
+    # T=3, K=2, E=3, B=2; pairs p0->e1 p1 unused p2->e0 p3->e1 p4, p5 unused
+    # N = [1, 2, 0]; P = [2, 2, 0]; offsets [0, 2, 4, 4]
+    # e0 rows 0..1: 2 S;  e1 rows 2..3: 0 3;  rows 4..7 sentinel S = 6
+    ids = np.array([[1, -1], [0, 1], [-1, -1]], np.int32)
+    a = orc.align(ids, E=3, B=2, cap=8)
+    assert a["expert_counts"].tolist() == [1, 2, 0]
+    assert a["expert_offsets"].tolist() == [0, 2, 4, 4]
+    assert a["sorted_ids"].tolist() == [2, 6, 0, 3, 6, 6, 6, 6]
+    assert a["block_expert"].tolist() == [0, 1, -1, -1]
+    assert a["inv_pos"].tolist() == [2, -1, 0, 3, -1, -1]
+
+
+def test_combine_skips_zero_weight_slots(orc):
+    rng = np.random.default_rng(43)
+    T, K, H = 4, 3, 5
+    y = rng.normal(size=(T * K, H))
+    w = rng.uniform(0.1, 1.0, size=(T, K))
+    w[:, 2] = 0.0
+    w[1, 1] = 0.0
+    y[2::K] = np.nan            # rows of the unused slots are never read
+    y[1 * K + 1] = np.inf
+    out = orc.combine(y, w)
+    for t in range(T):
+        ref = sum(w[t, k] * y[t * K + k] for k in range(K) if w[t, k] != 0.0)
+        assert np.allclose(out[t], ref, rtol=1e-15, atol=0)
+
+
+def test_layer_var_matches_its_steps(orc):
+    """Layer with per-token budgets = for each token, its k_t experts' SwiGLU
+    weighted by the softmax over its k_t selected logits, plus the shared
+    expert (alone for k_t = 0)."""
+    shape = configs.LayerShape("var_k", 64, 96, 6, 3, 32, "bf16", (12,), ("uniform",))
+    d = synth.layer_inputs(shape, 12, dense=False)
+    k_tok = np.array([3, 2, 1, 0, 3, 1, 2, 0, 3, 3, 1, 2], np.int32)
+    out, ids, w = orc.moe_layer_var(d["x"], d["logits"], d["w13"], d["w2"], 3, k_tok,
+                                    d["ws13"], d["ws2"])
+    l = d["logits"].numpy()
+    for t in range(12):
+        k = int(k_tok[t])
+        sel = _brute_topk(l[t], k) if k else []
+        assert list(ids[t, :k]) == sel and (ids[t, k:] == -1).all()
+        ref = orc.swiglu(d["x"][t:t + 1], d["ws13"], d["ws2"])[0]
+        if k:
+            ex = [math.exp(float(l[t, e]) - float(l[t, sel[0]])) for e in sel]
+            z = math.fsum(ex)
+            for e, v in zip(sel, ex):
+                ref = ref + (v / z) * orc.swiglu(d["x"][t:t + 1], d["w13"][e], d["w2"][e])[0]
+        assert np.allclose(out[t], ref, rtol=1e-12, atol=1e-13), t
+    # every budget equal to K is the fixed-K layer
+    full, fids, fw = orc.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], 3, d["ws13"], d["ws2"])
+    same, sids, sw = orc.moe_layer_var(d["x"], d["logits"], d["w13"], d["w2"], 3, np.full(12, 3),
+                                       d["ws13"], d["ws2"])
+    assert (fids == sids).all() and (fw == sw).all() and (full == same).all()
