@@ -71,7 +71,7 @@ def gate_up_kernel(shape, T, block_m):
     (mirrors the choice made in the C ABI; for the record only)."""
     H, I, K, E = shape.hidden, shape.inter, shape.topk, shape.experts
     tile = block_m in (64, 128) and H % 128 == 0
-    if tile and T * K >= 24 * E:
+    if tile and T * K >= 24 * E and T > 32:
         return "tile2_ffn_kernel (MFMA tiles through an LDS ring)"
     if shape.dtype == "bf16" and H % 128 == 0 and I % 64 == 0:
         if T <= 32:
@@ -454,16 +454,112 @@ def cost_profile(names, steps):
                     "n_star": {str(g): (None if f.n_star(g) is None else round(f.n_star(g), 1))
                                for g in gs}}
 
+        t_best = np.minimum(t_str, t_tile)
+
+        def per_replicas(t):
+            """For each G: the flat (weight-streaming) level m, the first N whose
+            time exceeds 1.25 m, the marginal cost per token over the three
+            largest N (least squares) and the token count at which that cost
+            alone would reach m (the threshold if the compute regime were
+            proportional to the tokens)."""
+            out = {}
+            for g in gs:
+                sel = G == g
+                n, tt = N[sel], t[sel]
+                m = float(np.median(tt[n <= max(g, 16)]))
+                over = n[tt > 1.25 * m]
+                tail = np.argsort(n)[-3:]
+                slope = float(np.polyfit(n[tail], tt[tail], 1)[0])
+                out[str(g)] = {"flat_us": round(m, 1),
+                               "flat_ends_at_N": None if len(over) == 0 else int(over.min()),
+                               "tail_us_per_token": round(slope, 4),
+                               "n_star_marginal": round(m / slope, 1) if slope > 0 else None}
+            return out
+
         rec = {"cost_profile": name, "hidden": base.hidden, "inter": base.inter, "dtype": base.dtype,
                "unit": "us", "steps": steps,
                "fit_auto": fit_rec(t_auto),
-               "fit_best": fit_rec(np.minimum(t_str, t_tile)),
+               "fit_best": fit_rec(t_best),
+               "per_replicas_best": per_replicas(t_best),
+               "per_replicas_auto": per_replicas(t_auto),
                "expert_weight_bytes": 3 * base.hidden * base.inter * 2,
+               # tokens per replica at which an expert's flops at the bf16 MFMA peak take as
+               # long as reading its weights at the HBM peak (1 flop per weight byte per token)
+               "n_star_roofline": round(BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9), 1),
                "points": {"columns": ["G", "N", "auto_us", "stream_us", "tile_us"],
                           "rows": [list(p) for p in pts]}}
         print(json.dumps(rec), flush=True)
         del d
         torch.cuda.empty_cache()
+
+
+# routing budgets of the per-token-K workload: a decode batch of requests that
+# each chose their own top-k (MoE-Prism page), uniform over these levels
+VAR_K_LEVELS = {"qwen2": [2, 4, 6, 8], "deepseek_v3": [2, 4, 6, 8]}
+VAR_K_WORK = [("qwen2", 32, "zipf"), ("deepseek_v3", 128, "uniform"), ("deepseek_v3", 128, "zipf")]
+
+
+def run_var_k(name, T, routing, steps, warmup):
+    """Per-token routing budgets (MoE-Prism page: the routing top-k as a
+    per-request knob): one pass over the mixed batch (moe_route_var), against
+    serving every token at the largest budget ("over-serving") and against one
+    pass per budget tier (split batches).  Reports tokens/s of each."""
+    import dataclasses
+    shape = configs.CONFIGS[name]
+    levels = VAR_K_LEVELS[name]
+    d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=False)
+    k_tok = synth.budgets(T, levels, seed=0, device="cuda")
+    var = MoELayer(shape, d, k_tok=k_tok)
+    var.forward()
+    torch.cuda.synchronize()
+    ids = var.topk_ids.cpu().numpy()
+    e_var = int(len(np.unique(ids[ids >= 0])))
+    ms_var, _, _ = time_steps(var.forward, steps, warmup)
+    fl_var = time_flushed(var.forward, steps)
+    full = MoELayer(shape, d)
+    full.forward()
+    torch.cuda.synchronize()
+    e_full = int(len(np.unique(full.topk_ids.cpu().numpy())))
+    ms_full, _, _ = time_steps(full.forward, steps, warmup)
+    fl_full = time_flushed(full.forward, steps)
+    del full
+    # split batches: one layer pass per budget tier over its tokens
+    kt = k_tok.cpu()
+    tiers = []
+    for k in sorted(set(kt.tolist())):
+        idx = torch.nonzero(kt == k).flatten().to("cuda")
+        sub = dict(d, x=d["x"][idx].contiguous(), logits=d["logits"][idx].contiguous())
+        tiers.append(MoELayer(dataclasses.replace(shape, topk=k), sub))
+
+    def split_pass():
+        for lay in tiers:
+            lay.forward()
+
+    split_pass()
+    torch.cuda.synchronize()
+    ms_split, _, _ = time_steps(split_pass, steps, warmup)
+    fl_split = time_flushed(split_pass, steps)
+    H, I, Is = shape.hidden, shape.inter, shape.shared_inter
+    pairs = int(kt.sum())
+    layer_bytes = e_var * 3 * H * I * 2 + 3 * H * Is * 2 + 2 * T * H * 2 + T * shape.experts * 4
+    rec = {"metric": "MoE-layer tokens/s at 1 GPU with per-token routing budgets",
+           "value": round(T / (ms_var * 1e-3), 2), "unit": "tokens/s", "ms_per_step": round(ms_var, 4),
+           "steps": steps, "warmup": warmup, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{name} T={T} {routing}", "budgets": levels,
+                      "pairs": pairs, "pairs_at_max_k": T * shape.topk,
+                      "e_active": e_var, "e_active_at_max_k": e_full},
+           "layer": {"achieved_GBps": round(layer_bytes / (ms_var * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(layer_bytes / (ms_var * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "over_serving": {"ms_per_step": round(ms_full, 4), "tokens_per_s": round(T / (ms_full * 1e-3), 2)},
+           "split_batches": {"ms_per_step": round(ms_split, 4), "tokens_per_s": round(T / (ms_split * 1e-3), 2),
+                             "passes": len(tiers)},
+           "flushed_median_ms": {"mixed": fl_var["median_ms"], "over_serving": fl_full["median_ms"],
+                                 "split_batches": fl_split["median_ms"]},
+           "speedup_vs_over_serving": round(ms_full / ms_var, 4),
+           "speedup_vs_split_batches": round(ms_split / ms_var, 4)}
+    del d, var, tiers
+    torch.cuda.empty_cache()
+    return rec
 
 
 def run_fp8(name, T, routing, steps, warmup):
@@ -538,6 +634,8 @@ def main():
                     help="run one piece `--steps` times, untimed (for counter runs)")
     ap.add_argument("--fp8", action="store_true",
                     help="also time the decode workloads with FP8 E4M3 weights (one line each)")
+    ap.add_argument("--var-k", action="store_true",
+                    help="per-token routing budgets vs max-budget and split-batch passes (MoE-Prism)")
     ap.add_argument("--cost-profile", action="store_true",
                     help="per-expert time vs tokens and replicas, max-affine fit and n* (TEMPO page)")
     ap.add_argument("--padding-sweep", action="store_true",
@@ -555,6 +653,11 @@ def main():
         return
     if args.cost_profile:
         cost_profile([args.config] if args.config else list(COST_REPLICAS), args.steps)
+        return
+    if args.var_k:
+        for name, T, routing in VAR_K_WORK:
+            if args.config in (None, name):
+                print(json.dumps(run_var_k(name, T, routing, args.steps, args.warmup)), flush=True)
         return
     if args.only:
         shape = configs.CONFIGS[args.config or "mixtral"]

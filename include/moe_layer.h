@@ -6,6 +6,7 @@
  * The layer pass is five stream-ordered calls:
  *
  *   moe_route        router logits -> top-K expert ids and combine weights
+ *                    (moe_route_var: a routing budget per token)
  *   moe_align        (token, slot) pairs -> expert buckets padded to the tile
  *   moe_grouped_ffn  per-expert SwiGLU: gate/up GEMM + SwiGLU, then down GEMM
  *                    (also callable as its two halves, moe_grouped_gate_up and
@@ -55,8 +56,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Schedules of the grouped FFN (and of the dense FFN). */
 typedef enum {
-    MOE_SCHED_AUTO = 0,    /* TILE once experts average 24 tokens (T*K >= 24*E) and
-                              block_m allows it; below that RING where it applies,
+    MOE_SCHED_AUTO = 0,    /* TILE once experts average 24 tokens (T*K >= 24*E), T > 32
+                              and block_m allows it; below that RING where it applies,
                               chosen per expert on the device (two regimes per expert,
                               TEMPO page): experts whose tokens fit a ring pass (16 or 32)
                               streamed, busier ones tiled when block_m allows it, else
@@ -157,12 +158,26 @@ moe_status moe_route(const float *logits, int64_t T, int E, int K, int32_t *topk
                      float *topk_w, void *stream);
 
 /*
+ * Routing with a per-token budget (MoE-Prism page: the routing top-k is a
+ * runtime knob chosen per request, so one batch mixes budgets).  Token t takes
+ * k_t = k_tok[t] experts, clamped to [0, Kmax], selected and renormalised as
+ * by moe_route with K = k_t; its slots k_t .. Kmax-1 get id -1 and weight 0.
+ * The rest of the pass runs with K = Kmax: moe_align leaves the unused slots
+ * out (no row, inv_pos -1), the grouped FFN never sees them, moe_combine
+ * skips their zero weights; a token with k_t = 0 gets only the shared experts.
+ * k_tok [T] int32 device memory.  Errors: as moe_route (Kmax for K).
+ */
+moe_status moe_route_var(const float *logits, int64_t T, int E, int Kmax, const int32_t *k_tok,
+                         int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
  * Alignment with block-wise padding (Serving-tax notes, "Padding model
  * (Section 5.1)": every expert's token count rounded up to a multiple of the
  * block B, P = sum_i ceil(N_i/B)*B; the 128-row grouped-GEMM tile of the
  * TEMPO page is the prefill choice of B).  Fills every array of `plan` (see
  * moe_plan) over its whole length.  Deterministic: buckets hold their pairs in
- * ascending p.  topk_ids [T][K] int32 in [0, E).
+ * ascending p.  topk_ids [T][K] int32 in [0, E), or negative for an unused
+ * slot (moe_route_var): such a pair gets no row and inv_pos -1.
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (E > 256), MOE_ECAPACITY (cap too small).
  */
 moe_status moe_align(const int32_t *topk_ids, int64_t T, int K, int E, const moe_plan *plan,
@@ -220,7 +235,9 @@ moe_status moe_grouped_down(const void *w2, moe_dtype dt, int64_t T, int H, int 
  * Combine, the "local sum" of finding 5 (Serving-tax notes):
  *   out[t] = sum_{k = 0..K-1, in slot order} topk_w[t][k] * y_pairs[t*K + k]  (+ shared[t])
  * accumulated in fp32, rounded once to odt.  No atomics: bit-identical on
- * every run.  shared may be NULL (a layer with no shared experts).
+ * every run.  shared may be NULL (a layer with no shared experts).  Slots of
+ * weight 0 are skipped and their rows not read (the unused slots of
+ * moe_route_var have no row).
  * y_pairs [T*K][H] ydt; topk_w [T][K] fp32; shared [T][H] sdt; out [T][H] odt.
  */
 moe_status moe_combine(const void *y_pairs, moe_dtype ydt, const float *topk_w, const void *shared,

@@ -20,7 +20,7 @@ PAD_BLOCK, PAD_MAX = 0, 1
 # every function the C header declares
 EXPORTS = ["moe_last_error", "moe_status_string", "moe_align_capacity", "moe_align_capacity_ex",
            "moe_ffn_workspace_bytes", "moe_ffn_workspace_bytes_ex", "dense_ffn_workspace_bytes",
-           "moe_route", "moe_align", "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
+           "moe_route", "moe_route_var", "moe_align", "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
            "moe_combine", "dense_ffn_fa", "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8",
            "dense_ffn_fp8"]
 
@@ -64,6 +64,8 @@ def lib():
         L.dense_ffn_workspace_bytes.argtypes = [i64, i32, i32]
         L.moe_route.restype = i32
         L.moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.moe_route_var.restype = i32
+        L.moe_route_var.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
         L.moe_align.restype = i32
         L.moe_align.argtypes = [vp, i64, i32, i32, P, vp]
         L.moe_align_ex.restype = i32
@@ -156,6 +158,13 @@ class Plan:
 def moe_route(logits, K, topk_ids, topk_w, stream=None):
     T, E = logits.shape
     _check(lib().moe_route(_ptr(logits), T, E, K, _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+
+
+def moe_route_var(logits, Kmax, k_tok, topk_ids, topk_w, stream=None):
+    """Routing with a per-token budget k_tok [T] int32 (device)."""
+    T, E = logits.shape
+    _check(lib().moe_route_var(_ptr(logits), T, E, Kmax, _ptr(k_tok), _ptr(topk_ids), _ptr(topk_w),
+                               _stream(stream)))
 
 
 def moe_align(topk_ids, E, plan, stream=None):

@@ -212,7 +212,8 @@ moe_status pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m,
   } else if (req == MOE_SCHED_STREAM || req == MOE_SCHED_RING) {
     *out = req;
   } else if (req == MOE_SCHED_AUTO) {
-    *out = (tile_ok(block_m, H) && T * K >= kTileFrom * (int64_t)E) ? MOE_SCHED_TILE
+    // (T <= 32: every expert fits one streaming pass, which beats a tile)
+    *out = (tile_ok(block_m, H) && T * K >= kTileFrom * (int64_t)E && T > 32) ? MOE_SCHED_TILE
                                                                      : MOE_SCHED_STREAM;
   } else {
     return fail(MOE_EINVAL, "schedule %d", (int)req);
@@ -290,8 +291,22 @@ moe_status moe_route(const float* logits, int64_t T, int E, int K, int32_t* topk
   if (!logits || !topk_ids || !topk_w || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
       !aligned(topk_w, 4))
     return fail(MOE_EINVAL, "moe_route: NULL or misaligned pointer");
-  return hip_status(moe::launch_route(logits, T, E, K, topk_ids, topk_w, (hipStream_t)stream),
+  return hip_status(moe::launch_route(logits, T, E, K, nullptr, topk_ids, topk_w,
+                                     (hipStream_t)stream),
                     "moe_route");
+}
+
+moe_status moe_route_var(const float* logits, int64_t T, int E, int Kmax, const int32_t* k_tok,
+                         int32_t* topk_ids, float* topk_w, void* stream) {
+  moe_status st = check_route_shape(T, E, Kmax);
+  if (st) return st;
+  if (T == 0) return ok();
+  if (!logits || !k_tok || !topk_ids || !topk_w || !aligned(logits, 4) || !aligned(k_tok, 4) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(MOE_EINVAL, "moe_route_var: NULL or misaligned pointer");
+  return hip_status(moe::launch_route(logits, T, E, Kmax, k_tok, topk_ids, topk_w,
+                                     (hipStream_t)stream),
+                    "moe_route_var");
 }
 
 moe_status moe_align_ex(const int32_t* topk_ids, int64_t T, int K, int E, const moe_plan* plan,

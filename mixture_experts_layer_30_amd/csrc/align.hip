@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int64_t p = base + tid;
     int e = p < TK ? ids[p] : -1;
     const bool valid = (unsigned)e < (unsigned)E;
+    if (!valid && p < TK) inv_pos[p] = -1;   // an unused slot (per-token budget)
     uint64_t same = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {

@@ -2,6 +2,9 @@
 //
 //   out[t][h] = sum_{k in slot order} w[t][k] * y[t*K + k][h]  (+ shared[t][h])
 //
+// Slots of weight 0 are skipped without reading their rows (the unused slots
+// of per-token budgets have no row).
+//
 // The expert rows are already in pair order (row t*K + k), so each token
 // gathers its own K rows: no atomics, no scatter, bit-identical results on
 // every run.  One thread owns 8 consecutive h of one token (16-byte loads for
@@ -65,6 +68,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const typename SY::T* __re
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   for (int k = 0; k < K; ++k) {
     const float wk = w[t * K + k];
+    if (wk == 0.0f) continue;   // an unused slot of a per-token budget: its row is never written
     float v[8];
     load8f<SY>(y + (t * K + k) * H + h0, v);
 #pragma unroll

@@ -10,8 +10,9 @@ constexpr int kDtF32 = 0;
 constexpr int kDtBF16 = 1;
 constexpr int kDtFP8 = 2;   // weights only: OCP E4M3 codes with fp32 row scales
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
-                        hipStream_t s);
+// k_tok (nullable): per-token budgets, clamped to [0, K]; unused slots get -1 / 0
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, const int32_t* k_tok,
+                        int32_t* ids, float* w, hipStream_t s);
 
 // max_pad: 0 block-wise padding, 1 max padding (every expert ceil(max N / B) * B rows)
 hipError_t launch_align(const int32_t* ids, int64_t T, int K, int E, int B, int64_t cap,

@@ -13,6 +13,10 @@
 // Because the first selected logit is the maximum, the renormalised weights
 // are exp(l_j - l_0) / sum_i exp(l_i - l_0), the same numbers as renormalising
 // the full softmax.
+//
+// With a per-token budget (the routing top-k as a per-request knob, MoE-Prism
+// page) token t keeps only its first k_t selections, renormalised over them;
+// its other slots get id -1 and weight 0.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,7 +24,8 @@ namespace moe {
 
 template <int G, int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T,
-                                                    int E, int K, int32_t* __restrict__ ids,
+                                                    int E, int K, const int32_t* __restrict__ k_tok,
+                                                    int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
   constexpr int kNone = 0x7fffffff;
   const int lane = threadIdx.x & (kWave - 1);
@@ -39,6 +44,12 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     v[j] = live[j] ? logits[t * E + e] : 0.0f;
   }
 
+  // the token's budget, clamped to [0, K] (uniform over the group)
+  int kt = K;
+  if (k_tok && active) {
+    const int b = k_tok[t];
+    kt = b < 0 ? 0 : (b > K ? K : b);
+  }
   float first = 0.0f, sum = 0.0f;
   for (int kk = 0; kk < K; ++kk) {
     // lane-local best among the live entries; e grows with j, so strict '>'
@@ -66,37 +77,42 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       if (gl + G * j == be) live[j] = false;
     if (active && gl == 0) {
       if (kk == 0) first = bv;
-      const float ex = expf(bv - first);
-      sum += ex;
-      ids[t * K + kk] = be;
-      w[t * K + kk] = ex;
+      if (kk < kt) {
+        const float ex = expf(bv - first);
+        sum += ex;
+        ids[t * K + kk] = be;
+        w[t * K + kk] = ex;
+      } else {
+        ids[t * K + kk] = -1;
+        w[t * K + kk] = 0.0f;
+      }
     }
   }
-  if (active && gl == 0) {
+  if (active && gl == 0 && kt > 0) {
     const float inv = 1.0f / sum;
-    for (int kk = 0; kk < K; ++kk) w[t * K + kk] = w[t * K + kk] * inv;
+    for (int kk = 0; kk < kt; ++kk) w[t * K + kk] = w[t * K + kk] * inv;
   }
 }
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
-                        hipStream_t s) {
+hipError_t launch_route(const float* logits, int64_t T, int E, int K, const int32_t* k_tok,
+                        int32_t* ids, float* w, hipStream_t s) {
   const int threads = 256;
   auto blocks_for = [&](int G) { return (unsigned)((T + (threads / G) - 1) / (threads / G)); };
   if (E <= 8)
     hipLaunchKernelGGL((route_kernel<8, 1>), dim3(blocks_for(8)), dim3(threads), 0, s, logits, T,
-                       E, K, ids, w);
+                       E, K, k_tok, ids, w);
   else if (E <= 16)
     hipLaunchKernelGGL((route_kernel<16, 1>), dim3(blocks_for(16)), dim3(threads), 0, s, logits,
-                       T, E, K, ids, w);
+                       T, E, K, k_tok, ids, w);
   else if (E <= 32)
     hipLaunchKernelGGL((route_kernel<32, 1>), dim3(blocks_for(32)), dim3(threads), 0, s, logits,
-                       T, E, K, ids, w);
+                       T, E, K, k_tok, ids, w);
   else if (E <= 64)
     hipLaunchKernelGGL((route_kernel<64, 1>), dim3(blocks_for(64)), dim3(threads), 0, s, logits,
-                       T, E, K, ids, w);
+                       T, E, K, k_tok, ids, w);
   else
     hipLaunchKernelGGL((route_kernel<64, 4>), dim3(blocks_for(64)), dim3(threads), 0, s, logits,
-                       T, E, K, ids, w);
+                       T, E, K, k_tok, ids, w);
   return hipGetLastError();
 }
 

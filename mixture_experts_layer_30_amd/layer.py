@@ -27,12 +27,15 @@ def default_block_m(T, K, E):
 
 class MoELayer:
     def __init__(self, shape, inputs, block_m=None, sched=B.SCHED_AUTO, out_dtype=None,
-                 pad=B.PAD_BLOCK, fp8=False):
+                 pad=B.PAD_BLOCK, fp8=False, k_tok=None):
         """fp8: run the experts, shared experts and DenseFA on the FP8 E4M3 codes
         and row scales of the inputs (keys q13/s13, q2/s2, qs13/ss13, qs2/ss2,
-        qfa13/sfa13, qfa2/sfa2; see synth.add_fp8_weights)."""
+        qfa13/sfa13, qfa2/sfa2; see synth.add_fp8_weights).  k_tok: per-token
+        routing budgets [T] int32 on the device (moe_route_var; K is then the
+        largest budget allowed)."""
         x = inputs["x"]
         self.fp8 = fp8
+        self.k_tok = k_tok
         self.shape, self.inputs, self.sched = shape, inputs, sched
         self.T = T = x.shape[0]
         H, I, E, K = shape.hidden, shape.inter, shape.experts, shape.topk
@@ -63,7 +66,11 @@ class MoELayer:
 
     # the five steps, callable one by one (the benchmark times them separately)
     def route(self):
-        B.moe_route(self.inputs["logits"], self.shape.topk, self.topk_ids, self.topk_w)
+        if self.k_tok is not None:
+            B.moe_route_var(self.inputs["logits"], self.shape.topk, self.k_tok, self.topk_ids,
+                            self.topk_w)
+        else:
+            B.moe_route(self.inputs["logits"], self.shape.topk, self.topk_ids, self.topk_w)
 
     def align(self):
         if self.pad == B.PAD_BLOCK:

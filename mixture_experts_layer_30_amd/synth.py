@@ -55,6 +55,15 @@ def router_logits(T, E, routing="uniform", zipf_s=1.2, seed=0, device="cpu", nam
     return l.contiguous()
 
 
+def budgets(T, levels, seed=0, device="cpu", name="k_tok"):
+    """Per-token routing budgets [T] int32, each drawn uniformly from `levels`
+    (a batch of decode requests with their own top-k, as on the MoE-Prism
+    page; one token per request)."""
+    g = _gen(seed, name, "cpu")
+    lv = torch.tensor(list(levels), dtype=torch.int32)
+    return lv[torch.randint(0, len(lv), (T,), generator=g)].to(device)
+
+
 def tokens(T, H, dtype="bf16", seed=0, device="cpu", name="x"):
     return _normal((T, H), 1.0, _DT[dtype], seed, name, device)
 

@@ -93,6 +93,18 @@ def test_route_argument_checks(L):
     assert route(L, T=0, logits=NULL, ids=NULL, w=NULL) == B.MOE_OK  # empty batch: no-op
 
 
+def test_route_var_argument_checks(L):
+    def rv(T=4, E=8, K=2, logits=FAKE, k=FAKE, ids=FAKE, w=FAKE):
+        return st(L.moe_route_var(logits, T, E, K, k, ids, w, None))
+    assert rv(K=9) == B.MOE_EINVAL
+    assert rv(K=0) == B.MOE_EINVAL
+    assert rv(E=300, K=2) == B.MOE_EUNSUPPORTED
+    assert rv(k=NULL) == B.MOE_EINVAL
+    assert rv(k=FAKE + 2) == B.MOE_EINVAL
+    assert b"moe_route_var" in L.moe_last_error()
+    assert rv(T=0, logits=NULL, k=NULL, ids=NULL, w=NULL) == B.MOE_OK  # empty batch: no-op
+
+
 def plan(cap=4864, block_m=16, ptr=FAKE):
     return B.moe_plan(ptr, ptr, ptr, ptr, ptr, block_m, cap)
 

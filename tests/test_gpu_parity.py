@@ -101,6 +101,65 @@ def test_route_empty_batch_is_a_noop():
     assert (ids.cpu() == -7).all()
 
 
+# ------------------------------------------------- per-token routing budget (MoE-Prism page)
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 8, 2), (40, 8, 2), (300, 64, 8), (128, 256, 8), (33, 10, 10)])
+def test_route_var_parity(T, E, K):
+    logits = tie_logits(T, E, seed=T + 3 * E)
+    k_tok = synth.budgets(T, list(range(0, K + 1)) + [-1, K + 3], seed=T)
+    ids = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), -7.0, dtype=torch.float32, device=DEV)
+    B.moe_route_var(logits.to(DEV), K, k_tok.to(DEV), ids, w)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route_var(logits, K, k_tok)
+    assert (ids.cpu().numpy() == rids).all()
+    got = w.cpu().numpy()
+    assert np.abs(got - rw).max() <= 1e-5
+    assert (got[rids < 0] == 0).all()
+
+
+@pytest.mark.parametrize("block_m", [1, 16, 64, 128])
+def test_align_with_unused_slots(block_m):
+    for T, E, K, levels in [(200, 8, 2, [0, 1, 2]), (500, 64, 8, [2, 4, 8]), (3, 4, 4, [0])]:
+        logits = synth.router_logits(T, E, "zipf", seed=T)
+        ids, _ = oracle.route_var(logits, K, synth.budgets(T, levels, seed=E))
+        assert_align_equal(ids, E, block_m)
+
+
+VAR_K_CASES = [
+    # (shape, T, levels, sched, block_m): streaming (ring, register), tiled, per-expert
+    (LayerShape("vark_ring", 256, 256, 8, 4, 128, "bf16", (24,), ("uniform",)), 24, [0, 1, 2, 4],
+     B.SCHED_AUTO, 16),
+    (LayerShape("vark_tile", 256, 384, 8, 4, 0, "bf16", (300,), ("zipf",)), 300, [1, 2, 4],
+     B.SCHED_TILE, 64),
+    (LayerShape("vark_stream", 192, 256, 16, 4, 0, "bf16", (70,), ("zipf",)), 70, [1, 3, 4],
+     B.SCHED_STREAM, 16),
+    (LayerShape("vark_auto", 256, 512, 64, 8, 128, "bf16", (200,), ("zipf",)), 200, [2, 4, 6, 8],
+     B.SCHED_AUTO, None),
+    # few experts: the ring launches split their contraction, the finish kernels skip unused pairs
+    (LayerShape("vark_split", 2048, 1024, 4, 2, 0, "bf16", (5,), ("uniform",)), 5, [0, 1, 2],
+     B.SCHED_AUTO, None),
+]
+
+
+@pytest.mark.parametrize("shape,T,levels,sched,block_m", VAR_K_CASES,
+                         ids=[c[0].name for c in VAR_K_CASES])
+def test_layer_parity_var_k(shape, T, levels, sched, block_m):
+    d, dev = layer_case(shape, T, shape.routing[0], seed=31)
+    k_tok = synth.budgets(T, levels, seed=5)
+    layer = MoELayer(shape, dev, block_m=block_m, sched=sched, k_tok=k_tok.to(DEV))
+    out = layer.forward().clone()
+    torch.cuda.synchronize()
+    ref, rids, _ = oracle.moe_layer_var(d["x"], d["logits"], d["w13"], d["w2"], shape.topk, k_tok,
+                                        d["ws13"], d["ws2"])
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    assert rel_err(out, ref) <= TOL
+    out2 = layer.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
 def run_align(ids_np, E, block_m, pad=B.PAD_BLOCK):
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(DEV)
     T, K = ids_np.shape
@@ -533,12 +592,16 @@ class HostWeights:
         return self.cache[e]
 
 
-def oracle_rows(dev, shape, tokens, hw):
-    """Oracle output of the given tokens: its route, its K experts, shared, combine."""
+def oracle_rows(dev, shape, tokens, hw, k_tok=None):
+    """Oracle output of the given tokens: its route, its K experts (or its own
+    budget's, k_tok [T] on the host), shared, combine."""
     x = dev["x"][tokens].cpu()
-    ids, w = oracle.route(dev["logits"][tokens].cpu(), shape.topk)
+    if k_tok is None:
+        ids, w = oracle.route(dev["logits"][tokens].cpu(), shape.topk)
+    else:
+        ids, w = oracle.route_var(dev["logits"][tokens].cpu(), shape.topk, k_tok[tokens])
     y = np.zeros((len(tokens) * shape.topk, shape.hidden))
-    for e in np.unique(ids):
+    for e in np.unique(ids[ids >= 0]):
         sel = np.argwhere(ids == e)
         w13, w2 = hw.expert(int(e))
         ye = oracle.swiglu(x[torch.from_numpy(sel[:, 0])], w13, w2)
@@ -597,6 +660,31 @@ def test_layer_parity_full_size_sampled(name, T, routing):
         torch.cuda.synchronize()
         ref_pa = oracle.dense_ffn(dev["x"][tokens].cpu(), dev["wpa13"].cpu(), dev["wpa2"].cpu())
         assert rel_err(pa[tokens], ref_pa) <= TOL
+    del dev, layer
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,T,routing,levels", [("qwen2", 32, "zipf", [0, 2, 4, 8]),
+                                                   ("deepseek_v3", 128, "uniform", [2, 4, 6, 8])])
+def test_layer_parity_var_k_full_size_sampled(name, T, routing, levels):
+    shape = configs.CONFIGS[name]
+    print(f"\n[var-K full-size parity] {name} T={T} {routing} budgets {levels}", flush=True)
+    dev = synth.layer_inputs(shape, T, routing, seed=0, device=DEV, dense=False)
+    k_tok = synth.budgets(T, levels, seed=1)
+    layer = MoELayer(shape, dev, k_tok=k_tok.to(DEV))
+    out = layer.forward()
+    torch.cuda.synchronize()
+    rids, rw = oracle.route_var(dev["logits"].cpu(), shape.topk, k_tok)
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    assert np.abs(layer.topk_w.cpu().numpy() - rw).max() <= 1e-5
+    got = {k: v.cpu().numpy() for k, v in layer.plan.arrays().items()}
+    ra = oracle.align(rids, shape.experts, layer.block_m, layer.plan.cap)
+    for k in ra:
+        assert (got[k] == ra[k]).all(), k
+    kt = k_tok.numpy()
+    tokens = sorted({0, T - 1, int(np.argmin(kt)), int(np.argmax(kt))})
+    ref = oracle_rows(dev, shape, tokens, HostWeights(dev), k_tok=kt)
+    assert rel_err(out[tokens], ref) <= TOL
     del dev, layer
     torch.cuda.empty_cache()
 
