@@ -305,7 +305,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   const int Kdim = kGateUp ? H : I;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wave-uniform, so that the per-wavefront tile counts below stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave >> 1, wn = wave & 1;
   const int m = lane & 15, g = lane >> 4;
 
@@ -372,37 +373,80 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // One step's matrix ops on the stage in slot `slot`.  With registers to
+  // spare (TN <= 4) the fragments of both 32-deep halves are read up front, so
+  // the second half's reads are in flight while the first half's ops issue
+  // (with TN = 8 that spills registers).  `masked` skips the 16-token tiles
+  // past the block's tokens.
+  constexpr int NB2 = TN <= 4 ? 2 : 1;
+  auto step = [&](int slot, auto masked) {
+    const uint8_t* A = sm.a[slot];
+    const uint8_t* Bt = sm.b[slot];
 #pragma unroll
-  for (int s0 = 0; s0 < ST - 1; ++s0)
-    if (s0 < nk) issue(s0);
-  for (int ks = 0; ks < nk; ++ks) {
-    // stage ks must be in LDS: the ST-2 stages issued after it may stay in flight
-    if (ks + ST - 2 < nk) wait_vmcnt<(ST - 2) * kLoads>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
-    if (ks + ST - 1 < nk) issue(ks + ST - 1);
-    const uint8_t* A = sm.a[ks % ST];
-    const uint8_t* Bt = sm.b[ks % ST];
+    for (int h = 0; h < 2 / NB2; ++h) {
+      u32x4 fa[NB2][TM], fb[NB2][TN];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 fa[TM], fb[TN];
+      for (int q = 0; q < NB2; ++q) {
+        const int s2 = h * NB2 + q;
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        fa[tm] = *reinterpret_cast<const u32x4*>(
-            A + lds_off(wm * (TM * 16) + tm * 16 + m, s2 * 4 + g));
+        for (int tm = 0; tm < TM; ++tm)
+          fa[q][tm] = *reinterpret_cast<const u32x4*>(
+              A + lds_off(wm * (TM * 16) + tm * 16 + m, s2 * 4 + g));
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        fb[tn] = *reinterpret_cast<const u32x4*>(
-            Bt + lds_off(wn * (BN / 2) + tn * 16 + m, s2 * 4 + g));
+        for (int tn = 0; tn < TN; ++tn)
+          fb[q][tn] = *reinterpret_cast<const u32x4*>(
+              Bt + lds_off(wn * (BN / 2) + tn * 16 + m, s2 * 4 + g));
+      }
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        if (tn < tn_live) {
+      for (int q = 0; q < NB2; ++q)
 #pragma unroll
-          for (int tm = 0; tm < TM; ++tm) acc[tm][tn] = mfma16x16x32(fa[tm], fb[tn], acc[tm][tn]);
+        for (int tn = 0; tn < TN; ++tn)
+          if (!decltype(masked)::value || tn < tn_live) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+              acc[tm][tn] = mfma16x16x32(fa[q][tm], fb[q][tn], acc[tm][tn]);
+          }
+      if (NB2 == 2 && !decltype(masked)::value) {
+        // order of the branch-free step: the first half's reads, then the
+        // second half's reads one between each of the first ops, then the
+        // rest; at most 15 reads are ever outstanding (the counter's limit),
+        // so each op waits only for its own operands
+        constexpr int NR = TM + TN;
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);   // DS reads
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN - NR, 0);
       }
     }
-  }
+  };
+  // The k loop, in a copy per path so that the steady-state body (wait for
+  // stage ks, barrier, issue stage ks + ST - 1, the step) is one basic block
+  // and the waits inside it count only the reads an op needs.
+  auto run = [&](auto masked) {
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+      if (s0 < nk) issue(s0);
+    int ks = 0;
+    for (; ks + ST - 1 < nk; ++ks) {
+      // stage ks must be in LDS: the ST-2 stages issued after it may stay in flight
+      wait_vmcnt<(ST - 2) * kLoads>();
+      barrier_no_fence();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
+      issue(ks + ST - 1);
+      step(ks % ST, masked);
+    }
+    for (; ks < nk; ++ks) {   // the last ST - 1 steps: nothing left to issue
+      wait_vmcnt<0>();
+      barrier_no_fence();
+      step(ks % ST, masked);
+    }
+  };
+  if (NB2 == 2 && tn_live == TN)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
 
   // epilogue: lane holds rows 4g..4g+3 of each 16-row tile, for token column m of each tile
   if (kGateUp) {
