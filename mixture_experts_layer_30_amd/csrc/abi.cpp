@@ -157,6 +157,13 @@ int pick_splits(int slabs, int nch) {
   return s < 1 ? 1 : (s > most ? most : s);
 }
 
+// Whether the tiled gate/up of dense rows has enough tiles for half the
+// compute units: (I / 128) x ceil(T / block).  A narrow FFN (the shared expert
+// of DeepSeek-V3, I = 2048, at 128 tokens: 16 tiles) is faster streamed.
+bool dense_tile_fills(int64_t T, int I, int block) {
+  return (int64_t)(I / 128) * ((T + block - 1) / block) >= 128;
+}
+
 DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   DensePlan p;
   p.tok_blocks = stream_tok_blocks(T);
@@ -510,8 +517,11 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   moe_schedule use;
   st = pick_schedule(sched, T, 1, 1, 128, H, &use);
   if (st) return st;
-  if (sched == MOE_SCHED_AUTO) use = (T <= 32 || !tile_ok(128, H)) ? MOE_SCHED_STREAM : MOE_SCHED_TILE;
   const DensePlan dp = dense_plan(T, H, I_fa, dt);
+  if (sched == MOE_SCHED_AUTO)
+    use = (T <= 32 || !tile_ok(128, H) || !dense_tile_fills(T, I_fa, dp.tile_block))
+              ? MOE_SCHED_STREAM
+              : MOE_SCHED_TILE;
   if (use == MOE_SCHED_TILE) {
     uint16_t* act = (uint16_t*)workspace;
     float* part = (float*)((char*)workspace + dp.act_bytes);
@@ -546,6 +556,16 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   return hip_status(e, "dense_ffn_fa down");
 }
 
+// FP8 experts are tiled once they average kTileFrom tokens (as the bf16
+// automatic schedule does) and the shape allows; below that every expert
+// streams through the ring, the busier ones in several passes (measured on
+// MI355X: cheaper than a second tiled launch for them, whose workgroups for
+// the other experts' blocks still have to start and exit)
+bool fp8_tiled(int64_t T, int K, int E, int H, int I, int block_m) {
+  return T > 32 && T * K >= kTileFrom * (int64_t)E && moe::tile_fp8_ok(H, I, block_m) &&
+         block_m <= 128;
+}
+
 static moe_status check_fp8_weights(const void* w, const float* scale, int H, int I,
                                     const char* what) {
   if (H % 128 != 0 || I % 128 != 0)
@@ -567,15 +587,21 @@ moe_status moe_grouped_gate_up_fp8(const void* x, int64_t T, int H, int I, int E
   if (T == 0) return ok();
   if (!x || !workspace || !aligned(x, 16) || !aligned(workspace, 16))
     return fail(MOE_EINVAL, "moe_grouped_gate_up_fp8: NULL or misaligned pointer");
-  // every expert in the ring, busy ones in several passes (measured faster than
-  // passes of 64 tokens for them)
   const moe::RowMap rm = grouped_rows(plan, K);
-  const int nb = ring_tok_blocks(T, K, E);
-  const GroupedSplit g = grouped_split_for(T, K, E, H, I, moe::ring_stage_k(moe::kDtFP8, nb, H),
-                                           plan->cap, workspace_bytes);
-  float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
-  hipError_t e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T, nb, g.gu,
-                                          (uint16_t*)workspace, part, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (fp8_tiled(T, K, E, H, I, plan->block_m)) {
+    e = moe::launch_tile_gate_up_fp8(x, w13, w13_scale, rm, plan->cap / plan->block_m, H, I,
+                                     (uint16_t*)workspace, s);
+  } else {
+    const int nb = ring_tok_blocks(T, K, E);
+    const GroupedSplit g = grouped_split_for(T, K, E, H, I,
+                                             moe::ring_stage_k(moe::kDtFP8, nb, H), plan->cap,
+                                             workspace_bytes);
+    float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
+    e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T, nb, g.gu,
+                                 (uint16_t*)workspace, part, s);
+  }
   return hip_status(e, "moe_grouped_gate_up_fp8");
 }
 
@@ -590,13 +616,21 @@ moe_status moe_grouped_down_fp8(const uint8_t* w2, const float* w2_scale, int64_
   if (!workspace || !y_pairs || !aligned(workspace, 16) || !aligned(y_pairs, 16))
     return fail(MOE_EINVAL, "moe_grouped_down_fp8: NULL or misaligned pointer");
   const moe::RowMap rm = grouped_rows(plan, K);
-  const int nb = ring_tok_blocks(T, K, E);
-  const GroupedSplit g = grouped_split_for(T, K, E, H, I, moe::ring_stage_k(moe::kDtFP8, nb, I),
-                                           plan->cap, workspace_bytes);
-  float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
-  hipError_t e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, rm,
-                                       E, H, I, T, nb, g.dn, y_pairs, moe::kDtBF16, part,
-                                       (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (fp8_tiled(T, K, E, H, I, plan->block_m)) {
+    e = moe::launch_tile_down_fp8(w2, w2_scale, (const uint16_t*)workspace, rm,
+                                  plan->cap / plan->block_m, H, I, y_pairs, moe::kDtBF16, 1,
+                                  nullptr, s);
+  } else {
+    const int nb = ring_tok_blocks(T, K, E);
+    const GroupedSplit g = grouped_split_for(T, K, E, H, I,
+                                             moe::ring_stage_k(moe::kDtFP8, nb, I), plan->cap,
+                                             workspace_bytes);
+    float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
+    e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, rm, E, H, I,
+                              T, nb, g.dn, y_pairs, moe::kDtBF16, part, s);
+  }
   return hip_status(e, "moe_grouped_down_fp8");
 }
 
@@ -627,6 +661,20 @@ moe_status dense_ffn_fp8(const void* x, int64_t T, int H, int I, const uint8_t* 
   rm.min_rows = 1;
   rm.max_rows = INT32_MAX;
   const DensePlan dp = dense_plan(T, H, I, MOE_BF16);
+  hipStream_t s = (hipStream_t)stream;
+  if (T > 32 && moe::tile_fp8_ok(H, I, dp.tile_block) && dense_tile_fills(T, I, dp.tile_block)) {
+    // past one streaming pass: the tiled schedule reads each weight tile once
+    // per token block (the streaming passes would read all weights again)
+    uint16_t* act = (uint16_t*)workspace;
+    float* part = (float*)((char*)workspace + dp.act_bytes);
+    rm.block_m = dp.tile_block;
+    const int64_t nblocks = (T + rm.block_m - 1) / rm.block_m;
+    hipError_t e = moe::launch_tile_gate_up_fp8(x, w13, w13_scale, rm, nblocks, H, I, act, s);
+    if (e != hipSuccess) return hip_status(e, "dense_ffn_fp8 gate/up");
+    e = moe::launch_tile_down_fp8(w2, w2_scale, act, rm, nblocks, H, I, out, odt, dp.tile_split,
+                                  part, s);
+    return hip_status(e, "dense_ffn_fp8 down");
+  }
   // contraction splits at the FP8 stage length, within the bf16 plan's (which
   // sized the workspace's partial sums)
   const int ks_gu = moe::ring_stage_k(moe::kDtFP8, dp.tok_blocks, H);
@@ -637,7 +685,6 @@ moe_status dense_ffn_fp8(const void* x, int64_t T, int H, int I, const uint8_t* 
   split_dn = split_dn < dp.ring_split_dn ? split_dn : dp.ring_split_dn;
   uint16_t* act = (uint16_t*)workspace;
   float* part = (float*)((char*)workspace + dp.act_bytes);
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, 1, H, I, T,
                                           dp.tok_blocks, split_gu, act, part, s);
   if (e != hipSuccess) return hip_status(e, "dense_ffn_fp8 gate/up");

@@ -80,6 +80,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// 8 FP8 E4M3 codes (two dwords, code j in byte j) as 8 bf16, exactly: every
+// E4M3 value is a bf16 value (v_cvt_scalef32_pk_bf16_fp8 with scale 1; checked
+// against the format's definition for all 256 codes)
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint2 v) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
+  return r;
+}
+
 template <class S>
 __device__ __forceinline__ void store_out(typename S::T* p, float v);
 template <>

@@ -64,6 +64,17 @@ hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const 
                             int64_t nblocks, int H, int I, void* y, int ydt, int ksplit,
                             float* part, hipStream_t s);
 
+// The tiled schedule with FP8 E4M3 weights and fp32 row scales (w13_scale
+// [E][2I], w2_scale [E][H]) and bf16 tokens; needs H % 256 == 0, I % 128 == 0 and
+// block_m 64, 128 or 256 (tile_fp8_ok).  ksplit as for launch_tile_down.
+bool tile_fp8_ok(int H, int I, int block_m);
+hipError_t launch_tile_gate_up_fp8(const void* x, const void* w13, const float* w13_scale,
+                                   const RowMap& rm, int64_t nblocks, int H, int I, uint16_t* act,
+                                   hipStream_t s);
+hipError_t launch_tile_down_fp8(const void* w2, const float* w2_scale, const uint16_t* act,
+                                const RowMap& rm, int64_t nblocks, int H, int I, void* y, int ydt,
+                                int ksplit, float* part, hipStream_t s);
+
 // act[o][i] = silu(g) * u with g, u the in-order sums over z < splits of
 // part[z][r][i] and part[z][r][I + i], o = out_row[r] (r when out_row is null;
 // rows with out_row[r] < 0 are skipped).

@@ -95,18 +95,6 @@ __device__ __forceinline__ int roff(int r, int s) { return r * RB + ((s ^ (r & 1
 // per 256 bytes) cover all 64 banks.
 __device__ __forceinline__ int roff8(int r, int s) { return r * 128 + ((s ^ ((r >> 1) & 7)) << 4); }
 
-// 8 FP8 E4M3 codes (two dwords, code j in byte j) as 8 bf16, exactly: every
-// E4M3 value is a bf16 value (v_cvt_scalef32_pk_bf16_fp8 with scale 1; checked
-// against the format's definition for all 256 codes)
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint2 v) {
-  u32x4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
-  return r;
-}
-
 __device__ __forceinline__ void barrier_nf() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int N>

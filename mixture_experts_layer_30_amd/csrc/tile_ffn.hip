@@ -228,17 +228,27 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
 constexpr int kT2BM = 256;
 constexpr int kRowBytes = kBK * 2;   // 128 bytes of one row per step
 
-template <int BN, int ST>
+// AROW: bytes of a weight row per step (128 for bf16, 64 for FP8 codes)
+template <int BN, int ST, int AROW>
 struct Tile2Smem {
-  uint8_t a[ST][kT2BM * kRowBytes];
+  uint8_t a[ST][kT2BM * AROW];
   uint8_t b[ST][BN * kRowBytes];
   int tok[BN];
   int dst[BN];
 };
 
 // stages that fit the 160 KB of LDS next to the token arrays
-template <int BN>
-constexpr int tile2_stages() { return BN >= 256 ? 2 : 3; }
+template <class SW, int BN>
+constexpr int tile2_stages() {
+  return SW::kBytes == 1 ? (BN >= 256 ? 3 : 4) : (BN >= 256 ? 2 : 3);
+}
+
+// byte offset of (row, 16-byte segment) in a stage of 64-byte FP8 weight rows:
+// segments permuted by bits 2..3 of the row, so the 16 rows of a fragment read
+// cover 16 different 16-byte bank groups
+__device__ __forceinline__ int lds8_off(int row, int seg) {
+  return row * 64 + ((seg ^ ((row >> 2) & 3)) << 4);
+}
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
@@ -266,21 +276,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <class SY, int BN, bool kGateUp, int NW>
+// SW: weight storage, BF16 or FP8 E4M3 codes with fp32 row scales (wscale
+// [E][2I] for gate/up, [E][H] for down): the codes are expanded exactly to
+// bf16 as the fragments are read, and the row scales multiply the sums.
+template <class SW, class SY, int BN, bool kGateUp, int NW>
 __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
-    const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
+    const typename SW::T* __restrict__ w, const float* __restrict__ wscale,
+    const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
     uint16_t* __restrict__ act, typename SY::T* __restrict__ y, int ntiles, int nblocks,
     int ksplit, float* __restrict__ part) {
-  constexpr int ST = tile2_stages<BN>();
+  constexpr bool kF8 = SW::kBytes == 1;
+  constexpr int AROW = kF8 ? 64 : kRowBytes;               // weight row bytes per step
+  constexpr int ASEG = AROW / 16;                          // lanes per weight row in a direct load
+  constexpr int ST = tile2_stages<SW, BN>();
   constexpr int NT = NW * kWave;
   constexpr int WM = NW / 2;                              // wavefront rows
   constexpr int TM = kT2BM / WM / 16;                     // 16-row tiles per wavefront
   constexpr int TN = BN / 2 / 16;                         // 16-token tiles per wavefront
-  constexpr int AInst = kT2BM * kRowBytes / 1024 / NW;    // direct loads per wave per step
+  constexpr int AInst = kT2BM * AROW / 1024 / NW;         // direct loads per wave per step
   constexpr int BInst = BN * kRowBytes / 1024 / NW;
   constexpr int kLoads = AInst + BInst;
   static_assert(BInst >= 1 && kLoads * (ST - 1) < 64, "load counts");
-  __shared__ Tile2Smem<BN, ST> sm;
+  __shared__ Tile2Smem<BN, ST, AROW> sm;
   // XCD-aware work item: XCD b % 8 takes items [xcd * per, (xcd + 1) * per)
   const int per = (int)(gridDim.x / 8);
   const int item0 = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
@@ -323,14 +340,17 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   }
   __syncthreads();
 
-  // Direct loads: instruction i of a stage fills LDS rows 8i..8i+7; lane l
-  // fills row 8i + l/8, slot l%8, which holds global segment (l%8) ^ swz(row).
+  // Direct loads: instruction i of a stage fills 1 KB of LDS rows; for bf16
+  // weights rows 8i..8i+7, lane l filling row 8i + l/8, slot l%8, which holds
+  // global segment (l%8) ^ swz(row); for FP8 weights rows 16i..16i+15, lane l
+  // filling row 16i + l/4, slot l%4, global segment (l%4) ^ ((row >> 2) & 3).
   const int i0 = tile * (kGateUp ? kT2BM / 2 : kT2BM);
-  const uint16_t* wexp = w + (size_t)e * (kGateUp ? 2 * (size_t)I * H : (size_t)H * I);
+  const uint8_t* wexp = reinterpret_cast<const uint8_t*>(w) +
+                        (size_t)e * (kGateUp ? 2 * (size_t)I * H : (size_t)H * I) * SW::kBytes;
   const uint8_t* asrc[AInst];
 #pragma unroll
   for (int j = 0; j < AInst; ++j) {
-    const int r = 8 * (wave * AInst + j) + lane / 8;
+    const int r = (1024 / AROW) * (wave * AInst + j) + lane / ASEG;
     size_t wr;
     if (kGateUp) {
       const int q = r >> 4;                       // 16-row group: even = gate, odd = up
@@ -339,7 +359,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
     } else {
       wr = (size_t)(i0 + r);
     }
-    asrc[j] = reinterpret_cast<const uint8_t*>(wexp + wr * Kdim) + (((lane & 7) ^ swz(r)) << 4);
+    const int aslot = kF8 ? ((lane & 3) ^ ((r >> 2) & 3)) : ((lane & 7) ^ swz(r));
+    asrc[j] = wexp + wr * Kdim * SW::kBytes + (aslot << 4);
   }
   const uint8_t* bsrc[BInst];
 #pragma unroll
@@ -358,7 +379,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
     const size_t kb = (size_t)(k0 + ks) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < AInst; ++j)
-      lds_direct16(asrc[j] + kb, &sm.a[st][(wave * AInst + j) * 1024]);
+      lds_direct16(asrc[j] + (size_t)(k0 + ks) * AROW, &sm.a[st][(wave * AInst + j) * 1024]);
 #pragma unroll
     for (int j = 0; j < BInst; ++j)
       lds_direct16(bsrc[j] + kb, &sm.b[st][(wave * BInst + j) * 1024]);
@@ -389,9 +410,14 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
       for (int q = 0; q < NB2; ++q) {
         const int s2 = h * NB2 + q;
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          fa[q][tm] = *reinterpret_cast<const u32x4*>(
-              A + lds_off(wm * (TM * 16) + tm * 16 + m, s2 * 4 + g));
+        for (int tm = 0; tm < TM; ++tm) {
+          const int r = wm * (TM * 16) + tm * 16 + m;
+          if constexpr (kF8)   // 8 codes at k = 32 s2 + 8 g: half (g & 1) of segment 2 s2 + g / 2
+            fa[q][tm] = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(
+                A + lds8_off(r, 2 * s2 + (g >> 1)) + 8 * (g & 1)));
+          else
+            fa[q][tm] = *reinterpret_cast<const u32x4*>(A + lds_off(r, s2 * 4 + g));
+        }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
           fb[q][tn] = *reinterpret_cast<const u32x4*>(
@@ -456,8 +482,13 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
       for (int tn = 0; tn < TN; ++tn) {
         const int j = wn * (BN / 2) + tn * 16 + m;
         if (j < nvalid) {
-          const f32x4 gs = acc[2 * p][tn], us = acc[2 * p + 1][tn];
+          f32x4 gs = acc[2 * p][tn], us = acc[2 * p + 1][tn];
           const int i = i0 + 16 * (wm * (TM / 2) + p) + 4 * g;
+          if constexpr (kF8) {   // row scales of the lane's 4 gate and 4 up rows
+            const float* se = wscale + (size_t)e * 2 * I;
+            gs = gs * *reinterpret_cast<const f32x4*>(se + i);
+            us = us * *reinterpret_cast<const f32x4*>(se + I + i);
+          }
           uint2 v;
           v.x = pack_bf16x2(silu(gs.x) * us.x, silu(gs.y) * us.y);
           v.y = pack_bf16x2(silu(gs.z) * us.z, silu(gs.w) * us.w);
@@ -472,7 +503,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
         const int j = wn * (BN / 2) + tn * 16 + m;
         if (j < nvalid) {
           const int h = i0 + wm * (TM * 16) + tm * 16 + 4 * g;
-          const f32x4 v = acc[tm][tn];
+          f32x4 v = acc[tm][tn];
+          if constexpr (kF8) v = v * *reinterpret_cast<const f32x4*>(wscale + (size_t)e * H + h);
           if (part) {  // split contraction: fp32 slice, summed in slice order by the finish kernel
             *reinterpret_cast<f32x4*>(part + ((size_t)zk * rm.dense_rows + sm.dst[j]) * H + h) = v;
           } else {
@@ -506,26 +538,27 @@ static void dn_launch(const void* w2, const uint16_t* act, const RowMap& rm, int
 // 1-D grid of tiles x blocks items, rounded up to a multiple of the 8 XCDs
 static unsigned xcd_grid(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
 
-template <int BN>
+template <int BN, class SW = BF16>
 static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
-                       int I, uint16_t* act, hipStream_t s) {
+                       int I, uint16_t* act, hipStream_t s, const float* wscale = nullptr) {
   const int ntiles = I / (kT2BM / 2);
-  hipLaunchKernelGGL((tile2_ffn_kernel<BF16, BN, true, MOE_TILE_WAVES>),
+  hipLaunchKernelGGL((tile2_ffn_kernel<SW, BF16, BN, true, MOE_TILE_WAVES>),
                      dim3(xcd_grid(ntiles * nblocks)), dim3(MOE_TILE_WAVES * kWave), 0, s,
-                     static_cast<const uint16_t*>(w13),
+                     static_cast<const typename SW::T*>(w13), wscale,
                      static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr, ntiles,
                      (int)nblocks, 1, (float*)nullptr);
 }
 
-template <class SY, int BN>
+template <class SY, int BN, class SW = BF16>
 static void dn2_launch(const void* w2, const uint16_t* act, const RowMap& rm, int64_t nblocks,
-                       int H, int I, void* y, int ksplit, float* part, hipStream_t s) {
+                       int H, int I, void* y, int ksplit, float* part, hipStream_t s,
+                       const float* wscale = nullptr) {
   const int ntiles = H / kT2BM;
-  hipLaunchKernelGGL((tile2_ffn_kernel<SY, BN, false, MOE_TILE_WAVES>),
+  hipLaunchKernelGGL((tile2_ffn_kernel<SW, SY, BN, false, MOE_TILE_WAVES>),
                      dim3(xcd_grid((int64_t)ksplit * ntiles * nblocks)),
-                     dim3(MOE_TILE_WAVES * kWave), 0, s, static_cast<const uint16_t*>(w2), act,
-                     rm, H, I, (uint16_t*)nullptr, static_cast<typename SY::T*>(y), ntiles,
-                     (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr);
+                     dim3(MOE_TILE_WAVES * kWave), 0, s, static_cast<const typename SW::T*>(w2),
+                     wscale, act, rm, H, I, (uint16_t*)nullptr, static_cast<typename SY::T*>(y),
+                     ntiles, (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr);
 }
 
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
@@ -577,6 +610,37 @@ hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const 
     if (wdt == kDtF32) dn_by_out<F32, 128>(w2, act, rm, nblocks, H, I, y, ydt, s);
     else dn_by_out<BF16, 128>(w2, act, rm, nblocks, H, I, y, ydt, s);
   }
+  return hipGetLastError();
+}
+
+bool tile_fp8_ok(int H, int I, int block_m) {
+  return H % kT2BM == 0 && I % (kT2BM / 2) == 0 &&
+         (block_m == 64 || block_m == 128 || block_m == 256);
+}
+
+hipError_t launch_tile_gate_up_fp8(const void* x, const void* w13, const float* w13_scale,
+                                   const RowMap& rm, int64_t nblocks, int H, int I, uint16_t* act,
+                                   hipStream_t s) {
+  if (rm.block_m == 256) gu2_launch<256, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale);
+  else if (rm.block_m == 128) gu2_launch<128, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale);
+  else gu2_launch<64, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_down_fp8(const void* w2, const float* w2_scale, const uint16_t* act,
+                                const RowMap& rm, int64_t nblocks, int H, int I, void* y, int ydt,
+                                int ksplit, float* part, hipStream_t s) {
+  auto go = [&](auto bn) {
+    constexpr int BN = decltype(bn)::value;
+    if (ydt == kDtF32)
+      dn2_launch<F32, BN, FP8>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, w2_scale);
+    else
+      dn2_launch<BF16, BN, FP8>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, w2_scale);
+  };
+  if (rm.block_m == 256) go(std::integral_constant<int, 256>{});
+  else if (rm.block_m == 128) go(std::integral_constant<int, 128>{});
+  else go(std::integral_constant<int, 64>{});
+  if (ksplit > 1) return launch_finish_down(part, ksplit, rm.dense_rows, H, y, ydt, s);
   return hipGetLastError();
 }
 

@@ -729,9 +729,12 @@ def test_layer_parity_fp8(shape, T, routing):
     assert torch.equal(out, out2)
 
 
-# stage lengths: 256 k (T <= 32, contraction a multiple of 256), 128 k with one
-# block (H, I not multiples of 256) and with four blocks (T > 32)
-@pytest.mark.parametrize("T,H,I", [(1, 256, 4096), (8, 384, 640), (40, 128, 1024), (100, 256, 512)])
+# streaming at 256 k per stage (T <= 32, contraction a multiple of 256), at 128 k
+# (H, I not multiples of 256; four blocks past 32 tokens when the tile grid would
+# be small), and the FP8 tile above 32 tokens with at least 128 gate/up tiles
+# (128- and 256-token blocks, split down projection)
+@pytest.mark.parametrize("T,H,I", [(1, 256, 4096), (8, 384, 640), (40, 128, 1024), (100, 256, 512),
+                                   (300, 256, 384), (80, 256, 16384), (200, 256, 16384)])
 def test_dense_ffn_fp8_parity(T, H, I):
     x = synth.tokens(T, H, "bf16", seed=I + 3)
     w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T + 3)
@@ -742,6 +745,24 @@ def test_dense_ffn_fp8_parity(T, H, I):
     out = torch.empty(T, H, dtype=torch.float32, device=DEV)
     B.dense_ffn_fp8(x.to(DEV), q13.to(DEV), s13.to(DEV), q2.to(DEV), s2.to(DEV), ws, out)
     torch.cuda.synchronize()
+    assert rel_err(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("block_m", [64, 128])
+def test_layer_parity_fp8_tiled(block_m):
+    """FP8 weights once experts average 24+ tokens: the FP8 tile takes every
+    expert, cold and busy (codes expanded on the fragment reads, row scales on
+    the sums)."""
+    shape = LayerShape("fp8_tiled", 512, 256, 8, 2, 0, "bf16", (300,), ("zipf",))
+    d, dev = fp8_case(shape, 300, "zipf", seed=37)
+    layer = MoELayer(shape, dev, fp8=True, block_m=block_m)
+    out = layer.forward().clone()
+    torch.cuda.synchronize()
+    counts = layer.plan.expert_counts.cpu().numpy()
+    assert (counts > 64).any() and ((counts > 32) & (counts <= 64)).any()
+    ref, rids, _ = oracle.moe_layer_fp8(d["x"], d["logits"], d["q13"], d["s13"], d["q2"], d["s2"],
+                                        shape.topk)
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
     assert rel_err(out, ref) <= TOL
 
 
