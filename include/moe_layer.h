@@ -62,8 +62,10 @@ typedef enum {
                               TEMPO page): experts whose tokens fit a ring pass (16 or 32)
                               streamed, busier ones tiled when block_m allows it, else
                               streamed by STREAM; else STREAM; dense rows: TILE above 32
-                              tokens when its gate/up grid, (I/128) x ceil(T/block), has
-                              at least 128 tiles, else streamed */
+                              tokens (a gate/up grid, (I/128) x ceil(T/block), of fewer
+                              than 128 tiles, or a down grid of fewer than 256, splits
+                              its contraction in fp32 slices added in slice order), else
+                              streamed */
     MOE_SCHED_STREAM = 1,  /* weight-streaming: each active expert's weights read once per
                               pass of up to 64 tokens, straight into MFMA operand registers;
                               any supported shape and dtype; for HBM-bound (decode) shapes */
@@ -272,8 +274,8 @@ moe_status dense_ffn_fa(const void *x, moe_dtype dt, int64_t T, int H, int I_fa,
  * several passes); once experts average 24 tokens (T*K >= 24*E, T > 32) the
  * tiled schedule takes every expert when block_m is 64 or 128, H % 256 == 0
  * and I % 128 == 0.  Dense rows are streamed up to 32 tokens and tiled above
- * (same shape conditions and a gate/up grid of at least 128 tiles, as for
- * dense_ffn_fa; else streamed).
+ * (same shape conditions, and the contraction splits of dense_ffn_fa's tiled
+ * schedule; else streamed).
  * Shapes: H % 128 == 0 and I % 128 == 0.  Pointers: codes 16-byte aligned,
  * scales 4-byte aligned.  Same plan and workspace as the bf16 calls.
  *   moe_grouped_gate_up_fp8: w13 [E][2I][H] codes, w13_scale [E][2I] fp32

@@ -145,6 +145,7 @@ GroupedSplit grouped_split_for(int64_t T, int K, int E, int H, int I, int ks, in
 struct DensePlan {
   int tok_blocks, split_gu, split_dn;  // streaming schedule
   int tile_block, tile_split;          // tiled schedule: token block and down-projection split
+  int tile_split_gu;                   // and gate/up split
   bool ring_gu, ring_dn;               // LDS-ring streaming applies to the half
   int ring_split_gu, ring_split_dn;    // and the contraction split it uses
   int64_t act_bytes, part_bytes;
@@ -157,11 +158,18 @@ int pick_splits(int slabs, int nch) {
   return s < 1 ? 1 : (s > most ? most : s);
 }
 
-// Whether the tiled gate/up of dense rows has enough tiles for half the
-// compute units: (I / 128) x ceil(T / block).  A narrow FFN (the shared expert
-// of DeepSeek-V3, I = 2048, at 128 tokens: 16 tiles) is faster streamed.
-bool dense_tile_fills(int64_t T, int I, int block) {
-  return (int64_t)(I / 128) * ((T + block - 1) / block) >= 128;
+// Contraction split of a tiled launch over dense rows with `items` output
+// tiles, when there are fewer than `below`: one 512-thread workgroup per CU, so
+// aim at 256 workgroups, keeping at least 8 contraction steps of 64 per slice.
+// Measured on MI355X: a narrow FFN (the shared expert of DeepSeek-V3, I = 2048,
+// at 128 tokens: 16 gate/up tiles, split 14 ways) runs 2.3x faster split, but
+// gate/up grids of 144-224 tiles run 5-15% slower split in 2, hence below =
+// 128 there (the down projection, split below 256, was measured separately).
+int tile_splits(int64_t items, int kdim, int64_t below) {
+  if (items <= 0 || items >= below) return 1;
+  const int64_t most = kdim / 64 / 8 > 1 ? kdim / 64 / 8 : 1;
+  const int64_t want = (256 + items - 1) / items;
+  return (int)(want < most ? want : most);
 }
 
 DensePlan dense_plan(int64_t T, int H, int I, int dt) {
@@ -172,18 +180,16 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   // tiled: 256-token blocks where the 256-row bf16 tile covers both halves and more than
   // 128 rows come (each weight tile then read once per 256 tokens; measured faster than
   // 128-token blocks from 192 rows up); the down projection, H/256 tiles per block, is
-  // split when that leaves fewer than 256 workgroups
+  // split when that leaves fewer than 256 workgroups, gate/up (I/128 tiles per block)
+  // when fewer than 128
   const bool tile2 = dt == MOE_BF16 && I % 128 == 0 && H % 256 == 0;
   p.tile_block = (tile2 && T > 128) ? 256 : 128;
   p.tile_split = 1;
+  p.tile_split_gu = 1;
   if (tile2) {
-    const int64_t items = (int64_t)(H / 256) * ((T + p.tile_block - 1) / p.tile_block);
-    if (items > 0 && items < 256) {
-      // one 512-thread workgroup per CU: aim at 256, keeping >= 8 contraction steps a slice
-      const int64_t most = I / 64 / 8 > 1 ? I / 64 / 8 : 1;
-      const int64_t want = (256 + items - 1) / items;
-      p.tile_split = (int)(want < most ? want : most);
-    }
+    const int64_t nb = (T + p.tile_block - 1) / p.tile_block;
+    p.tile_split = tile_splits((int64_t)(H / 256) * nb, I, 256);
+    p.tile_split_gu = tile_splits((int64_t)(I / 128) * nb, H, 128);
   }
   p.ring_gu = moe::ring_gate_up_ok(dt, dt, H, I);
   p.ring_dn = moe::ring_down_ok(dt, H, I);
@@ -191,9 +197,10 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   p.ring_split_dn = p.ring_dn ? moe::ring_down_splits(T, H, I) : 1;
   p.act_bytes = round_up(round_up(T, 128) * (int64_t)I * 2, 256);
   // partial sums of whichever split schedule runs: the largest of them
-  const int64_t cand[5] = {p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0,
+  const int64_t cand[6] = {p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0,
                            p.split_dn > 1 ? (int64_t)p.split_dn * T * H * 4 : 0,
                            p.tile_split > 1 ? (int64_t)p.tile_split * T * H * 4 : 0,
+                           p.tile_split_gu > 1 ? (int64_t)p.tile_split_gu * T * 2 * I * 4 : 0,
                            p.ring_split_gu > 1 ? (int64_t)p.ring_split_gu * T * 2 * I * 4 : 0,
                            p.ring_split_dn > 1 ? (int64_t)p.ring_split_dn * T * H * 4 : 0};
   p.part_bytes = 0;
@@ -519,15 +526,14 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   if (st) return st;
   const DensePlan dp = dense_plan(T, H, I_fa, dt);
   if (sched == MOE_SCHED_AUTO)
-    use = (T <= 32 || !tile_ok(128, H) || !dense_tile_fills(T, I_fa, dp.tile_block))
-              ? MOE_SCHED_STREAM
-              : MOE_SCHED_TILE;
+    use = (T <= 32 || !tile_ok(128, H)) ? MOE_SCHED_STREAM : MOE_SCHED_TILE;
   if (use == MOE_SCHED_TILE) {
     uint16_t* act = (uint16_t*)workspace;
     float* part = (float*)((char*)workspace + dp.act_bytes);
     rm.block_m = dp.tile_block;
     const int64_t nblocks = (T + rm.block_m - 1) / rm.block_m;
-    hipError_t e = moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s);
+    hipError_t e = moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s,
+                                            dp.tile_split_gu, part);
     if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
     e = moe::launch_tile_down(w2, dt, act, rm, nblocks, H, I_fa, out, odt, dp.tile_split, part, s);
     return hip_status(e, "dense_ffn_fa down");
@@ -662,14 +668,15 @@ moe_status dense_ffn_fp8(const void* x, int64_t T, int H, int I, const uint8_t* 
   rm.max_rows = INT32_MAX;
   const DensePlan dp = dense_plan(T, H, I, MOE_BF16);
   hipStream_t s = (hipStream_t)stream;
-  if (T > 32 && moe::tile_fp8_ok(H, I, dp.tile_block) && dense_tile_fills(T, I, dp.tile_block)) {
+  if (T > 32 && moe::tile_fp8_ok(H, I, dp.tile_block)) {
     // past one streaming pass: the tiled schedule reads each weight tile once
     // per token block (the streaming passes would read all weights again)
     uint16_t* act = (uint16_t*)workspace;
     float* part = (float*)((char*)workspace + dp.act_bytes);
     rm.block_m = dp.tile_block;
     const int64_t nblocks = (T + rm.block_m - 1) / rm.block_m;
-    hipError_t e = moe::launch_tile_gate_up_fp8(x, w13, w13_scale, rm, nblocks, H, I, act, s);
+    hipError_t e = moe::launch_tile_gate_up_fp8(x, w13, w13_scale, rm, nblocks, H, I, act, s,
+                                                dp.tile_split_gu, part);
     if (e != hipSuccess) return hip_status(e, "dense_ffn_fp8 gate/up");
     e = moe::launch_tile_down_fp8(w2, w2_scale, act, rm, nblocks, H, I, out, odt, dp.tile_split,
                                   part, s);

@@ -56,8 +56,12 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
                               float* part, hipStream_t s);
 
 // LDS-tiled MFMA schedule: one workgroup per (block_m-row token block, 128 weight rows).
+// ksplit > 1 (dense rows, bf16, I % 128 == 0 only): the contraction in slices whose
+// fp32 gate and up sums go to part [ksplit][rows][2I], the SwiGLU applied by the
+// finish kernel after adding them in slice order.
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
-                               int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s);
+                               int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s,
+                               int ksplit = 1, float* part = nullptr);
 // ksplit > 1 (dense rows, bf16, H % 256 == 0 only) splits the contraction into
 // slices whose fp32 sums go to part [ksplit][rows][H], added in order by a finish kernel.
 hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
@@ -66,11 +70,12 @@ hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const 
 
 // The tiled schedule with FP8 E4M3 weights and fp32 row scales (w13_scale
 // [E][2I], w2_scale [E][H]) and bf16 tokens; needs H % 256 == 0, I % 128 == 0 and
-// block_m 64, 128 or 256 (tile_fp8_ok).  ksplit as for launch_tile_down.
+// block_m 64, 128 or 256 (tile_fp8_ok).  ksplit as for launch_tile_gate_up and
+// launch_tile_down.
 bool tile_fp8_ok(int H, int I, int block_m);
 hipError_t launch_tile_gate_up_fp8(const void* x, const void* w13, const float* w13_scale,
                                    const RowMap& rm, int64_t nblocks, int H, int I, uint16_t* act,
-                                   hipStream_t s);
+                                   hipStream_t s, int ksplit = 1, float* part = nullptr);
 hipError_t launch_tile_down_fp8(const void* w2, const float* w2_scale, const uint16_t* act,
                                 const RowMap& rm, int64_t nblocks, int H, int I, void* y, int ydt,
                                 int ksplit, float* part, hipStream_t s);

@@ -302,7 +302,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   const int per = (int)(gridDim.x / 8);
   const int item0 = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (item0 >= ksplit * ntiles * nblocks) return;
-  const int zk = item0 / (ntiles * nblocks);   // slice of a split contraction (dense down only)
+  const int zk = item0 / (ntiles * nblocks);   // slice of a split contraction (dense rows only)
   const int item = item0 % (ntiles * nblocks);
   const int tile = item / nblocks;
   const int blk = item % nblocks;
@@ -489,6 +489,12 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
             gs = gs * *reinterpret_cast<const f32x4*>(se + i);
             us = us * *reinterpret_cast<const f32x4*>(se + I + i);
           }
+          if (part) {  // split contraction: this slice's fp32 sums, SwiGLU in the finish kernel
+            float* pr = part + ((size_t)zk * rm.dense_rows + row0 + j) * (2 * (size_t)I);
+            *reinterpret_cast<f32x4*>(pr + i) = gs;
+            *reinterpret_cast<f32x4*>(pr + I + i) = us;
+            continue;
+          }
           uint2 v;
           v.x = pack_bf16x2(silu(gs.x) * us.x, silu(gs.y) * us.y);
           v.y = pack_bf16x2(silu(gs.z) * us.z, silu(gs.w) * us.w);
@@ -540,13 +546,15 @@ static unsigned xcd_grid(int64_t items) { return (unsigned)((items + 7) / 8 * 8)
 
 template <int BN, class SW = BF16>
 static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
-                       int I, uint16_t* act, hipStream_t s, const float* wscale = nullptr) {
+                       int I, uint16_t* act, hipStream_t s, const float* wscale = nullptr,
+                       int ksplit = 1, float* part = nullptr) {
   const int ntiles = I / (kT2BM / 2);
   hipLaunchKernelGGL((tile2_ffn_kernel<SW, BF16, BN, true, MOE_TILE_WAVES>),
-                     dim3(xcd_grid(ntiles * nblocks)), dim3(MOE_TILE_WAVES * kWave), 0, s,
+                     dim3(xcd_grid((int64_t)ksplit * ntiles * nblocks)),
+                     dim3(MOE_TILE_WAVES * kWave), 0, s,
                      static_cast<const typename SW::T*>(w13), wscale,
                      static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr, ntiles,
-                     (int)nblocks, 1, (float*)nullptr);
+                     (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr);
 }
 
 template <class SY, int BN, class SW = BF16>
@@ -562,11 +570,13 @@ static void dn2_launch(const void* w2, const uint16_t* act, const RowMap& rm, in
 }
 
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
-                               int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s) {
+                               int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s,
+                               int ksplit, float* part) {
   if (xdt == kDtBF16 && I % (kT2BM / 2) == 0) {
-    if (rm.block_m == 256) gu2_launch<256>(x, w13, rm, nblocks, H, I, act, s);
-    else if (rm.block_m == 128) gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s);
-    else gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s);
+    if (rm.block_m == 256) gu2_launch<256>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part);
+    else if (rm.block_m == 128) gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part);
+    else gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part);
+    if (ksplit > 1) return launch_finish_gate_up(part, ksplit, rm.dense_rows, I, act, s);
     return hipGetLastError();
   }
   if (rm.block_m == 64) {
@@ -620,10 +630,14 @@ bool tile_fp8_ok(int H, int I, int block_m) {
 
 hipError_t launch_tile_gate_up_fp8(const void* x, const void* w13, const float* w13_scale,
                                    const RowMap& rm, int64_t nblocks, int H, int I, uint16_t* act,
-                                   hipStream_t s) {
-  if (rm.block_m == 256) gu2_launch<256, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale);
-  else if (rm.block_m == 128) gu2_launch<128, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale);
-  else gu2_launch<64, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale);
+                                   hipStream_t s, int ksplit, float* part) {
+  if (rm.block_m == 256)
+    gu2_launch<256, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part);
+  else if (rm.block_m == 128)
+    gu2_launch<128, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part);
+  else
+    gu2_launch<64, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part);
+  if (ksplit > 1) return launch_finish_gate_up(part, ksplit, rm.dense_rows, I, act, s);
   return hipGetLastError();
 }
 

@@ -276,17 +276,21 @@ def test_dense_ffn_parity(T, H, I, dt, odt):
 
 DENSE_TILE_CASES = [
     # (T, H, I): 256-token blocks with a ragged tail and the down projection split in 7
-    # uneven slices; 128-token blocks split in 2; two full 256-token blocks
+    # uneven slices; 128-token blocks split in 2; two full 256-token blocks; two gate/up
+    # tiles split in 5 uneven slices (8 or 9 steps of 64); the DeepSeek-V3 shared expert
+    # at 128 tokens (16 gate/up tiles split in 14, 28 down tiles split in 4)
     (600, 256, 3968),
     (333, 512, 1280),
     (512, 256, 1024),
+    (70, 2816, 256),
+    (128, 7168, 2048),
 ]
 
 
 @pytest.mark.parametrize("T,H,I", DENSE_TILE_CASES)
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
 def test_dense_ffn_tile_parity(T, H, I, odt):
-    """The tiled schedule on dense rows, where few output tiles make the down
+    """The tiled schedule on dense rows, where few output tiles make either
     projection split its contraction (fp32 slices summed in slice order)."""
     x = synth.tokens(T, H, "bf16", seed=I)
     w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T)
@@ -730,11 +734,12 @@ def test_layer_parity_fp8(shape, T, routing):
 
 
 # streaming at 256 k per stage (T <= 32, contraction a multiple of 256), at 128 k
-# (H, I not multiples of 256; four blocks past 32 tokens when the tile grid would
-# be small), and the FP8 tile above 32 tokens with at least 128 gate/up tiles
-# (128- and 256-token blocks, split down projection)
+# (H, I not multiples of 256; four blocks past 32 tokens when the shape does not
+# tile), and the FP8 tile above 32 tokens (128- and 256-token blocks, split
+# down projection; split gate/up for the few tiles of a narrow FFN)
 @pytest.mark.parametrize("T,H,I", [(1, 256, 4096), (8, 384, 640), (40, 128, 1024), (100, 256, 512),
-                                   (300, 256, 384), (80, 256, 16384), (200, 256, 16384)])
+                                   (300, 256, 384), (80, 256, 16384), (200, 256, 16384),
+                                   (70, 2816, 256), (128, 7168, 2048)])
 def test_dense_ffn_fp8_parity(T, H, I):
     x = synth.tokens(T, H, "bf16", seed=I + 3)
     w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T + 3)
