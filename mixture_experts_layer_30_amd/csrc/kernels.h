@@ -62,6 +62,12 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
                                int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s,
                                int ksplit = 1, float* part = nullptr);
+// The gate/up tile of 512 weight rows x 128 tokens for bf16 experts that hold
+// several 128-token blocks: block_m 128, I % 256 == 0, H % 32 == 0 and an
+// expert's gate/up matrix below 4 GB (tile_wide_ok); hipErrorInvalidValue else.
+bool tile_wide_ok(int block_m, int H, int I);
+hipError_t launch_tile_gate_up_wide(const void* x, const void* w13, const RowMap& rm,
+                                    int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s);
 // ksplit > 1 (dense rows, bf16, H % 256 == 0 only) splits the contraction into
 // slices whose fp32 sums go to part [ksplit][rows][H], added in order by a finish kernel.
 hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,

@@ -544,6 +544,233 @@ static void dn_launch(const void* w2, const uint16_t* act, const RowMap& rm, int
 // 1-D grid of tiles x blocks items, rounded up to a multiple of the 8 XCDs
 static unsigned xcd_grid(int64_t items) { return (unsigned)((items + 7) / 8 * 8); }
 
+
+// ---------------------------------------------------------------------------
+// Wide gate/up tile for experts holding several 128-token blocks: a workgroup
+// of 8 wavefronts computes 512 weight rows (256 gate/up column pairs) x one
+// 128-token block, each wavefront 128 rows x 64 tokens (4 x 2), over steps of
+// 32 of the contraction (64-byte rows: 40 KB a stage, 3 stages in LDS).  Per
+// matrix op it moves 17% fewer bytes into LDS and reads 25% fewer out of it
+// than the 256-row tile, and the next step's fragments are read while the
+// current step's ops issue.  Measured on MI355X it is faster once experts
+// average 4 blocks (Mixtral-shaped experts at 512 tokens each: 1.10 vs 1.25
+// ms for the gate/up GEMM) and slower with fewer blocks, where 512-row tiles
+// leave too few workgroups per weight column.
+//
+// Pipeline at step t (stage t's fragments already in registers): wait for
+// this wavefront's loads of stage t+1, barrier (stage t+1 in LDS for every
+// wavefront; every wavefront has finished reading stage t's slot), load
+// stage t+3 into stage t's slot, then the ops on stage t with the fragment
+// reads of stage t+1 in flight.  Loads run two steps ahead.
+constexpr int kWBM = 512;           // weight rows per workgroup
+constexpr int kWBN = 128;           // tokens per workgroup (the alignment block)
+constexpr int kWRow = 64;           // bytes of a row per step (32 bf16)
+constexpr int kWST = 3;             // stages
+constexpr int kWWaves = 8;
+
+// byte offset of (row, 16-byte segment) in a stage of 64-byte rows: a 16-byte
+// fragment read is served 8 lanes (8 consecutive rows, one segment) at a
+// time from 128 bytes of banks, which hold two 64-byte rows; permuting the
+// segments by bits 1..2 of the row puts the 8 reads in 8 different places
+// (0 bank-conflict cycles measured; bits 2..3 gave a 2-way conflict)
+__device__ __forceinline__ int ldsw_off(int row, int seg) {
+  return row * kWRow + ((seg ^ ((row >> 1) & 3)) << 4);
+}
+
+struct WideSmem {
+  uint8_t a[kWST][kWBM * kWRow];
+  uint8_t b[kWST][kWBN * kWRow];
+  int tok[kWBN];
+};
+
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (0x7 << 4) | (N << 8));
+}
+
+__global__ __launch_bounds__(kWWaves * kWave, 1) void wide_gate_up_kernel(
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
+    uint16_t* __restrict__ act, int ntiles, int nblocks) {
+  constexpr int TM = 8, TN = 4;                          // 16-row / 16-token tiles per wavefront
+  constexpr int AInst = kWBM * kWRow / 1024 / kWWaves;   // direct loads per wavefront per stage
+  constexpr int BInst = kWBN * kWRow / 1024 / kWWaves;
+  constexpr int kLoads = AInst + BInst;
+  __shared__ WideSmem sm;
+  const int per = (int)(gridDim.x / 8);
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= ntiles * nblocks) return;
+  const int tile = item / nblocks;
+  const int blk = item % nblocks;
+  const bool dense = rm.counts == nullptr;
+  int e, row0, nvalid;
+  if (dense) {
+    e = 0;
+    row0 = blk * kWBN;
+    nvalid = min(kWBN, (int)(rm.dense_rows - row0));
+  } else {
+    e = rm.block_expert[blk];
+    if (e < 0) return;
+    if (rm.counts[e] < rm.min_rows || rm.counts[e] > rm.max_rows) return;
+    row0 = blk * kWBN;
+    nvalid = min(kWBN, rm.offsets[e] + rm.counts[e] - row0);
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m = lane & 15, g = lane >> 4;
+
+  for (int j = tid; j < kWBN; j += kWWaves * kWave) {
+    const int row = row0 + (j < nvalid ? j : 0);   // rows past the bucket reuse its first row
+    sm.tok[j] = dense ? row : (nvalid > 0 ? rm.sorted_ids[row] / rm.K : 0);
+  }
+  __syncthreads();
+
+  // Direct loads: instruction n of a stage fills LDS rows 16n..16n+15 (1 KB),
+  // lane l filling row 16n + l/4, slot l%4 with the row's global segment
+  // (l%4) ^ ((row >> 1) & 3).  Weight instruction n is 16-row group n of the
+  // tile: even groups are gate rows, odd groups the up rows of the same 16
+  // columns.  Weight addresses are a wave-uniform row offset per instruction
+  // plus one 32-bit lane offset (an expert's matrix is below 4 GB).
+  const int i0 = tile * (kWBM / 2);
+  const uint8_t* wexp = reinterpret_cast<const uint8_t*>(w) + (size_t)e * 2 * (size_t)I * H * 2;
+  const int lrow = lane >> 2;
+  const int lseg = (lane & 3) ^ ((lrow >> 1) & 3);
+  const uint32_t alane = (uint32_t)lrow * (uint32_t)H * 2u + (uint32_t)(lseg << 4);
+  uint32_t arow[AInst];
+#pragma unroll
+  for (int j = 0; j < AInst; ++j) {
+    const int q = wave * AInst + j;
+    const int i = i0 + 16 * (q >> 1);
+    arow[j] = (uint32_t)((q & 1) ? I + i : i) * (uint32_t)H * 2u;
+  }
+  const uint8_t* bsrc[BInst];
+#pragma unroll
+  for (int j = 0; j < BInst; ++j) {
+    const int r = 16 * (wave * BInst + j) + lrow;
+    bsrc[j] = reinterpret_cast<const uint8_t*>(xs + (size_t)sm.tok[r] * H) + (lseg << 4);
+  }
+  const int nk = H / 32;
+  auto issue = [&](int ks) {
+    const int st = ks % kWST;
+    const uint32_t kb = (uint32_t)ks * kWRow;
+#pragma unroll
+    for (int j = 0; j < AInst; ++j)
+      lds_direct16(wexp + (arow[j] + kb + alane), &sm.a[st][(wave * AInst + j) * 1024]);
+#pragma unroll
+    for (int j = 0; j < BInst; ++j)
+      lds_direct16(bsrc[j] + kb, &sm.b[st][(wave * BInst + j) * 1024]);
+  };
+
+  // this wavefront's 16-token tiles that hold at least one token
+  const int tn_live = min(TN, max(0, (nvalid - wn * (kWBN / 2) + 15) / 16));
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragments of a stage: lane (m, g) reads k-group g of row 16 tm + m; the
+  // masked path skips the 16-token tiles past the block's tokens
+  auto read = [&](int slot, u32x4 (&fa)[TM], u32x4 (&fb)[TN], auto masked) {
+    const uint8_t* A = sm.a[slot];
+    const uint8_t* Bt = sm.b[slot];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      fa[tm] = *reinterpret_cast<const u32x4*>(A + ldsw_off(wm * 128 + tm * 16 + m, g));
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      if (!decltype(masked)::value || tn < tn_live)
+        fb[tn] = *reinterpret_cast<const u32x4*>(Bt + ldsw_off(wn * (kWBN / 2) + tn * 16 + m, g));
+  };
+  auto ops = [&](const u32x4 (&fa)[TM], const u32x4 (&fb)[TN], auto masked) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      if (!decltype(masked)::value || tn < tn_live) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) acc[tm][tn] = mfma16x16x32(fa[tm], fb[tn], acc[tm][tn]);
+      }
+  };
+  // step t on fragments (ca, cb), reading stage t+1's into (na, nb); the
+  // steady form (t + 3 < nk) has no conditions, so it is one basic block
+  auto body = [&](int t, u32x4 (&ca)[TM], u32x4 (&cb)[TN], u32x4 (&na)[TM], u32x4 (&nb)[TN],
+                  auto steady, auto masked) {
+    if constexpr (decltype(steady)::value) {
+      wait_vmcnt<kLoads>();
+      wait_lgkmcnt<0>();
+      barrier_no_fence();
+      issue(t + 3);
+      read((t + 1) % kWST, na, nb, masked);   // completes while the ops issue
+      ops(ca, cb, masked);
+    } else {
+      if (t + 2 < nk) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
+      wait_lgkmcnt<0>();
+      barrier_no_fence();
+      if (t + 3 < nk) issue(t + 3);
+      if (t + 1 < nk) read((t + 1) % kWST, na, nb, masked);
+      ops(ca, cb, masked);
+    }
+  };
+  auto run = [&](auto masked) {
+    u32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+#pragma unroll
+    for (int s0 = 0; s0 < kWST; ++s0)
+      if (s0 < nk) issue(s0);
+    // stage 0 landed (the later stages may stay in flight)
+    if (nk >= 3) wait_vmcnt<2 * kLoads>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    read(0, fa0, fb0, masked);
+    int t = 0;
+    for (; t + 4 < nk; t += 2) {
+      body(t, fa0, fb0, fa1, fb1, std::true_type{}, masked);
+      body(t + 1, fa1, fb1, fa0, fb0, std::true_type{}, masked);
+    }
+    for (; t < nk; t += 2) {
+      body(t, fa0, fb0, fa1, fb1, std::false_type{}, masked);
+      if (t + 1 < nk) body(t + 1, fa1, fb1, fa0, fb0, std::false_type{}, masked);
+    }
+  };
+  if (tn_live == TN)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
+
+  // epilogue: lane holds rows 4g..4g+3 of each 16-row tile, for token column m
+  // of each tile; tile pair (2p, 2p+1) is the gate and up of 16 columns
+#pragma unroll
+  for (int p = 0; p < TM / 2; ++p)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+      const int j = wn * (kWBN / 2) + tn * 16 + m;
+      if (j < nvalid) {
+        const f32x4 gs = acc[2 * p][tn], us = acc[2 * p + 1][tn];
+        const int i = i0 + 16 * (wm * (TM / 2) + p) + 4 * g;
+        uint2 v;
+        v.x = pack_bf16x2(silu(gs.x) * us.x, silu(gs.y) * us.y);
+        v.y = pack_bf16x2(silu(gs.z) * us.z, silu(gs.w) * us.w);
+        *reinterpret_cast<uint2*>(act + (size_t)(row0 + j) * I + i) = v;
+      }
+    }
+}
+
+bool tile_wide_ok(int block_m, int H, int I) {
+  return block_m == kWBN && I % (kWBM / 2) == 0 && H % 32 == 0 && H >= 32 &&
+         (int64_t)2 * I * H * 2 < ((int64_t)1 << 32);
+}
+
+hipError_t launch_tile_gate_up_wide(const void* x, const void* w13, const RowMap& rm,
+                                    int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s) {
+  if (!tile_wide_ok(rm.block_m, H, I)) return hipErrorInvalidValue;
+  const int ntiles = I / (kWBM / 2);
+  hipLaunchKernelGGL(wide_gate_up_kernel, dim3(xcd_grid((int64_t)ntiles * nblocks)),
+                     dim3(kWWaves * kWave), 0, s, static_cast<const uint16_t*>(w13),
+                     static_cast<const uint16_t*>(x), rm, H, I, act, ntiles, (int)nblocks);
+  return hipGetLastError();
+}
+
 template <int BN, class SW = BF16>
 static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
                        int I, uint16_t* act, hipStream_t s, const float* wscale = nullptr,

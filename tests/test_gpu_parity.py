@@ -382,6 +382,9 @@ TILE_SHAPES = [
     # tokens), ragged last pairs and single blocks
     (LayerShape("tile2_pairs", 512, 384, 8, 2, 256, "bf16", (900,), ("uniform",)), 900, "uniform", 128),
     (LayerShape("tile2_pairs_zipf", 256, 256, 8, 2, 0, "bf16", (1000,), ("zipf",)), 1000, "zipf", 128),
+    # experts averaging >= 512 tokens: the 512-row gate/up tile (two column tiles), ragged blocks
+    (LayerShape("tile_wide", 256, 512, 4, 2, 0, "bf16", (1100,), ("zipf",)), 1100, "zipf", 128),
+    (LayerShape("tile_wide_u", 512, 256, 4, 1, 256, "bf16", (2100,), ("uniform",)), 2100, "uniform", 128),
 ]
 
 
@@ -621,6 +624,7 @@ FULL_CASES = [
     ("mixtral", 1, "uniform"),     # two experts: the down projection splits its contraction
     ("mixtral", 32, "uniform"),
     ("mixtral", 1024, "uniform"),
+    ("mixtral", 2048, "uniform"),  # 512 tokens per expert: the 512-row gate/up tile
     ("qwen2", 1, "zipf"),
     ("qwen2", 32, "zipf"),
     ("qwen2", 256, "zipf"),
