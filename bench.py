@@ -72,6 +72,9 @@ def gate_up_kernel(shape, T, block_m):
     H, I, K, E = shape.hidden, shape.inter, shape.topk, shape.experts
     tile = block_m in (64, 128) and H % 128 == 0
     if tile and T * K >= 24 * E and T > 32:
+        if (shape.dtype == "bf16" and block_m == 128 and T * K >= 512 * E and I % 256 == 0
+                and H % 32 == 0):
+            return "wide_gate_up_kernel (512-row MFMA tiles through an LDS ring)"
         return "tile2_ffn_kernel (MFMA tiles through an LDS ring)"
     if shape.dtype == "bf16" and H % 128 == 0 and I % 64 == 0:
         if T <= 32:
