@@ -102,7 +102,7 @@ hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H
 // elements by persistent workgroups (one per CU).  *_ok tells whether a shape
 // qualifies; *_splits is the contraction split it uses for `rows` dense rows at
 // ks elements per stage (part holds [splits][rows][2I] resp. [splits][rows][H]
-// fp32); grouped rows never split.
+// fp32).
 bool ring_gate_up_ok(int xdt, int wdt, int H, int I);
 bool ring_down_ok(int wdt, int H, int I);
 int ring_gate_up_splits(int64_t rows, int H, int I, int ks = 128);
