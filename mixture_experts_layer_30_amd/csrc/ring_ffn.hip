@@ -495,7 +495,11 @@ int num_cus() {
 // Contraction slices for dense rows: the count minimising the stages on the
 // critical path (rounds of G slab slices x stages per slice) plus the fp32 partial
 // sums' round trip, in units of one stage of all G workgroups (256-byte weight
-// rows per stage).
+// rows per stage).  The round trip is weighted 3x its bytes: scattered fp32
+// stores and a separate finish launch move them far slower than the weight
+// stream (measured on MI355X at 32 dense rows: Mixtral's DenseFA, 448 gate/up
+// slabs, ran 150 us split in 4 and 136 us unsplit, as the weighted model picks;
+// DeepSeek-V3's, 288 slabs, stays split in 4: 179 us against 196 unsplit).
 int ring_splits(int nslabs, int nks, int64_t rows, int outdim, int G) {
   int best = 1;
   double best_t = 1e30;
@@ -503,7 +507,7 @@ int ring_splits(int nslabs, int nks, int64_t rows, int outdim, int G) {
   for (int ks = 1; ks <= 16 && ks * 4 <= nks; ++ks) {
     const int64_t items = (int64_t)nslabs * ks;
     double t = (double)((items + G - 1) / G) * ((nks + ks - 1) / ks);
-    if (ks > 1) t += 2.0 * ks * rows * outdim * 4 / stage_bytes;
+    if (ks > 1) t += 3.0 * 2.0 * ks * rows * outdim * 4 / stage_bytes;
     if (t < best_t - 1e-9) {
       best_t = t;
       best = ks;
@@ -637,7 +641,7 @@ int ring_grouped_splits(int64_t pairs, int64_t experts, int H, int I, bool gate_
   if (slabs < 256 || s == 1) return s;
   const double t1 = (double)((slabs + 255) / 256) * nks;
   const double ts = (double)((slabs * s + 255) / 256) * ((nks + s - 1) / s) +
-                    2.0 * s * pairs * outdim * 4 / ((double)kRRows * 256 * 256);
+                    3.0 * 2.0 * s * pairs * outdim * 4 / ((double)kRRows * 256 * 256);
   return ts < 0.75 * t1 ? s : 1;
 }
 

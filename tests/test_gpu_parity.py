@@ -378,8 +378,8 @@ TILE_SHAPES = [
     # the 256-row tile on both halves, ragged last block
     (LayerShape("tile2_both", 512, 512, 8, 2, 256, "bf16", (333,), ("zipf",)), 333, "zipf", 128),
     (LayerShape("tile2_both_b64", 256, 256, 8, 2, 0, "bf16", (190,), ("uniform",)), 190, "uniform", 64),
-    # 256-token workgroups over pairs of 128-row blocks of one expert (experts average >= 192
-    # tokens), ragged last pairs and single blocks
+    # experts holding several 128-row blocks (averages of 225 and 250 tokens), ragged last
+    # blocks
     (LayerShape("tile2_pairs", 512, 384, 8, 2, 256, "bf16", (900,), ("uniform",)), 900, "uniform", 128),
     (LayerShape("tile2_pairs_zipf", 256, 256, 8, 2, 0, "bf16", (1000,), ("zipf",)), 1000, "zipf", 128),
     # experts averaging >= 512 tokens: the 512-row gate/up tile (two column tiles), ragged blocks
