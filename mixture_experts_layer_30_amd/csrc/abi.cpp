@@ -89,11 +89,15 @@ int stream_tok_blocks(int64_t max_rows) {
 // Token blocks per pass of the LDS-ring schedule, whose LDS holds the pass's
 // token rows next to the weights (more blocks, fewer stages in flight): the
 // expected load of an expert, T*K/E, with a margin.  An expert above 16 times
-// that takes several passes.
-int ring_tok_blocks(int64_t T, int K, int E) {
+// that takes several passes.  With whole_pass (bf16 weights) a pass takes every
+// token up to 32, so no expert is left to a second launch (measured on MI355X:
+// Qwen2 at T=32 with Zipf routing, expected load 4 tokens per expert, 0.508 ->
+// 0.461 ms); FP8 weights, whose busy experts stay in the ring launch for more
+// passes, keep the margin rule there (0.308 ms against 0.342 with one pass).
+int ring_tok_blocks(int64_t T, int K, int E, bool whole_pass = true) {
   const int64_t lam = (T * K + E - 1) / E;
   int64_t want = 2 * lam + 8;
-  if (want > T) want = T;
+  if (want > T || (whole_pass && T <= 32)) want = T;
   // four blocks would leave room for only three stages (measured slower than
   // handing the busier experts to the register-streaming kernel)
   return stream_tok_blocks(want < 32 ? want : 32);
@@ -109,9 +113,9 @@ struct GroupedSplit {
   int64_t part_bytes;
 };
 
-GroupedSplit grouped_split(int64_t T, int K, int E, int H, int I, int ks) {
+GroupedSplit grouped_split(int64_t T, int K, int E, int H, int I, int ks, bool whole_pass = true) {
   GroupedSplit g{1, 1, 0};
-  const int nb = ring_tok_blocks(T, K, E);
+  const int nb = ring_tok_blocks(T, K, E, whole_pass);
   if (T <= 0 || T > 16 * nb || H % 128 || I % 128) return g;
   const int64_t pairs = T * K;
   const int64_t experts = pairs < E ? pairs : E;
@@ -127,12 +131,14 @@ int64_t grouped_part_offset(int64_t cap, int I) { return round_up(cap * (int64_t
 // The split a grouped call uses: the plan's (at the weights' stage length ks,
 // at most the bf16 plan's, which sized the workspace), or none when the
 // caller's workspace has no room for the partial sums.
+// (A split needs every expert within one pass; the pass of whole_pass = false
+// is never longer, so the bf16 sizing of the workspace covers it.)
 GroupedSplit grouped_split_for(int64_t T, int K, int E, int H, int I, int ks, int64_t cap,
-                               int64_t workspace_bytes) {
-  GroupedSplit g = grouped_split(T, K, E, H, I, 128);
+                               int64_t workspace_bytes, bool whole_pass = true) {
+  GroupedSplit g = grouped_split(T, K, E, H, I, 128, whole_pass);
   if (workspace_bytes < grouped_part_offset(cap, I) + g.part_bytes) return GroupedSplit{1, 1, 0};
   if (ks != 128) {
-    const GroupedSplit f = grouped_split(T, K, E, H, I, ks);
+    const GroupedSplit f = grouped_split(T, K, E, H, I, ks, whole_pass);
     g.gu = f.gu < g.gu ? f.gu : g.gu;
     g.dn = f.dn < g.dn ? f.dn : g.dn;
   }
@@ -611,10 +617,10 @@ moe_status moe_grouped_gate_up_fp8(const void* x, int64_t T, int H, int I, int E
     e = moe::launch_tile_gate_up_fp8(x, w13, w13_scale, rm, plan->cap / plan->block_m, H, I,
                                      (uint16_t*)workspace, s);
   } else {
-    const int nb = ring_tok_blocks(T, K, E);
+    const int nb = ring_tok_blocks(T, K, E, false);
     const GroupedSplit g = grouped_split_for(T, K, E, H, I,
                                              moe::ring_stage_k(moe::kDtFP8, nb, H), plan->cap,
-                                             workspace_bytes);
+                                             workspace_bytes, false);
     float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
     e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T, nb, g.gu,
                                  (uint16_t*)workspace, part, s);
@@ -640,10 +646,10 @@ moe_status moe_grouped_down_fp8(const uint8_t* w2, const float* w2_scale, int64_
                                   plan->cap / plan->block_m, H, I, y_pairs, moe::kDtBF16, 1,
                                   nullptr, s);
   } else {
-    const int nb = ring_tok_blocks(T, K, E);
+    const int nb = ring_tok_blocks(T, K, E, false);
     const GroupedSplit g = grouped_split_for(T, K, E, H, I,
                                              moe::ring_stage_k(moe::kDtFP8, nb, I), plan->cap,
-                                             workspace_bytes);
+                                             workspace_bytes, false);
     float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
     e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, rm, E, H, I,
                               T, nb, g.dn, y_pairs, moe::kDtBF16, part, s);
