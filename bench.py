@@ -216,16 +216,8 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
     alg = algorithmic(shape, T, e_active)
 
     def step(a=None, b=None, stream=None):
-        layer.route()
-        layer.align()
-        if a is not None:
-            a.record(stream)
-        layer.gate_up()
-        if b is not None:
-            b.record(stream)
-        layer.down()
-        layer.shared()
-        layer.combine()
+        # the layer pass, events around its gate/up launch on the current stream
+        layer.forward((a, b) if a is not None else None)
 
     ms, wall_ms, gu_ms = time_steps(step, steps, warmup, mid=True)
     fa_ms, _, _ = time_steps(layer.dense_fa, steps, warmup)
@@ -585,16 +577,8 @@ def run_fp8(name, T, routing, steps, warmup):
     torch.cuda.synchronize()
 
     def step(a=None, b=None, stream=None):
-        layer.route()
-        layer.align()
-        if a is not None:
-            a.record(stream)
-        layer.gate_up()
-        if b is not None:
-            b.record(stream)
-        layer.down()
-        layer.shared()
-        layer.combine()
+        # the layer pass, events around its gate/up launch on the current stream
+        layer.forward((a, b) if a is not None else None)
 
     ms, _, gu_ms = time_steps(step, steps, warmup, mid=True)
     fa_ms, _, _ = time_steps(layer.dense_fa, steps, warmup)

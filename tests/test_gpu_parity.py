@@ -584,6 +584,32 @@ def test_layer_on_a_side_stream():
     assert rel_err(out, ref) <= TOL
 
 
+def test_layer_shared_experts_on_the_side_stream():
+    """forward() runs the shared experts on a second stream joined before the
+    combine: repeated passes (each forking after the previous combine) equal
+    the five calls made one after another on one stream, bit for bit, also
+    when the caller's stream is not the default one."""
+    shape = SMALL_SHAPES[1][0]
+    d, dev = layer_case(shape, 70, "zipf", seed=9)
+    layer = MoELayer(shape, dev)
+    layer.route(); layer.align(); layer.gate_up(); layer.down(); layer.shared(); layer.combine()
+    torch.cuda.synchronize()
+    seq = layer.out.clone()
+    layer.out.zero_()
+    layer.shared_out.zero_()
+    outs = [layer.forward().clone() for _ in range(3)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            outs.append(layer.forward().clone())
+    s.synchronize()
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, seq)
+    ref, _, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], shape.topk, d["ws13"], d["ws2"])
+    assert rel_err(seq, ref) <= TOL
+
+
 # ---------------------------------------------------------------- full-size layers, sampled tokens
 
 
