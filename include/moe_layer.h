@@ -59,9 +59,12 @@ typedef enum {
     MOE_SCHED_AUTO = 0,    /* TILE once experts average 24 tokens (T*K >= 24*E), T > 32
                               and block_m allows it; below that RING where it applies,
                               chosen per expert on the device (two regimes per expert,
-                              TEMPO page): experts whose tokens fit a ring pass (16 or 32)
-                              streamed, busier ones tiled when block_m allows it, else
-                              streamed by STREAM; else STREAM; dense rows: TILE above 32
+                              TEMPO page): experts whose tokens fit a ring pass (every
+                              token up to T = 32; 16 or 32 beyond) streamed, busier ones
+                              tiled when block_m allows it, else streamed by STREAM; else
+                              STREAM; the bf16 gate/up tile is 512 weight rows wide once
+                              experts average 512 tokens (T*K >= 512*E, block_m 128,
+                              I % 256 == 0); dense rows: TILE above 32
                               tokens (a gate/up grid, (I/128) x ceil(T/block), of fewer
                               than 128 tiles, or a down grid of fewer than 256, splits
                               its contraction in fp32 slices added in slice order), else
@@ -69,8 +72,9 @@ typedef enum {
     MOE_SCHED_STREAM = 1,  /* weight-streaming: each active expert's weights read once per
                               pass of up to 64 tokens, straight into MFMA operand registers;
                               any supported shape and dtype; for HBM-bound (decode) shapes */
-    MOE_SCHED_TILE = 2,    /* MFMA tiles of block_m tokens x 128 weight rows staged through
-                              LDS; for MFMA-bound (prefill) shapes; needs block_m 64 or 128 */
+    MOE_SCHED_TILE = 2,    /* MFMA tiles of block_m tokens x 128 to 512 weight rows
+                              staged through an LDS ring by direct loads; for MFMA-bound
+                              (prefill) shapes; needs block_m 64 or 128 */
     MOE_SCHED_RING = 3     /* weight-streaming through an LDS ring filled by whole-line
                               direct loads, one persistent workgroup per CU; needs bf16,
                               H % 128 == 0 and I % 64 == 0 (gate/up), I % 128 == 0 (down) */

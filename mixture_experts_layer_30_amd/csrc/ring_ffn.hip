@@ -481,14 +481,17 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
 
 namespace {
 
+// compute units of the device current at the first call (a static initialised
+// once, so concurrent first calls from several host threads do not race)
 int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
+  static const int n = [] {
+    int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    return cus;
+  }();
   return n;
 }
 
