@@ -73,7 +73,8 @@ typedef enum {
                               pass of up to 64 tokens, straight into MFMA operand registers;
                               any supported shape and dtype; for HBM-bound (decode) shapes */
     MOE_SCHED_TILE = 2,    /* MFMA tiles of block_m tokens x 128 to 512 weight rows
-                              staged through an LDS ring by direct loads; for MFMA-bound
+                              staged through LDS (a ring of direct loads for bf16 and FP8
+                              weights, registers for fp32); for MFMA-bound
                               (prefill) shapes; needs block_m 64 or 128 */
     MOE_SCHED_RING = 3     /* weight-streaming through an LDS ring filled by whole-line
                               direct loads, one persistent workgroup per CU; needs bf16,
