@@ -657,6 +657,8 @@ FULL_CASES = [
     ("qwen2", 2048, "zipf"),
     ("deepseek_v3", 128, "uniform"),
     ("deepseek_v3", 128, "zipf"),
+    ("mixtral", 4096, "uniform"),     # 1024 tokens per expert: wide gate/up tile, 8 blocks each
+    ("deepseek_v3", 4096, "zipf"),    # 32 768 pairs over 256 experts, skewed, tiled at block 128
 ]
 
 
