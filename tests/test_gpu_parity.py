@@ -610,6 +610,37 @@ def test_layer_shared_experts_on_the_side_stream():
     assert rel_err(seq, ref) <= TOL
 
 
+def test_layer_pass_captured_in_a_graph():
+    """The pass allocates nothing and issues no memset, so it can be captured
+    in a HIP graph (the shared experts' side stream included): several
+    replays, with eager work and synchronisations between them, each equal
+    the eager pass bit for bit."""
+    shape = SMALL_SHAPES[1][0]
+    d, dev = layer_case(shape, 70, "zipf", seed=13)
+    layer = MoELayer(shape, dev)
+    ref = layer.forward().clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward()
+    torch.cuda.synchronize()
+    for i in range(4):
+        layer.out.zero_()
+        layer.shared_out.fill_(float(i))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, ref), f"replay {i}"
+        eager = layer.forward().clone()      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref)
+
+
 # ---------------------------------------------------------------- full-size layers, sampled tokens
 
 
