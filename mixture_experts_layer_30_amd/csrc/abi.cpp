@@ -579,6 +579,13 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   return hip_status(e, "dense_ffn_fa down");
 }
 
+// FP8 ring passes of one token block leave experts with more than 16 tokens
+// to several passes, each streaming the expert's weights again; past 64 tokens
+// those experts go to a second ring launch of two-block passes instead
+// (measured on MI355X: DeepSeek-V3 at T=128 with Zipf routing 0.842 -> 0.783
+// ms; at 32-64 tokens the second launch cost as much as it saved, or more).
+bool fp8_hot_pass(int64_t T, int nb) { return nb == 1 && T > 64; }
+
 // FP8 experts are tiled once they average kTileFrom tokens (as the bf16
 // automatic schedule does) and the shape allows; below that every expert
 // streams through the ring, the busier ones in several passes (measured on
@@ -622,8 +629,19 @@ moe_status moe_grouped_gate_up_fp8(const void* x, int64_t T, int H, int I, int E
                                              moe::ring_stage_k(moe::kDtFP8, nb, H), plan->cap,
                                              workspace_bytes, false);
     float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
-    e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T, nb, g.gu,
-                                 (uint16_t*)workspace, part, s);
+    if (fp8_hot_pass(T, nb)) {
+      moe::RowMap cold = rm, hot = rm;
+      cold.max_rows = 16;
+      hot.min_rows = 17;
+      e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, cold, E, H, I, T, 1, 1,
+                                   (uint16_t*)workspace, part, s);
+      if (e == hipSuccess)
+        e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, hot, E, H, I, T, 2, 1,
+                                     (uint16_t*)workspace, part, s);
+    } else {
+      e = moe::launch_ring_gate_up(x, moe::kDtFP8, w13, w13_scale, rm, E, H, I, T, nb, g.gu,
+                                   (uint16_t*)workspace, part, s);
+    }
   }
   return hip_status(e, "moe_grouped_gate_up_fp8");
 }
@@ -651,8 +669,19 @@ moe_status moe_grouped_down_fp8(const uint8_t* w2, const float* w2_scale, int64_
                                              moe::ring_stage_k(moe::kDtFP8, nb, I), plan->cap,
                                              workspace_bytes, false);
     float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
-    e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, rm, E, H, I,
-                              T, nb, g.dn, y_pairs, moe::kDtBF16, part, s);
+    if (fp8_hot_pass(T, nb)) {
+      moe::RowMap cold = rm, hot = rm;
+      cold.max_rows = 16;
+      hot.min_rows = 17;
+      e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, cold, E, H,
+                                I, T, 1, 1, y_pairs, moe::kDtBF16, part, s);
+      if (e == hipSuccess)
+        e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, hot, E,
+                                  H, I, T, 2, 1, y_pairs, moe::kDtBF16, part, s);
+    } else {
+      e = moe::launch_ring_down(w2, moe::kDtFP8, w2_scale, (const uint16_t*)workspace, rm, E, H,
+                                I, T, nb, g.dn, y_pairs, moe::kDtBF16, part, s);
+    }
   }
   return hip_status(e, "moe_grouped_down_fp8");
 }

@@ -775,6 +775,10 @@ FP8_SHAPES = [
     (LayerShape("fp8_items", 128, 512, 64, 6, 0, "bf16", (50,), ("uniform",)), 50, "uniform"),
     # busy experts in several passes at 128 k per stage (H, I not multiples of 256)
     (LayerShape("fp8_hot128", 384, 384, 8, 2, 0, "bf16", (120,), ("zipf",)), 120, "zipf"),
+    # one-block passes past 64 tokens: experts above 16 tokens in a second ring launch of
+    # two-block passes (256 k and 128 k per stage)
+    (LayerShape("fp8_hot_pass", 256, 256, 64, 2, 128, "bf16", (100,), ("zipf",)), 100, "zipf"),
+    (LayerShape("fp8_hot_pass128", 384, 384, 64, 2, 0, "bf16", (90,), ("zipf",)), 90, "zipf"),
 ]
 
 
