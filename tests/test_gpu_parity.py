@@ -221,6 +221,35 @@ def test_align_max_padding_adversarial():
     assert_align_equal(np.tile(np.arange(16, dtype=np.int32), (37, 1)), 16, 32, pad=B.PAD_MAX)
 
 
+def test_empty_batch_every_entry_point():
+    """T = 0 is a successful no-op for every compute entry point (zero-size
+    tensors may hand the library NULL pointers)."""
+    H, I, E, K = 128, 128, 8, 2
+    x = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=1, device=DEV, experts=E)
+    plan = B.Plan(0, K, E, 16, DEV)
+    ids = torch.empty(0, K, dtype=torch.int32, device=DEV)
+    tw = torch.empty(0, K, dtype=torch.float32, device=DEV)
+    B.moe_align(ids, E, plan)
+    ws = torch.empty(1 << 12, dtype=torch.uint8, device=DEV)
+    y = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    for sched in (B.SCHED_AUTO, B.SCHED_STREAM, B.SCHED_TILE, B.SCHED_RING):
+        B.moe_grouped_gate_up(x, w13, K, plan, ws, sched)
+        B.moe_grouped_down(w2, 0, K, plan, ws, y, sched)
+    B.moe_combine(y, tw, out)
+    dw13, dw2 = synth.swiglu_weights(I, H, "bf16", seed=2, device=DEV)
+    B.dense_ffn_fa(x, dw13, dw2, ws, out)
+    q13, s13 = synth.quantize_fp8_rows(w13)
+    q2, s2 = synth.quantize_fp8_rows(w2)
+    B.moe_grouped_gate_up_fp8(x, q13, s13, K, plan, ws)
+    B.moe_grouped_down_fp8(q2, s2, 0, K, plan, ws, y)
+    dq13, ds13 = synth.quantize_fp8_rows(dw13)
+    dq2, ds2 = synth.quantize_fp8_rows(dw2)
+    B.dense_ffn_fp8(x, dq13, ds13, dq2, ds2, ws, out)
+    torch.cuda.synchronize()
+
+
 def test_align_empty_batch():
     cap, got = run_align(np.zeros((0, 2), np.int32), 8, 16)
     assert cap == 0
