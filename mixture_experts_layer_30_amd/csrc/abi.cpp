@@ -164,18 +164,35 @@ int pick_splits(int slabs, int nch) {
   return s < 1 ? 1 : (s > most ? most : s);
 }
 
-// Contraction split of a tiled launch over dense rows with `items` output
-// tiles, when there are fewer than `below`: one 512-thread workgroup per CU, so
-// aim at 256 workgroups, keeping at least 8 contraction steps of 64 per slice.
-// Measured on MI355X: a narrow FFN (the shared expert of DeepSeek-V3, I = 2048,
-// at 128 tokens: 16 gate/up tiles, split 14 ways) runs 2.3x faster split, but
-// gate/up grids of 144-224 tiles run 5-15% slower split in 2, hence below =
-// 128 there (the down projection, split below 256, was measured separately).
-int tile_splits(int64_t items, int kdim, int64_t below) {
-  if (items <= 0 || items >= below) return 1;
-  const int64_t most = kdim / 64 / 8 > 1 ? kdim / 64 / 8 : 1;
-  const int64_t want = (256 + items - 1) / items;
-  return (int)(want < most ? want : most);
+// Contraction split of a tiled launch over dense rows: `tiles` output tiles per
+// token block, `nb` blocks, contraction kdim, T tokens.  The 512-thread
+// workgroups run one per CU, so the grid goes in rounds of 256; split s gives
+// each workgroup 1/s of a tile's contraction (at least 8 steps of 64) and adds
+// fp32 partial sums (s x T x rows, written, then read by the finish kernel).
+// In units of one unsplit tile's time the s in 1..most minimising
+//   rounds(s) * (1/s + 3*64/kdim) + [s > 1] * 4*s*T/kdim * tiles/256
+// is taken: the first term counts the rounds with the pipeline fill of each
+// (three steps), the second prices the partials against the weight bytes the
+// full chip streams in one round.  Measured on MI355X: a narrow FFN (the
+// shared expert of DeepSeek-V3, I = 2048, at 128 tokens: 16 gate/up tiles)
+// runs 2.3x faster split 14 ways, while a split that spills a few workgroups
+// into a second round (144 gate/up tiles split in 2) is 5-15% slower.
+int tile_splits(int64_t tiles, int64_t nb, int kdim, int64_t T) {
+  const int64_t items = tiles * nb;
+  if (items <= 0 || kdim <= 0) return 1;
+  const int most = kdim / 64 / 8 > 1 ? kdim / 64 / 8 : 1;
+  int best = 1;
+  double best_cost = 0.0;
+  for (int s = 1; s <= most; ++s) {
+    const double rounds = (double)((items * s + 255) / 256);
+    double c = rounds * (1.0 / s + 192.0 / kdim);
+    if (s > 1) c += 4.0 * s * (double)T / kdim * (double)tiles / 256.0;
+    if (s == 1 || c < best_cost) {
+      best = s;
+      best_cost = c;
+    }
+  }
+  return best;
 }
 
 DensePlan dense_plan(int64_t T, int H, int I, int dt) {
@@ -185,17 +202,16 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   p.split_dn = pick_splits(H / 64, I / 64);
   // tiled: 256-token blocks where the 256-row bf16 tile covers both halves and more than
   // 128 rows come (each weight tile then read once per 256 tokens; measured faster than
-  // 128-token blocks from 192 rows up); the down projection, H/256 tiles per block, is
-  // split when that leaves fewer than 256 workgroups, gate/up (I/128 tiles per block)
-  // when fewer than 128
+  // 128-token blocks from 192 rows up); the contraction splits of the down projection
+  // (H/256 tiles per block) and of gate/up (I/128 tiles per block) by the rounds model above
   const bool tile2 = dt == MOE_BF16 && I % 128 == 0 && H % 256 == 0;
   p.tile_block = (tile2 && T > 128) ? 256 : 128;
   p.tile_split = 1;
   p.tile_split_gu = 1;
   if (tile2) {
     const int64_t nb = (T + p.tile_block - 1) / p.tile_block;
-    p.tile_split = tile_splits((int64_t)(H / 256) * nb, I, 256);
-    p.tile_split_gu = tile_splits((int64_t)(I / 128) * nb, H, 128);
+    p.tile_split = tile_splits(H / 256, nb, I, T);
+    p.tile_split_gu = tile_splits(I / 128, nb, H, T);
   }
   p.ring_gu = moe::ring_gate_up_ok(dt, dt, H, I);
   p.ring_dn = moe::ring_down_ok(dt, H, I);
