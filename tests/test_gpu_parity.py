@@ -307,12 +307,15 @@ DENSE_TILE_CASES = [
     # (T, H, I): 256-token blocks with a ragged tail and the down projection split in 7
     # uneven slices; 128-token blocks split in 2; two full 256-token blocks; two gate/up
     # tiles split in 5 uneven slices (8 or 9 steps of 64); the DeepSeek-V3 shared expert
-    # at 128 tokens (16 gate/up tiles split in 14, 28 down tiles split in 4)
+    # at 128 tokens (16 gate/up tiles split in 14, 28 down tiles split in 4); 144 gate/up
+    # tiles split in 3 (432 workgroups, where 2 would spill into a second round) with 8 down
+    # tiles split in 32
     (600, 256, 3968),
     (333, 512, 1280),
     (512, 256, 1024),
     (70, 2816, 256),
     (128, 7168, 2048),
+    (40, 2048, 18432),
 ]
 
 
