@@ -9,19 +9,24 @@
 // in padding rows), the expert of every B-row block and the inverse map.
 //
 // One workgroup of 1024 threads does it all; T*K is at most a few tens of
-// thousands of pairs, so the pass is a few microseconds:
-//  1. histogram of the expert ids in LDS (atomics only on counts, so the
-//     result does not depend on their order);
+// thousands of pairs, so the pass is a few microseconds.  Wavefront w owns the
+// w-th of up to 16 contiguous chunks of the pairs (a multiple of 64 each, at
+// least 256), whose ids it loads 8 steps of 64 at a time:
+//  1. per-wavefront histograms of the expert ids in LDS (atomics only on
+//     counts, so the result does not depend on their order), summed per expert;
 //  2. one wavefront scans the padded counts (E <= 256, four per lane; for max
-//     padding after a max-reduction of the counts);
-//  3. padding rows get the sentinel and every block its expert, each row
-//     finding its bucket by binary search over the LDS offsets;
-//  4. a stable scatter in rounds of 1024 consecutive pairs: inside a
-//     wavefront, lanes holding the same expert are found with 8 ballots (one
-//     per bit of the id), a lane's rank is the popcount of the matching lower
-//     lanes, and the per-wavefront counts in LDS order the wavefronts; a
-//     running fill per expert carries the order across rounds.  The result is
-//     the ascending-p order, independent of scheduling.
+//     padding after a max-reduction of the counts), and each expert's count
+//     is turned into per-wavefront starting rows (the rows of the expert's
+//     pairs in earlier chunks come first);
+//  3. every block gets its expert (binary search over the LDS offsets) and
+//     each expert's padding rows, and the rows past the padded total, the
+//     sentinel;
+//  4. a stable scatter, each wavefront walking its own chunk 64 pairs at a
+//     time with no workgroup barrier: lanes holding the same expert are found
+//     with 8 ballots (one per bit of the id), a lane's rank is the popcount of
+//     the matching lower lanes, and the group's first lane advances the
+//     wavefront's starting row for that expert.  The result is the
+//     ascending-p order, independent of scheduling.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,6 +35,8 @@ namespace moe {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kMaxExperts = 256;
+constexpr int kBatch = 8;   // 64-pair steps whose ids a wavefront loads at once
+constexpr int kMinChunk = 256;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t TK, int E, int B, int64_t cap, int max_pad,
@@ -37,24 +44,40 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     int32_t* __restrict__ block_expert, int32_t* __restrict__ inv_pos) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_fill[kMaxExperts];
-  __shared__ int s_wcnt[kAlignWaves][kMaxExperts];
+  __shared__ int s_wrow[kAlignWaves][kMaxExperts];   // per-wavefront counts, then starting rows
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
 
-  for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
-    s_cnt[e] = 0;
-    s_fill[e] = 0;
-  }
-  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&s_wcnt[0][0])[i] = 0;
+  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&s_wrow[0][0])[i] = 0;
   __syncthreads();
 
-  // 1. histogram
-  for (int64_t p = tid; p < TK; p += kAlignThreads) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+  // this wavefront's chunk [c0, c1) of the pairs: at least kMinChunk, so
+  // that small batches use few wavefronts (nw) and the loops over them stay short
+  const int64_t chunk =
+      max((int64_t)kMinChunk, ((TK + kAlignWaves - 1) / kAlignWaves + kWave - 1) / kWave * kWave);
+  const int nw = (int)((TK + chunk - 1) / chunk);
+  const int64_t c0 = min(TK, (int64_t)wave * chunk);
+  const int64_t c1 = min(TK, c0 + chunk);
+
+  // 1. histograms (kBatch loads in flight per lane)
+  for (int64_t b0 = c0; b0 < c1; b0 += kBatch * kWave) {
+    int ev[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t p = b0 + j * kWave + lane;
+      ev[j] = p < c1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if ((unsigned)ev[j] < (unsigned)E) atomicAdd(&s_wrow[wave][ev[j]], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
+    int n = 0;
+    for (int w = 0; w < nw; ++w) n += s_wrow[w][e];
+    s_cnt[e] = n;
   }
   __syncthreads();
 
@@ -100,7 +123,15 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 
   for (int e = tid; e <= E; e += kAlignThreads) {
     offsets[e] = s_off[e];
-    if (e < E) counts[e] = s_cnt[e];
+    if (e < E) {
+      counts[e] = s_cnt[e];
+      int row = s_off[e];
+      for (int w = 0; w < nw; ++w) {
+        const int n = s_wrow[w][e];
+        s_wrow[w][e] = row;
+        row += n;
+      }
+    }
   }
 
   // bucket of row r: the largest e with s_off[e] <= r (so that empty buckets,
@@ -120,45 +151,48 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int64_t r = b * B;
     block_expert[b] = r < num_padded ? bucket_of((int)r) : -1;
   }
+  // sentinel rows: each expert's padding, then everything past num_padded
   const int sentinel = (int)TK;
-  for (int64_t r = tid; r < cap; r += kAlignThreads) {
-    if (r >= num_padded) {
-      sorted_ids[r] = sentinel;
-    } else {
-      const int e = bucket_of((int)r);
-      if (r - s_off[e] >= s_cnt[e]) sorted_ids[r] = sentinel;
-    }
+  for (int e = wave; e < E; e += kAlignWaves) {   // one wavefront per expert
+    const int r1 = s_off[e + 1];
+    for (int r = s_off[e] + s_cnt[e] + lane; r < r1; r += kWave) sorted_ids[r] = sentinel;
   }
+  for (int64_t r = num_padded + tid; r < cap; r += kAlignThreads) sorted_ids[r] = sentinel;
 
-  // 4. stable scatter
+  __syncthreads();   // every wavefront's starting rows are in LDS
+
+  // 4. stable scatter of this wavefront's chunk
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int64_t base = 0; base < TK; base += kAlignThreads) {
-    const int64_t p = base + tid;
-    int e = p < TK ? ids[p] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    if (!valid && p < TK) inv_pos[p] = -1;   // an unused slot (per-token budget)
-    uint64_t same = __ballot(valid);
+  for (int64_t b0 = c0; b0 < c1; b0 += kBatch * kWave) {
+    int ev[kBatch];
 #pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool b = (e >> bit) & 1;
-      const uint64_t bal = __ballot(b);
-      same &= b ? bal : ~bal;
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t p = b0 + j * kWave + lane;
+      ev[j] = p < c1 ? ids[p] : -1;
     }
-    const int rank = __popcll(same & lower);
-    if (valid && rank == 0) s_wcnt[wave][e] = __popcll(same);
-    __syncthreads();
-    if (valid) {
-      int pos = s_off[e] + s_fill[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][e];
-      sorted_ids[pos] = (int)p;
-      inv_pos[p] = pos;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int64_t p = b0 + j * kWave + lane;
+      const int e = ev[j];
+      const bool valid = (unsigned)e < (unsigned)E;
+      if (!valid && p < c1) inv_pos[p] = -1;   // an unused slot (per-token budget)
+      uint64_t same = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool b = (e >> bit) & 1;
+        const uint64_t bal = __ballot(b);
+        same &= b ? bal : ~bal;
+      }
+      const int rank = __popcll(same & lower);
+      if (valid) {
+        // every lane reads the row before the group's first lane advances it
+        // (one wavefront's LDS accesses complete in program order)
+        const int pos = s_wrow[wave][e] + rank;
+        sorted_ids[pos] = (int)p;
+        inv_pos[p] = pos;
+      }
+      if (valid && rank == 0) s_wrow[wave][e] += __popcll(same);
     }
-    __syncthreads();
-    if (valid && rank == 0) {
-      atomicAdd(&s_fill[e], s_wcnt[wave][e]);
-      s_wcnt[wave][e] = 0;
-    }
-    __syncthreads();
   }
 }
 

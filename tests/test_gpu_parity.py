@@ -201,9 +201,13 @@ def test_align_adversarial(block_m):
     assert_align_equal(np.tile(np.arange(16, dtype=np.int32), (37, 1)), 16, block_m)
     # single token
     assert_align_equal(np.array([[3, 1]], np.int32), 4, block_m)
-    # many rounds of the scatter: 32768 pairs
+    # 32768 pairs: 16 wavefront chunks of 2048, each walked in batches of 8 x 64
     ids, _ = oracle.route(synth.router_logits(4096, 64, "zipf", seed=1), 8)
     assert_align_equal(ids, 64, block_m)
+    # 4097 pairs: 13 chunks of 320 and a ragged last one, every expert in every chunk,
+    # and all of 5000 pairs on one expert (its rows follow the chunks in order)
+    assert_align_equal((np.arange(4097) % 5).astype(np.int32).reshape(4097, 1), 5, block_m)
+    assert_align_equal(np.zeros((2500, 2), np.int32), 8, block_m)
 
 
 @pytest.mark.parametrize("T,E,K,routing", ROUTE_CASES)
