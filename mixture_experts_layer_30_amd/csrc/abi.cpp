@@ -88,15 +88,20 @@ int stream_tok_blocks(int64_t max_rows) {
 
 // Token blocks per pass of the LDS-ring schedule, whose LDS holds the pass's
 // token rows next to the weights (more blocks, fewer stages in flight): the
-// expected load of an expert, T*K/E, with a margin.  An expert above 16 times
-// that takes several passes.  With whole_pass (bf16 weights) a pass takes every
-// token up to 32, so no expert is left to a second launch (measured on MI355X:
-// Qwen2 at T=32 with Zipf routing, expected load 4 tokens per expert, 0.508 ->
-// 0.461 ms); FP8 weights, whose busy experts stay in the ring launch for more
-// passes, keep the margin rule there (0.308 ms against 0.342 with one pass).
+// expected load of an expert, lam = T*K/E, with a margin.  An expert above 16
+// times that takes several passes.  With whole_pass (bf16 weights) a pass
+// takes every token up to 32, so no expert is left to a second launch
+// (measured on MI355X: Qwen2 at T=32 with Zipf routing, expected load 4 tokens
+// per expert, 0.508 -> 0.461 ms); bf16 uses 2*lam + 8 above that.  FP8
+// weights, whose busy experts stay in the ring launch for more passes, take
+// lam + 8: their 256-element stages hold 512-byte token rows, so a second
+// token block costs a whole stage (3 in flight instead of 4), which a rare
+// second pass costs less than (Mixtral at T=32, 8 tokens per expert: one
+// block, 0.281 -> 0.249 ms per FP8 pass; Qwen2 at T=64 Zipf 0.421 -> 0.397 ms;
+// one pass for every token measured 0.342 against 0.308 ms for Qwen2 at T=32).
 int ring_tok_blocks(int64_t T, int K, int E, bool whole_pass = true) {
   const int64_t lam = (T * K + E - 1) / E;
-  int64_t want = 2 * lam + 8;
+  int64_t want = whole_pass ? 2 * lam + 8 : lam + 8;
   if (want > T || (whole_pass && T <= 32)) want = T;
   // four blocks would leave room for only three stages (measured slower than
   // handing the busier experts to the register-streaming kernel)
