@@ -11,12 +11,12 @@
 // One workgroup of 1024 threads does it all; T*K is at most a few tens of
 // thousands of pairs, so the pass is a few microseconds.  Wavefront w owns the
 // w-th of up to 16 contiguous chunks of the pairs (a multiple of 64 each, at
-// least 256), whose ids it loads 8 steps of 64 at a time:
+// least 256), whose ids it loads 4 steps of 64 at a time:
 //  1. per-wavefront histograms of the expert ids in LDS (atomics only on
-//     counts, so the result does not depend on their order), summed per expert;
-//  2. one wavefront scans the padded counts (E <= 256, four per lane; for max
-//     padding after a max-reduction of the counts), and each expert's count
-//     is turned into per-wavefront starting rows (the rows of the expert's
+//     counts, so the result does not depend on their order);
+//  2. one wavefront sums them per expert and scans the padded counts (E <=
+//     256, four per lane; for max padding after a max-reduction of the
+//     counts), and each expert's count is turned into per-wavefront starting rows (the rows of the expert's
 //     pairs in earlier chunks come first);
 //  3. every block gets its expert (binary search over the LDS offsets) and
 //     each expert's padding rows, and the rows past the padded total, the
@@ -35,7 +35,7 @@ namespace moe {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kMaxExperts = 256;
-constexpr int kBatch = 8;   // 64-pair steps whose ids a wavefront loads at once
+constexpr int kBatch = 4;   // 64-pair steps whose ids a wavefront loads at once
 constexpr int kMinChunk = 256;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
@@ -55,42 +55,48 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 
   // this wavefront's chunk [c0, c1) of the pairs: at least kMinChunk, so
   // that small batches use few wavefronts (nw) and the loops over them stay short
-  const int64_t chunk =
-      max((int64_t)kMinChunk, ((TK + kAlignWaves - 1) / kAlignWaves + kWave - 1) / kWave * kWave);
-  const int nw = (int)((TK + chunk - 1) / chunk);
+  // (T*K < 2^31, so 32-bit unsigned arithmetic holds these)
+  const uint32_t tk = (uint32_t)TK;
+  const uint32_t chunk = max((uint32_t)kMinChunk, ((tk + kAlignWaves - 1) / kAlignWaves + kWave - 1) / kWave * kWave);
+  const int nw = (int)((tk + chunk - 1) / chunk);
   const int64_t c0 = min(TK, (int64_t)wave * chunk);
-  const int64_t c1 = min(TK, c0 + chunk);
+  const int64_t c1 = min(TK, c0 + (int64_t)chunk);
 
-  // 1. histograms (kBatch loads in flight per lane)
+  // 1. histograms (up to kBatch loads in flight per lane; the steps past the
+  // chunk's end, a wavefront-uniform condition, are skipped)
   for (int64_t b0 = c0; b0 < c1; b0 += kBatch * kWave) {
     int ev[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int64_t p = b0 + j * kWave + lane;
-      ev[j] = p < c1 ? ids[p] : -1;
+      ev[j] = (b0 + j * kWave < c1 && p < c1) ? ids[p] : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j)
+    for (int j = 0; j < kBatch; ++j) {
+      if (b0 + j * kWave >= c1) break;
       if ((unsigned)ev[j] < (unsigned)E) atomicAdd(&s_wrow[wave][ev[j]], 1);
-  }
-  __syncthreads();
-  for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
-    int n = 0;
-    for (int w = 0; w < nw; ++w) n += s_wrow[w][e];
-    s_cnt[e] = n;
+    }
   }
   __syncthreads();
 
-  // 2. exclusive prefix sum of the padded counts, one wavefront
+  // 2. exclusive prefix sum of the padded counts, one wavefront, which first
+  // adds up each of its lane's four experts' per-wavefront counts
   if (wave == 0) {
+    int cnt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;
+      int n = 0;
+      if (e < E)
+        for (int w = 0; w < nw; ++w) n += s_wrow[w][e];
+      cnt[j] = n;
+      if (e < E) s_cnt[e] = n;
+    }
     int slot = 0;   // max padding: every expert's padded size
     if (max_pad) {
       int mx = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane * 4 + j;
-        mx = max(mx, e < E ? s_cnt[e] : 0);
-      }
+      for (int j = 0; j < 4; ++j) mx = max(mx, cnt[j]);
 #pragma unroll
       for (int d = kWave / 2; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d));
       slot = (mx + B - 1) / B * B;
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane * 4 + j;
-      const int n = e < E ? s_cnt[e] : 0;
+      const int n = cnt[j];
       loc[j] = run;
       run += e < E ? (max_pad ? slot : (n + B - 1) / B * B) : 0;
     }
@@ -168,10 +174,11 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int64_t p = b0 + j * kWave + lane;
-      ev[j] = p < c1 ? ids[p] : -1;
+      ev[j] = (b0 + j * kWave < c1 && p < c1) ? ids[p] : -1;
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
+      if (b0 + j * kWave >= c1) break;
       const int64_t p = b0 + j * kWave + lane;
       const int e = ev[j];
       const bool valid = (unsigned)e < (unsigned)E;
