@@ -50,9 +50,9 @@ def lib():
         L.orc_align_mode.argtypes = [vp, i64, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp]
         L.orc_align_mode.restype = i32
         L.orc_swiglu.argtypes = [vp, i32, i64, i32, i32, vp, vp, i32, dp]
-        L.orc_swiglu.restype = None
+        L.orc_swiglu.restype = i32
         L.orc_swiglu_s.argtypes = [vp, i32, i64, i32, i32, vp, vp, i32, vp, vp, dp]
-        L.orc_swiglu_s.restype = None
+        L.orc_swiglu_s.restype = i32
         L.orc_fp8_e4m3.argtypes = [ctypes.c_uint8]
         L.orc_fp8_e4m3.restype = ctypes.c_double
         L.orc_combine.argtypes = [dp, dp, dp, i64, i32, i32, dp]
@@ -110,6 +110,14 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _check(rc, what):
+    """Raises for a nonzero oracle return code (-3: a host allocation failed)."""
+    if rc == -3:
+        raise MemoryError(f"{what}: out of host memory")
+    if rc:
+        raise ValueError(f"{what}: bad arguments (code {rc})")
+
+
 def set_threads(n):
     lib().orc_set_threads(int(n))
 
@@ -125,9 +133,7 @@ def route(logits, K):
     T, E = l.shape
     ids = np.empty((T, K), np.int32)
     w = np.empty((T, K), np.float64)
-    rc = lib().orc_route(_p(l), T, E, K, _p(ids), _p(w))
-    if rc:
-        raise ValueError(f"orc_route: bad arguments (E={E}, K={K})")
+    _check(lib().orc_route(_p(l), T, E, K, _p(ids), _p(w)), f"orc_route (E={E}, K={K})")
     return ids, w
 
 
@@ -147,9 +153,8 @@ def route_var(logits, Kmax, k_tok):
     k = _budget(k_tok, T)
     ids = np.empty((T, Kmax), np.int32)
     w = np.empty((T, Kmax), np.float64)
-    rc = lib().orc_route_var(_p(l), T, E, Kmax, _p(k), _p(ids), _p(w))
-    if rc:
-        raise ValueError(f"orc_route_var: bad arguments (E={E}, Kmax={Kmax})")
+    _check(lib().orc_route_var(_p(l), T, E, Kmax, _p(k), _p(ids), _p(w)),
+           f"orc_route_var (E={E}, Kmax={Kmax})")
     return ids, w
 
 
@@ -169,8 +174,7 @@ def align(ids, E, B, cap, mode="block"):
                               _p(out["block_expert"]), _p(out["inv_pos"]))
     if rc == -2:
         raise ValueError("orc_align: padded total exceeds capacity")
-    if rc:
-        raise ValueError("orc_align: bad arguments")
+    _check(rc, "orc_align")
     return out
 
 
@@ -184,7 +188,7 @@ def swiglu(x, w13, w2):
     I = a13.shape[0] // 2
     assert a13.shape == (2 * I, H) and a2.shape == (H, I)
     y = np.empty((n, H), np.float64)
-    lib().orc_swiglu(_p(xa), xdt, n, H, I, _p(a13), _p(a2), wdt, _p(y))
+    _check(lib().orc_swiglu(_p(xa), xdt, n, H, I, _p(a13), _p(a2), wdt, _p(y)), "orc_swiglu")
     return y
 
 
@@ -208,7 +212,8 @@ def swiglu_fp8(x, q13, s13, q2, s2):
     sc13, sc2 = _scales(s13), _scales(s2)
     assert a13.shape == (2 * I, H) and a2.shape == (H, I) and sc13.shape == (2 * I,) and sc2.shape == (H,)
     y = np.empty((n, H), np.float64)
-    lib().orc_swiglu_s(_p(xa), xdt, n, H, I, _p(a13), _p(a2), wdt, _p(sc13), _p(sc2), _p(y))
+    _check(lib().orc_swiglu_s(_p(xa), xdt, n, H, I, _p(a13), _p(a2), wdt, _p(sc13), _p(sc2), _p(y)),
+           "orc_swiglu_s")
     return y
 
 
@@ -236,8 +241,7 @@ def moe_layer_fp8(x, logits, q13, s13, q2, s2, K, qs13=None, ss13=None, qs2=None
     rc = lib().orc_moe_layer_s(_p(xa), xdt, _p(la), T, H, I, E, K, _p(a13), _p(a2), wdt, _p(sc13),
                                _p(sc2), Is, _p(b13), _p(b2), _p(_scales(ss13)), _p(_scales(ss2)),
                                _p(ids), _p(w), _p(out))
-    if rc:
-        raise ValueError("orc_moe_layer: bad arguments")
+    _check(rc, "orc_moe_layer")
     return out, ids, w
 
 
@@ -273,8 +277,7 @@ def moe_layer_var(x, logits, w13, w2, Kmax, k_tok, ws13=None, ws2=None):
     w = np.empty((T, Kmax), np.float64)
     rc = lib().orc_moe_layer_k(_p(xa), xdt, _p(la), _p(k), T, H, I, E, Kmax, _p(a13), _p(a2), wdt,
                                None, None, Is, _p(s13), _p(s2), None, None, _p(ids), _p(w), _p(out))
-    if rc:
-        raise ValueError("orc_moe_layer_k: bad arguments")
+    _check(rc, "orc_moe_layer_k")
     return out, ids, w
 
 
@@ -296,6 +299,5 @@ def moe_layer(x, logits, w13, w2, K, ws13=None, ws2=None):
     w = np.empty((T, K), np.float64)
     rc = lib().orc_moe_layer(_p(xa), xdt, _p(la), T, H, I, E, K, _p(a13), _p(a2), wdt, Is,
                              _p(s13), _p(s2), _p(ids), _p(w), _p(out))
-    if rc:
-        raise ValueError("orc_moe_layer: bad arguments")
+    _check(rc, "orc_moe_layer")
     return out, ids, w

@@ -148,7 +148,7 @@ int orc_max_threads(void)
  * The selection compares the fp32 logits themselves: softmax is increasing,
  * so the K largest logits are the K largest probabilities, and ties between
  * equal logits go to the lower expert id (IEEE comparison, -0 == +0).
- * Returns 0, or -1 if K is outside [1, E].
+ * Returns 0, -1 if K is outside [1, E], -3 if out of host memory.
  */
 int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double *w);
 
@@ -156,7 +156,8 @@ int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double
  * Routing with a per-token budget: token t takes k_t = k_tok[t], clamped to
  * [0, Kmax], experts, selected and renormalised as by orc_route with K = k_t;
  * slots k_t .. Kmax-1 of its row hold id -1 and weight 0.  ids and w are
- * [T][Kmax].  Returns 0, or -1 if Kmax is outside [1, E].
+ * [T][Kmax].  Returns 0, -1 if Kmax is outside [1, E], -3 if out of host
+ * memory.
  */
 int orc_route_var(const float *logits, int64_t T, int E, int Kmax, const int32_t *k_tok,
                   int32_t *ids, double *w)
@@ -165,8 +166,8 @@ int orc_route_var(const float *logits, int64_t T, int E, int Kmax, const int32_t
         return -1;
     for (int64_t t = 0; t < T; ++t) {
         int k = k_tok[t] < 0 ? 0 : (k_tok[t] > Kmax ? Kmax : k_tok[t]);
-        if (k > 0)
-            orc_route(logits + t * E, 1, E, k, ids + t * Kmax, w + t * Kmax);
+        if (k > 0 && orc_route(logits + t * E, 1, E, k, ids + t * Kmax, w + t * Kmax) != 0)
+            return -3;
         for (int j = k; j < Kmax; ++j) {
             ids[t * Kmax + j] = -1;
             w[t * Kmax + j] = 0.0;
@@ -181,6 +182,11 @@ int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double
         return -1;
     double *p = malloc(sizeof(double) * (size_t)E);
     unsigned char *taken = malloc((size_t)E);
+    if (!p || !taken) {
+        free(p);
+        free(taken);
+        return -3;
+    }
     for (int64_t t = 0; t < T; ++t) {
         const float *l = logits + t * E;
         double m = l[0];
@@ -229,7 +235,7 @@ int orc_route(const float *logits, int64_t T, int E, int K, int32_t *ids, double
  * A pair with a negative id is an unused slot (per-token budget): it is in no
  * bucket and inv_pos[p] = -1.
  * cap must be a multiple of B.  Returns 0, -1 on bad arguments (an id >= E
- * among them), -2 if the padded total exceeds cap.
+ * among them), -2 if the padded total exceeds cap, -3 if out of host memory.
  */
 int orc_align_mode(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, int mode,
                    int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
@@ -260,6 +266,8 @@ int orc_align_mode(const int32_t *ids, int64_t T, int K, int E, int B, int64_t c
     for (int64_t r = 0; r < cap; ++r)
         sorted_ids[r] = (int32_t)TK;
     int32_t *fill = calloc((size_t)E, sizeof(int32_t));
+    if (!fill)
+        return -3;
     for (int64_t p = 0; p < TK; ++p) {
         int e = ids[p];
         if (e < 0) {
@@ -290,29 +298,38 @@ int orc_align(const int32_t *ids, int64_t T, int K, int E, int B, int64_t cap, i
 /*
  * y[r][:] = SwiGLU(x[r][:]) for n rows with one set of weights
  * (w13 [2I][H] gate rows then up rows, w2 [H][I]).  Serves a single expert,
- * the shared experts and DenseFA.  Parallel over rows.
+ * the shared experts and DenseFA.  Parallel over rows.  Returns 0, or -3 if
+ * a thread's buffers could not be allocated (y is then incomplete).
  */
-void orc_swiglu_s(const void *x, int xdt, int64_t n, int H, int I, const void *w13,
-                  const void *w2, int wdt, const float *s13, const float *s2, double *y)
+int orc_swiglu_s(const void *x, int xdt, int64_t n, int H, int I, const void *w13,
+                 const void *w2, int wdt, const float *s13, const float *s2, double *y)
 {
+    int rc = 0;
 #pragma omp parallel
     {
         double *xv = malloc(sizeof(double) * (size_t)H);
         double *scratch = malloc(sizeof(double) * swiglu_scratch(H, I));
+        if (!xv || !scratch) {
+#pragma omp atomic write
+            rc = -3;
+        }
 #pragma omp for schedule(dynamic, 1)
         for (int64_t r = 0; r < n; ++r) {
+            if (!xv || !scratch)
+                continue;
             decode_row(x, xdt, r, H, xv, NULL);
             swiglu_token(xv, H, I, w13, w2, wdt, s13, s2, scratch, y + r * H);
         }
         free(xv);
         free(scratch);
     }
+    return rc;
 }
 
-void orc_swiglu(const void *x, int xdt, int64_t n, int H, int I, const void *w13, const void *w2,
-                int wdt, double *y)
+int orc_swiglu(const void *x, int xdt, int64_t n, int H, int I, const void *w13, const void *w2,
+               int wdt, double *y)
 {
-    orc_swiglu_s(x, xdt, n, H, I, w13, w2, wdt, NULL, NULL, y);
+    return orc_swiglu_s(x, xdt, n, H, I, w13, w2, wdt, NULL, NULL, y);
 }
 
 /*
@@ -338,8 +355,8 @@ void orc_combine(const double *y, const double *w, const double *s, int64_t T, i
  * each of its K experts on it, add the shared experts (weight 1, width Is;
  * Is = 0 for none), and combine.  w13 is [E][2I][H], w2 is [E][H][I]; for FP8
  * weights s13 [E][2I], s2 [E][H], ss13 [2Is], ss2 [H] are the row scales
- * (NULL otherwise).  ids_out/w_out (nullable) receive the routing.  Returns 0
- * or the route error.
+ * (NULL otherwise).  ids_out/w_out (nullable) receive the routing.  Returns 0,
+ * -1 on bad arguments, -3 if out of host memory (out is then incomplete).
  */
 int orc_moe_layer_k(const void *x, int xdt, const float *logits, const int32_t *k_tok, int64_t T,
                     int H, int I, int E, int K, const void *w13, const void *w2, int wdt,
@@ -370,7 +387,7 @@ int orc_moe_layer_k(const void *x, int xdt, const float *logits, const int32_t *
     if (E < 1 || K < 1 || K > E || T < 0)
         return -1;
     const size_t esize = elem_size(wdt);
-    int rc = 0;
+    int rc = 0;  /* written by any thread that fails, with an atomic write */
 #pragma omp parallel
     {
         double *xv = malloc(sizeof(double) * (size_t)H);
@@ -379,11 +396,20 @@ int orc_moe_layer_k(const void *x, int xdt, const float *logits, const int32_t *
         double *y = malloc(sizeof(double) * (size_t)H * (size_t)(K + 1));
         int32_t *ids = malloc(sizeof(int32_t) * (size_t)K);
         double *w = malloc(sizeof(double) * (size_t)K);
+        const int have = xv && scratch && y && ids && w;
+        if (!have) {
+#pragma omp atomic write
+            rc = -3;
+        }
 #pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < T; ++t) {
+            if (!have)
+                continue;
             const int32_t kt = k_tok ? k_tok[t] : K;
-            if (orc_route_var(logits + t * E, 1, E, K, &kt, ids, w) != 0) {
-                rc = -1;
+            const int rr = orc_route_var(logits + t * E, 1, E, K, &kt, ids, w);
+            if (rr != 0) {
+#pragma omp atomic write
+                rc = rr;
                 continue;
             }
             decode_row(x, xdt, t, H, xv, NULL);

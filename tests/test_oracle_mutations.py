@@ -32,8 +32,8 @@ MUTANTS = {
     "fp8_subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
     "fp8_row_scale_ignored": ("const double sc = scale ? (double)scale[row] : 1.0;",
                               "const double sc = 1.0;"),
-    "budget_renormalised_over_kmax": ("orc_route(logits + t * E, 1, E, k, ids + t * Kmax, w + t * Kmax);",
-                                      "orc_route(logits + t * E, 1, E, Kmax, ids + t * Kmax, w + t * Kmax);"),
+    "budget_renormalised_over_kmax": ("orc_route(logits + t * E, 1, E, k, ids + t * Kmax, w + t * Kmax)",
+                                      "orc_route(logits + t * E, 1, E, Kmax, ids + t * Kmax, w + t * Kmax)"),
     "unused_slot_counted": ("if (ids[p] >= 0)\n            counts[ids[p]] += 1;",
                             "counts[ids[p] < 0 ? 0 : ids[p]] += 1;"),
     "layer_ignores_budget": ("const int32_t kt = k_tok ? k_tok[t] : K;", "const int32_t kt = K;"),
