@@ -37,7 +37,9 @@ FP32_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "MoE-layer tokens/s at 1 GPU, % HBM/MFMA roofline, tax τ vs DenseFA"
 
-HEADLINE = [("mixtral", 32, "uniform")]
+# the largest workload that fits one GPU: a DeepSeek-V3-shaped layer (22.5 GB of routed
+# weights resident) at the decode batch where the notes place DeepSeek's peak tax (128)
+HEADLINE = [("deepseek_v3", 128, "uniform")]
 ALL = [("tiny", 64, "uniform"), ("mixtral", 32, "uniform"), ("mixtral", 1024, "uniform"),
        ("qwen2", 1, "zipf"), ("qwen2", 32, "zipf"), ("qwen2", 256, "zipf"), ("qwen2", 2048, "zipf"),
        ("deepseek_v3", 128, "uniform"), ("deepseek_v3", 128, "zipf")] + \
@@ -172,8 +174,10 @@ def breakdown(layer, reps=10):
     return out
 
 
-def cpu_baseline(shape, dev_inputs, T, budget_s=20.0, min_s=10.0):
-    """The oracle (as it is) on the host cores, on a bounded sample of the batch."""
+def cpu_baseline(shape, dev_inputs, T, budget_s=20.0, min_s=10.0, host_bytes=8 << 30):
+    """The oracle (as it is) on the host cores, on a bounded sample of the batch:
+    at most budget_s of estimated work per pass, and no more tokens than keep
+    the host copy of the experts they use within host_bytes."""
     import oracle
     x = dev_inputs["x"].cpu()
     logits = dev_inputs["logits"].cpu()
@@ -184,11 +188,22 @@ def cpu_baseline(shape, dev_inputs, T, budget_s=20.0, min_s=10.0):
     n = int(max(1, min(T, budget_s * 0.4e9 * threads / macs_tok)))
     tokens = np.linspace(0, T - 1, n).round().astype(np.int64)
     tokens = np.unique(tokens)
-    used = np.unique(ids[tokens])
+    w13d, w2d = dev_inputs["w13"], dev_inputs["w2"]
+    per_expert = w13d[0].numel() * w13d.element_size() + w2d[0].numel() * w2d.element_size()
+    keep, used = [], set()
+    for t in tokens:
+        more = used | set(ids[t].tolist())
+        if keep and len(more) * per_expert > host_bytes:
+            break
+        keep.append(int(t))
+        used = more
+    tokens = np.array(keep, dtype=np.int64)
+    used = sorted(used)
     # only the experts the sample routes to are copied; the others are never read
+    # (torch.empty leaves their pages untouched)
     E = shape.experts
-    w13 = torch.zeros((E,) + tuple(dev_inputs["w13"].shape[1:]), dtype=dev_inputs["w13"].dtype)
-    w2 = torch.zeros((E,) + tuple(dev_inputs["w2"].shape[1:]), dtype=dev_inputs["w2"].dtype)
+    w13 = torch.empty((E,) + tuple(w13d.shape[1:]), dtype=w13d.dtype)
+    w2 = torch.empty((E,) + tuple(w2d.shape[1:]), dtype=w2d.dtype)
     for e in used:
         w13[e] = dev_inputs["w13"][e].cpu()
         w2[e] = dev_inputs["w2"][e].cpu()
@@ -205,8 +220,9 @@ def cpu_baseline(shape, dev_inputs, T, budget_s=20.0, min_s=10.0):
         reps += 1
     return {"value": round(reps * len(tokens) / dt, 3), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(tokens)} of the {T} tokens of the same batch (weights bf16 on host, "
-                      f"fp64 accumulation), {reps} pass{'es' if reps > 1 else ''}, {dt:.2f} s wall"}
+            "sample": f"{len(tokens)} of the {T} tokens of the same batch ({len(used)} experts' "
+                      f"weights bf16 on host, fp64 accumulation), {reps} pass{'es' if reps > 1 else ''}, "
+                      f"{dt:.2f} s wall"}
 
 
 def run_workload(name, T, routing, steps, warmup, do_cpu):
@@ -226,6 +242,9 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
         layer.forward((a, b) if a is not None else None)
 
     ms, wall_ms, gu_ms = time_steps(step, steps, warmup, mid=True)
+    # the gate/up launch alone, back to back (nothing else on the GPU: the number a
+    # kernel trace of it reports; in the pass the shared experts stream beside it)
+    gu_alone_ms, _, _ = time_steps(layer.gate_up, steps, warmup)
     fa_ms, _, _ = time_steps(layer.dense_fa, steps, warmup)
     pa_ms, _, _ = time_steps(layer.dense_pa, steps, warmup)
     bd = breakdown(layer)
@@ -249,10 +268,19 @@ def run_workload(name, T, routing, steps, warmup, do_cpu):
     workload = f"{name} T={T} {routing}"
     traffic = measured_traffic(workload)
     roof["traffic"] = traffic
+    # not counted in this run: read from the committed counter record, and only while
+    # the kernel's sources are the ones the counters were taken with
+    roof["traffic_source"] = ("profiles/hbm_traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE runs "
+                              "of the same kernel sources, scaled by a device copy's counts"
+                              if traffic is not None else None)
     roof["kernel"] = gate_up_kernel(shape, T, layer.block_m)
     roof["algorithmic_bytes"] = alg["gu_bytes"]
     roof["algorithmic_flops"] = alg["gu_flops"]
     roof["avg_launch_us"] = round(gu_ms * 1e3, 2)
+    roof["isolated_avg_launch_us"] = round(gu_alone_ms * 1e3, 2)
+    roof["isolated_frac"] = round((alg["gu_bytes"] / (gu_alone_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                                  if roof["bound"] == "hbm" else
+                                  (alg["gu_flops"] / (gu_alone_ms * 1e-3) / 1e12 / peak_flops), 4)
 
     layer_s = ms * 1e-3
     rec = {

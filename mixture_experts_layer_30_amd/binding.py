@@ -216,8 +216,21 @@ def dense_ffn_fa(x, w13, w2, workspace, out, sched=SCHED_AUTO, stream=None):
                               sched, _stream(stream)))
 
 
+def _need(t, dtype, what):
+    """The FP8 entry points take no dtype argument for these tensors: check here."""
+    if t.dtype != dtype:
+        raise MoEError(MOE_EUNSUPPORTED, f"{what} must be {dtype}, got {t.dtype}")
+
+
+def _fp8_weights(q, s, what):
+    _need(q, torch.uint8, what + " codes")
+    _need(s, torch.float32, what + " row scales")
+
+
 def moe_grouped_gate_up_fp8(x, q13, s13, K, plan, workspace, stream=None):
-    """FP8 E4M3 expert weights: q13 uint8 [E,2I,H] codes, s13 fp32 [E,2I] row scales."""
+    """FP8 E4M3 expert weights: q13 uint8 [E,2I,H] codes, s13 fp32 [E,2I] row scales; x bf16."""
+    _need(x, torch.bfloat16, "x")
+    _fp8_weights(q13, s13, "w13")
     T, H = x.shape
     E, I2, _ = q13.shape
     _check(lib().moe_grouped_gate_up_fp8(_ptr(x), T, H, I2 // 2, E, K, _ptr(q13), _ptr(s13),
@@ -227,6 +240,8 @@ def moe_grouped_gate_up_fp8(x, q13, s13, K, plan, workspace, stream=None):
 
 def moe_grouped_down_fp8(q2, s2, T, K, plan, workspace, y_pairs, stream=None):
     """q2 uint8 [E,H,I] codes, s2 fp32 [E,H] row scales; y_pairs bf16."""
+    _need(y_pairs, torch.bfloat16, "y_pairs")
+    _fp8_weights(q2, s2, "w2")
     E, H, I = q2.shape
     _check(lib().moe_grouped_down_fp8(_ptr(q2), _ptr(s2), T, H, I, E, K, ctypes.byref(plan.c),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -234,6 +249,10 @@ def moe_grouped_down_fp8(q2, s2, T, K, plan, workspace, y_pairs, stream=None):
 
 
 def dense_ffn_fp8(x, q13, s13, q2, s2, workspace, out, stream=None):
+    """x bf16 [T,H]; q13/s13, q2/s2 FP8 codes and row scales; out bf16 or fp32."""
+    _need(x, torch.bfloat16, "x")
+    _fp8_weights(q13, s13, "w13")
+    _fp8_weights(q2, s2, "w2")
     T, H = x.shape
     I = q2.shape[1]
     _check(lib().dense_ffn_fp8(_ptr(x), T, H, I, _ptr(q13), _ptr(s13), _ptr(q2), _ptr(s2),

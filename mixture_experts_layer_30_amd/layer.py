@@ -44,6 +44,8 @@ class MoELayer:
         routing budgets [T] int32 on the device (moe_route_var; K is then the
         largest budget allowed)."""
         x = inputs["x"]
+        if fp8 and x.dtype != torch.bfloat16:
+            raise B.MoEError(B.MOE_EUNSUPPORTED, f"FP8 weights need bf16 tokens, got {x.dtype}")
         self.fp8 = fp8
         self.k_tok = k_tok
         self.shape, self.inputs, self.sched = shape, inputs, sched

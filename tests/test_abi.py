@@ -187,3 +187,33 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_fp8_binding_rejects_other_activation_dtypes(L):
+    """The FP8 entry points take no dtype for x and y_pairs (bf16 by definition):
+    the binding refuses other dtypes before calling the library."""
+    import torch
+    x32 = torch.zeros(4, 128)
+    q = torch.zeros(2, 256, 128, dtype=torch.uint8)
+    s = torch.ones(2, 256)
+    p = B.Plan(4, 1, 2, 16, "cpu")
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(B.MoEError) as e:
+        B.moe_grouped_gate_up_fp8(x32, q, s, 1, p, ws)
+    assert e.value.status == B.MOE_EUNSUPPORTED
+    with pytest.raises(B.MoEError):   # scales must be fp32
+        B.moe_grouped_gate_up_fp8(x32.bfloat16(), q, s.double(), 1, p, ws)
+    q2 = torch.zeros(2, 128, 128, dtype=torch.uint8)
+    with pytest.raises(B.MoEError):
+        B.moe_grouped_down_fp8(q2, torch.ones(2, 128), 4, 1, p, ws, torch.zeros(4, 128))
+    with pytest.raises(B.MoEError):
+        B.dense_ffn_fp8(x32, q[0], s[0], q2[0], torch.ones(128), ws, torch.zeros(4, 128))
+
+
+def test_layer_rejects_fp8_with_fp32_tokens():
+    import torch
+    from mixture_experts_layer_30_amd.configs import LayerShape
+    from mixture_experts_layer_30_amd.layer import MoELayer
+    shape = LayerShape("t", 128, 128, 2, 1, 0, "f32", (4,), ("uniform",))
+    with pytest.raises(B.MoEError):
+        MoELayer(shape, {"x": torch.zeros(4, 128), "logits": torch.zeros(4, 2)}, fp8=True)
