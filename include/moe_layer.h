@@ -22,7 +22,10 @@
  *
  * Conventions (all calls):
  *  - Every buffer is device memory owned by the caller; the library never
- *    allocates, frees or keeps state between calls, and is thread-safe.
+ *    allocates or frees memory.  The state it keeps between calls is the
+ *    per-thread message of moe_last_error() and the per-GPU workspace array of
+ *    moe_grouped_ffn_noalloc (with its device address); every other call is
+ *    thread-safe.
  *  - Tensors are dense row-major; base pointers are 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    on it and the call returns without waiting; results are valid once the
@@ -225,6 +228,31 @@ moe_status moe_grouped_ffn(const void *x, moe_dtype dt, int64_t T, int H, int I,
                            const void *w13, const void *w2, const moe_plan *plan,
                            void *workspace, int64_t workspace_bytes, void *y_pairs,
                            void *stream);
+
+/*
+ * Allocation-free variant of moe_grouped_ffn, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid allocation.  It computes what moe_grouped_ffn computes, with the
+ * same kernels and schedules as moe_grouped_ffn given a workspace of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes, but that workspace is a device array held
+ * by the library: one array of MOE_NOALLOC_SCRATCH_BYTES on each GPU the
+ * library runs on, from when its code is loaded there until the process ends.
+ * The caller passes the inputs, the plan and y_pairs as for moe_grouped_ffn;
+ * the call allocates and frees no device memory.
+ * Every call on one GPU shares that GPU's array and finds the last call's
+ * contents in it; no part of it needs to start at zero (rows of the array
+ * that hold no token may be read by the tiled schedule, but their products
+ * are never stored).  Calls that overlap on one GPU race (two streams, or two
+ * host threads whose calls are not ordered on one stream): their results are
+ * undefined.  Calls ordered on one stream are safe.
+ * Errors: as moe_grouped_ffn; MOE_ECAPACITY when moe_ffn_workspace_bytes(
+ * plan->cap, I) exceeds MOE_NOALLOC_SCRATCH_BYTES, checked before any device
+ * call.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((int64_t)128 << 20)
+moe_status moe_grouped_ffn_noalloc(const void *x, moe_dtype dt, int64_t T, int H, int I, int E,
+                                   int K, const void *w13, const void *w2, const moe_plan *plan,
+                                   void *y_pairs, void *stream);
 
 /* First half of moe_grouped_ffn: writes a = silu(W1 x) * (W3 x) as bf16 into
  * workspace row r, columns 0..I-1, for every valid row r. */

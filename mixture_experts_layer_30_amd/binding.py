@@ -22,7 +22,10 @@ EXPORTS = ["moe_last_error", "moe_status_string", "moe_align_capacity", "moe_ali
            "moe_ffn_workspace_bytes", "moe_ffn_workspace_bytes_ex", "dense_ffn_workspace_bytes",
            "moe_route", "moe_route_var", "moe_align", "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
            "moe_combine", "dense_ffn_fa", "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8",
-           "dense_ffn_fp8"]
+           "dense_ffn_fp8", "moe_grouped_ffn_noalloc"]
+
+# workspace bytes held per GPU by moe_grouped_ffn_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class MoEError(RuntimeError):
@@ -72,6 +75,8 @@ def lib():
         L.moe_align_ex.argtypes = [vp, i64, i32, i32, P, i32, vp]
         L.moe_grouped_ffn.restype = i32
         L.moe_grouped_ffn.argtypes = [vp, i32, i64, i32, i32, i32, i32, vp, vp, P, vp, i64, vp, vp]
+        L.moe_grouped_ffn_noalloc.restype = i32
+        L.moe_grouped_ffn_noalloc.argtypes = [vp, i32, i64, i32, i32, i32, i32, vp, vp, P, vp, vp]
         L.moe_grouped_gate_up.restype = i32
         L.moe_grouped_gate_up.argtypes = [vp, i32, i64, i32, i32, i32, i32, vp, P, vp, i64, i32, vp]
         L.moe_grouped_down.restype = i32
@@ -183,6 +188,14 @@ def moe_grouped_ffn(x, w13, w2, K, plan, workspace, y_pairs, stream=None):
     _check(lib().moe_grouped_ffn(_ptr(x), _dt(x), T, H, I2 // 2, E, K, _ptr(w13), _ptr(w2),
                                  ctypes.byref(plan.c), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _ptr(y_pairs), _stream(stream)))
+
+
+def moe_grouped_ffn_noalloc(x, w13, w2, K, plan, y_pairs, stream=None):
+    """moe_grouped_ffn with the library's own per-GPU workspace (no workspace argument)."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    _check(lib().moe_grouped_ffn_noalloc(_ptr(x), _dt(x), T, H, I2 // 2, E, K, _ptr(w13), _ptr(w2),
+                                         ctypes.byref(plan.c), _ptr(y_pairs), _stream(stream)))
 
 
 def moe_grouped_gate_up(x, w13, K, plan, workspace, sched=SCHED_AUTO, stream=None):

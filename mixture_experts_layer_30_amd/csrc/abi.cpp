@@ -285,6 +285,18 @@ moe_status pick_stream(moe_schedule req, bool ring_ok, bool auto_ok, const char*
 
 }  // namespace
 
+namespace moe {
+
+int set_last_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_err; }

@@ -6,6 +6,9 @@
 
 namespace moe {
 
+// Records the message moe_last_error() returns on this thread; returns status.
+int set_last_error(int status, const char* fmt, ...);
+
 constexpr int kDtF32 = 0;
 constexpr int kDtBF16 = 1;
 constexpr int kDtFP8 = 2;   // weights only: OCP E4M3 codes with fp32 row scales

@@ -217,3 +217,18 @@ def test_layer_rejects_fp8_with_fp32_tokens():
     shape = LayerShape("t", 128, 128, 2, 1, 0, "f32", (4,), ("uniform",))
     with pytest.raises(B.MoEError):
         MoELayer(shape, {"x": torch.zeros(4, 128), "logits": torch.zeros(4, 2)}, fp8=True)
+
+
+def test_noalloc_argument_checks(L):
+    """moe_grouped_ffn_noalloc checks its plan against the library's array before
+    any device call; an empty batch returns without touching the device."""
+    assert st(L.moe_grouped_ffn_noalloc(FAKE, B.MOE_BF16, 32, 4096, 14336, 8, 2, FAKE, FAKE, None,
+                                        FAKE, None)) == B.MOE_EINVAL
+    big = plan(cap=33792)   # 33792 rows x 14336 x 2 B of activations: far above the array
+    assert B.moe_ffn_workspace_bytes(33792, 14336) > B.NOALLOC_SCRATCH_BYTES
+    assert st(L.moe_grouped_ffn_noalloc(FAKE, B.MOE_BF16, 16384, 4096, 14336, 8, 2, FAKE, FAKE,
+                                        ctypes.byref(big), FAKE, None)) == B.MOE_ECAPACITY
+    assert "allocation-free" in L.moe_last_error().decode()
+    small = plan(cap=192)
+    assert st(L.moe_grouped_ffn_noalloc(NULL, B.MOE_BF16, 0, 4096, 14336, 8, 2, FAKE, FAKE,
+                                        ctypes.byref(small), NULL, None)) == B.MOE_OK
