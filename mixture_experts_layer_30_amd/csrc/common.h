@@ -92,6 +92,24 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(uint2 v) {
   return r;
 }
 
+// Four consecutive outputs with one store instruction (p 8-byte aligned for
+// bf16, 16-byte aligned for fp32).  Stores count in vmcnt like loads, so an
+// epilogue of single-element stores makes the next wait for a stage in flight
+// also wait for them.
+template <class S>
+__device__ __forceinline__ void store_out4(typename S::T* p, f32x4 v);
+template <>
+__device__ __forceinline__ void store_out4<F32>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store_out4<BF16>(uint16_t* p, f32x4 v) {
+  uint2 q;
+  q.x = pack_bf16x2(v.x, v.y);
+  q.y = pack_bf16x2(v.z, v.w);
+  *reinterpret_cast<uint2*>(p) = q;
+}
+
 template <class S>
 __device__ __forceinline__ void store_out(typename S::T* p, float v);
 template <>

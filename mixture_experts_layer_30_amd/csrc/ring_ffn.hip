@@ -447,10 +447,8 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
               const int c = ic.slab * 64 + 8 * wave + 2 * g;
               if (part) {
                 float* pr = part + ((size_t)ic.z * prows + pair) * (2 * (size_t)I);
-                pr[c] = v.x;
-                pr[c + 1] = v.y;
-                pr[I + c] = v.z;
-                pr[I + c + 1] = v.w;
+                *reinterpret_cast<float2*>(pr + c) = float2{v.x, v.y};   // c is even
+                *reinterpret_cast<float2*>(pr + I + c) = float2{v.z, v.w};
               } else {
                 *reinterpret_cast<uint32_t*>(act + row * I + c) =
                     pack_bf16x2(silu(v.x) * v.z, silu(v.y) * v.w);
@@ -464,10 +462,7 @@ __global__ __launch_bounds__(kRThreads, 1) void ring_ffn_kernel(
                 *reinterpret_cast<f32x4*>(part + ((size_t)ic.z * prows + dst) * H + h) = v;
               } else {
                 typename SY::T* o = y + (size_t)dst * H + h;
-                store_out<SY>(o + 0, v.x);
-                store_out<SY>(o + 1, v.y);
-                store_out<SY>(o + 2, v.z);
-                store_out<SY>(o + 3, v.w);
+                store_out4<SY>(o, v);
               }
             }
           }

@@ -188,10 +188,7 @@ __global__ __launch_bounds__(kTileThreads, 2) void tile_ffn_kernel(
           const int h = i0 + wm * 64 + tm * 16 + 4 * g;
           typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
           const f32x4 v = acc[tm][tn];
-          store_out<SY>(o + 0, v.x);
-          store_out<SY>(o + 1, v.y);
-          store_out<SY>(o + 2, v.z);
-          store_out<SY>(o + 3, v.w);
+          store_out4<SY>(o, v);
         }
       }
   }
@@ -515,10 +512,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
             *reinterpret_cast<f32x4*>(part + ((size_t)zk * rm.dense_rows + sm.dst[j]) * H + h) = v;
           } else {
             typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
-            store_out<SY>(o + 0, v.x);
-            store_out<SY>(o + 1, v.y);
-            store_out<SY>(o + 2, v.z);
-            store_out<SY>(o + 3, v.w);
+            store_out4<SY>(o, v);
           }
         }
       }
