@@ -65,8 +65,11 @@ typedef enum {
                               TEMPO page): experts whose tokens fit a ring pass (every
                               token up to T = 32; 16 or 32 beyond) streamed, busier ones
                               tiled when block_m allows it, else streamed by STREAM; else
-                              STREAM; the bf16 gate/up tile is 512 weight rows wide once
-                              experts average 512 tokens (T*K >= 512*E, block_m 128,
+                              STREAM; SPAN instead of TILE for the gate/up half once
+                              experts average 256 tokens (T*K >= 256*E) and for the down
+                              half when also (H/256) * (T*K/256 + E) <= 256, where SPAN
+                              applies; else the bf16 gate/up tile is 512 weight rows wide
+                              once experts average 512 tokens (T*K >= 512*E, block_m 128,
                               I % 256 == 0); dense rows: TILE above 32
                               tokens (a gate/up grid, (I/128) x ceil(T/block), of fewer
                               than 128 tiles, or a down grid of fewer than 256, splits
@@ -79,9 +82,16 @@ typedef enum {
                               staged through LDS (a ring of direct loads for bf16 and FP8
                               weights, registers for fp32); for MFMA-bound
                               (prefill) shapes; needs block_m 64 or 128 */
-    MOE_SCHED_RING = 3     /* weight-streaming through an LDS ring filled by whole-line
+    MOE_SCHED_RING = 3,    /* weight-streaming through an LDS ring filled by whole-line
                               direct loads, one persistent workgroup per CU; needs bf16,
                               H % 128 == 0 and I % 64 == 0 (gate/up), I % 128 == 0 (down) */
+    MOE_SCHED_SPAN = 4     /* MFMA tiles of 256 weight rows x spans of up to 256 of one
+                              expert's tokens, any block_m: each weight tile streamed once
+                              per span, by persistent workgroups (one per CU) that cut the
+                              items into one run per XCD; for MFMA-bound (prefill) shapes;
+                              needs bf16, E <= 512, H % 256 == 0, I % 128 == 0 and an
+                              expert's gate/up matrix, x and the activations each below
+                              4 GB (else MOE_EUNSUPPORTED) */
 } moe_schedule;
 
 /*

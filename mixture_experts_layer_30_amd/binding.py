@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_layer.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-SCHED_AUTO, SCHED_STREAM, SCHED_TILE, SCHED_RING = 0, 1, 2, 3
+SCHED_AUTO, SCHED_STREAM, SCHED_TILE, SCHED_RING, SCHED_SPAN = 0, 1, 2, 3, 4
 PAD_BLOCK, PAD_MAX = 0, 1
 
 # every function the C header declares

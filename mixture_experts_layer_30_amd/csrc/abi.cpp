@@ -251,6 +251,35 @@ bool wide_gate_up(moe_dtype dt, int64_t T, int K, int E, int block_m, int H, int
   return dt == MOE_BF16 && T * K >= (int64_t)512 * E && moe::tile_wide_ok(block_m, H, I);
 }
 
+// The span schedule: bf16, E <= 512, H % 256 == 0, I % 128 == 0 and 32-bit
+// offsets into an expert's gate/up matrix, x (T rows) and act (act_rows rows).
+bool span_shape_ok(moe_dtype dt, int E, int H, int I, int64_t T, int64_t act_rows) {
+  return dt == MOE_BF16 && moe::span_ok(E, H, I, T, act_rows);
+}
+
+// AUTO takes the span schedule for the gate/up half once experts average 256
+// tokens (T*K >= 256*E), and for the down half only while its items fit one
+// round of MI355X's 256 CUs ((H/256) x (T*K/256 + E) <= 256, a bound on the
+// spans).  Measured on MI355X: gate/up 708 vs 750 us (Mixtral-shaped, T=1024)
+// and 997 vs 1130 us (T=2048, against the 512-row tile); down 405 vs 439 us at
+// T=1024 but 774 vs 631 us at T=2048, where its 3.5x longer items (the I-long
+// contraction) leave a second, mostly idle round.  Below 256 tokens an expert
+// the 128-token tiles win (Qwen2-shaped, T=256: 398 vs 520 us).
+bool span_auto_gate_up(moe_dtype dt, int64_t T, int K, int E, int H, int I, int64_t cap) {
+  return T * K >= (int64_t)256 * E && span_shape_ok(dt, E, H, I, T, cap);
+}
+
+bool span_auto_down(moe_dtype dt, int64_t T, int K, int E, int H, int I, int64_t cap) {
+  return T * K >= (int64_t)256 * E && (int64_t)(H / 256) * (T * K / 256 + E) <= 256 &&
+         span_shape_ok(dt, E, H, I, T, cap);
+}
+
+moe_status span_unsupported(const char* what) {
+  return fail(MOE_EUNSUPPORTED, "%s: span schedule needs bf16, E <= 512, H %% 256 == 0, "
+              "I %% 128 == 0 and an expert's gate/up matrix, x and the activations each "
+              "below 4 GB", what);
+}
+
 moe_status pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m, int H,
                          moe_schedule* out) {
   if (req == MOE_SCHED_TILE) {
@@ -258,7 +287,7 @@ moe_status pick_schedule(moe_schedule req, int64_t T, int K, int E, int block_m,
       return fail(MOE_EUNSUPPORTED, "tile schedule needs block_m 64 or 128 and H %% 128 == 0 "
                   "(block_m = %d, H = %d)", block_m, H);
     *out = MOE_SCHED_TILE;
-  } else if (req == MOE_SCHED_STREAM || req == MOE_SCHED_RING) {
+  } else if (req == MOE_SCHED_STREAM || req == MOE_SCHED_RING || req == MOE_SCHED_SPAN) {
     *out = req;
   } else if (req == MOE_SCHED_AUTO) {
     // (T <= 32: every expert fits one streaming pass, which beats a tile)
@@ -437,6 +466,9 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
   const bool ring = moe::ring_gate_up_ok(dt, dt, H, I);
   st = pick_stream(sched, ring, ring, "moe_grouped_gate_up", &use);
   if (st) return st;
+  if (sched == MOE_SCHED_AUTO && use == MOE_SCHED_TILE &&
+      span_auto_gate_up(dt, T, K, E, H, I, plan->cap))
+    use = MOE_SCHED_SPAN;
   // automatic below kTileFrom tokens per expert: experts that fit a ring pass
   // are streamed, busier ones tiled where the plan's block allows (two regimes
   // per expert, TEMPO page).  From kTileFrom on every expert is tiled: two
@@ -445,7 +477,10 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (use == MOE_SCHED_TILE && wide_gate_up(dt, T, K, E, plan->block_m, H, I))
+  if (use == MOE_SCHED_SPAN) {
+    if (!span_shape_ok(dt, E, H, I, T, plan->cap)) return span_unsupported("moe_grouped_gate_up");
+    e = moe::launch_span_gate_up(x, w13, rm, E, H, I, T, T * K, (uint16_t*)workspace, s);
+  } else if (use == MOE_SCHED_TILE && wide_gate_up(dt, T, K, E, plan->block_m, H, I))
     e = moe::launch_tile_gate_up_wide(x, w13, rm, plan->cap / plan->block_m, H, I,
                                       (uint16_t*)workspace, s);
   else if (use == MOE_SCHED_TILE)
@@ -489,11 +524,18 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   const bool ring = moe::ring_down_ok(dt, H, I);
   st = pick_stream(sched, ring, ring, "moe_grouped_down", &use);
   if (st) return st;
+  if (sched == MOE_SCHED_AUTO && use == MOE_SCHED_TILE &&
+      span_auto_down(dt, T, K, E, H, I, plan->cap))
+    use = MOE_SCHED_SPAN;
   const bool hot_tiled = sched == MOE_SCHED_AUTO && tile_ok(plan->block_m, H);
   const moe::RowMap rm = grouped_rows(plan, K);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (use == MOE_SCHED_TILE)
+  if (use == MOE_SCHED_SPAN) {
+    if (!span_shape_ok(dt, E, H, I, T, plan->cap)) return span_unsupported("moe_grouped_down");
+    e = moe::launch_span_down(w2, (const uint16_t*)workspace, rm, E, H, I, plan->cap, T * K,
+                              y_pairs, dt, s);
+  } else if (use == MOE_SCHED_TILE)
     e = moe::launch_tile_down(w2, dt, (const uint16_t*)workspace, rm, plan->cap / plan->block_m,
                               H, I, y_pairs, dt, 1, nullptr, s);
   else if (use == MOE_SCHED_RING) {
@@ -577,6 +619,14 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
   const DensePlan dp = dense_plan(T, H, I_fa, dt);
   if (sched == MOE_SCHED_AUTO)
     use = (T <= 32 || !tile_ok(128, H)) ? MOE_SCHED_STREAM : MOE_SCHED_TILE;
+  if (use == MOE_SCHED_SPAN) {
+    if (!span_shape_ok(dt, 1, H, I_fa, T, T)) return span_unsupported("dense_ffn_fa");
+    uint16_t* act = (uint16_t*)workspace;
+    hipError_t e = moe::launch_span_gate_up(x, w13, rm, 1, H, I_fa, T, T, act, s);
+    if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
+    e = moe::launch_span_down(w2, act, rm, 1, H, I_fa, T, T, out, odt, s);
+    return hip_status(e, "dense_ffn_fa down");
+  }
   if (use == MOE_SCHED_TILE) {
     uint16_t* act = (uint16_t*)workspace;
     float* part = (float*)((char*)workspace + dp.act_bytes);

@@ -89,6 +89,21 @@ hipError_t launch_tile_down_fp8(const void* w2, const float* w2_scale, const uin
                                 const RowMap& rm, int64_t nblocks, int H, int I, void* y, int ydt,
                                 int ksplit, float* part, hipStream_t s);
 
+// Prefill-shape schedule with each 256-row weight tile streamed once per span
+// of up to 256 of an expert's tokens (dense rows: of the T rows), by persistent
+// workgroups: bf16 weights and tokens, E <= 512, H % 256 == 0, I % 128 == 0,
+// and an expert's gate/up matrix, the x_rows x H tokens and the act_rows x I
+// activations each below 4 GB (span_ok; hipErrorInvalidValue else).
+// rows_bound bounds the grouped rows (T * K; the plan's cap for the act rows);
+// only experts with min_rows..max_rows tokens are computed.
+bool span_ok(int E, int H, int I, int64_t x_rows, int64_t act_rows);
+hipError_t launch_span_gate_up(const void* x, const void* w13, const RowMap& rm, int E, int H,
+                               int I, int64_t x_rows, int64_t rows_bound, uint16_t* act,
+                               hipStream_t s);
+hipError_t launch_span_down(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H,
+                            int I, int64_t act_rows, int64_t rows_bound, void* y, int ydt,
+                            hipStream_t s);
+
 // act[o][i] = silu(g) * u with g, u the in-order sums over z < splits of
 // part[z][r][i] and part[z][r][I + i], o = out_row[r] (r when out_row is null;
 // rows with out_row[r] < 0 are skipped).

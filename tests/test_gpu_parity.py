@@ -441,6 +441,70 @@ def test_layer_parity_forced_schedule(shape, T, routing, block_m, sched):
     assert rel_err(fa, oracle.dense_ffn(d["x"], d["wfa13"], d["wfa2"])) <= TOL
 
 
+SPAN_SHAPES = [
+    # (shape, T, routing, block_m, pad): the span schedule (bf16, H % 256 == 0,
+    # I % 128 == 0).  Zipf: a hot expert with three spans, the last ragged, and
+    # experts with a handful of tokens; uniform: 275 tokens an expert (a full span
+    # and one of 19 tokens); many experts with one short span each; padding blocks
+    # of 16 and max padding (spans follow the expert's rows, not the blocks)
+    (LayerShape("span_spans", 256, 256, 4, 2, 128, "bf16", (700,), ("zipf",)), 700, "zipf", 128, "block"),
+    (LayerShape("span_b16", 512, 384, 8, 2, 0, "bf16", (300,), ("uniform",)), 300, "uniform", 16, "block"),
+    (LayerShape("span_many", 256, 128, 64, 6, 256, "bf16", (200,), ("uniform",)), 200, "uniform", 64, "block"),
+    (LayerShape("span_two", 768, 512, 4, 1, 0, "bf16", (1100,), ("uniform",)), 1100, "uniform", 128, "block"),
+    (LayerShape("span_maxpad", 256, 256, 16, 2, 128, "bf16", (300,), ("zipf",)), 300, "zipf", 64, "max"),
+]
+
+
+@pytest.mark.parametrize("shape,T,routing,block_m,pad", SPAN_SHAPES, ids=[s[0].name for s in SPAN_SHAPES])
+def test_layer_parity_span(shape, T, routing, block_m, pad):
+    """The span schedule forced on every half: routed experts, the shared expert
+    and DenseFA (dense rows as one expert)."""
+    d, dev = layer_case(shape, T, routing, seed=17)
+    layer = MoELayer(shape, dev, block_m=block_m, sched=B.SCHED_SPAN,
+                     pad=B.PAD_MAX if pad == "max" else B.PAD_BLOCK)
+    out = layer.forward().clone()
+    fa = layer.dense_fa().clone()
+    torch.cuda.synchronize()
+    ref, rids, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], shape.topk,
+                                    d["ws13"], d["ws2"])
+    assert (layer.topk_ids.cpu().numpy() == rids).all()
+    counts = np.bincount(rids.reshape(-1), minlength=shape.experts)
+    if shape.name in ("span_spans", "span_two"):
+        assert counts.max() > 256   # several spans for some expert
+    assert rel_err(out, ref) <= TOL
+    assert rel_err(fa, oracle.dense_ffn(d["x"], d["wfa13"], d["wfa2"])) <= TOL
+    out2 = layer.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("T,H,I", [(300, 256, 384), (40, 512, 128), (513, 256, 256)])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_dense_ffn_span_parity(T, H, I, odt):
+    """The span schedule on dense rows: spans of 256 rows, the last ragged."""
+    x = synth.tokens(T, H, "bf16", seed=I + 1)
+    w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=T + 1)
+    ref = oracle.swiglu(x, w13, w2)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(T, H, I), dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, H, dtype=odt, device=DEV)
+    B.dense_ffn_fa(x.to(DEV), w13.to(DEV), w2.to(DEV), ws, out, sched=B.SCHED_SPAN)
+    torch.cuda.synchronize()
+    assert rel_err(out, ref) <= TOL
+
+
+def test_span_schedule_rejects_unsupported_shape():
+    # H % 256 != 0
+    shape = LayerShape("span_bad", 384, 256, 8, 2, 0, "bf16", (300,), ("uniform",))
+    d, dev = layer_case(shape, 300, "uniform")
+    layer = MoELayer(shape, dev, block_m=128, sched=B.SCHED_SPAN)
+    layer.route()
+    layer.align()
+    with pytest.raises(B.MoEError):
+        layer.gate_up()
+    with pytest.raises(B.MoEError):
+        layer.down()
+
+
 RING_SHAPES = [
     # (shape, T, routing): one and two 16-token blocks per pass; experts busier than
     # a pass (handed to the register-streaming kernel); more work than workgroups
