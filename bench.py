@@ -75,7 +75,7 @@ def gate_up_kernel(shape, T, block_m):
     tile = block_m in (64, 128) and H % 128 == 0
     if tile and T * K >= 24 * E and T > 32:
         if (shape.dtype == "bf16" and T * K >= 256 * E and E <= 512 and H % 256 == 0
-                and I % 128 == 0):
+                and I % 128 == 0 and (I // 128) * ((T * K + 255) // 256) >= 768):
             return "span_ffn_kernel (256-row MFMA tiles over 256-token spans, persistent)"
         if (shape.dtype == "bf16" and block_m == 128 and T * K >= 512 * E and I % 256 == 0
                 and H % 32 == 0):

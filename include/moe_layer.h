@@ -65,10 +65,11 @@ typedef enum {
                               TEMPO page): experts whose tokens fit a ring pass (every
                               token up to T = 32; 16 or 32 beyond) streamed, busier ones
                               tiled when block_m allows it, else streamed by STREAM; else
-                              STREAM; SPAN instead of TILE for the gate/up half once
-                              experts average 256 tokens (T*K >= 256*E) and for the down
-                              half when also (H/256) * (T*K/256 + E) <= 256, where SPAN
-                              applies; else the bf16 gate/up tile is 512 weight rows wide
+                              STREAM; SPAN instead of TILE where it applies, once experts
+                              average 256 tokens (T*K >= 256*E), with n = ceil(T*K/256):
+                              for the gate/up half when (I/128)*n >= 768, for the down half
+                              when (H/256)*n >= 128 and (H/256)*(T*K/256 + E) <= 256;
+                              else the bf16 gate/up tile is 512 weight rows wide
                               once experts average 512 tokens (T*K >= 512*E, block_m 128,
                               I % 256 == 0); dense rows: TILE above 32
                               tokens (a gate/up grid, (I/128) x ceil(T/block), of fewer

@@ -257,21 +257,31 @@ bool span_shape_ok(moe_dtype dt, int E, int H, int I, int64_t T, int64_t act_row
   return dt == MOE_BF16 && moe::span_ok(E, H, I, T, act_rows);
 }
 
-// AUTO takes the span schedule for the gate/up half once experts average 256
-// tokens (T*K >= 256*E), and for the down half only while its items fit one
-// round of MI355X's 256 CUs ((H/256) x (T*K/256 + E) <= 256, a bound on the
-// spans).  Measured on MI355X: gate/up 708 vs 750 us (Mixtral-shaped, T=1024)
-// and 997 vs 1130 us (T=2048, against the 512-row tile); down 405 vs 439 us at
-// T=1024 but 774 vs 631 us at T=2048, where its 3.5x longer items (the I-long
-// contraction) leave a second, mostly idle round.  Below 256 tokens an expert
-// the 128-token tiles win (Qwen2-shaped, T=256: 398 vs 520 us).
+// AUTO takes the span schedule where its items fill the CUs several times over
+// (a span kernel's workgroups each take whole items, a weight tile's whole
+// contraction).  With n = ceil(T*K / 256), a lower bound on the spans:
+//   gate/up: experts average 256 tokens (T*K >= 256*E) and (I/128) * n >= 768
+//            items, three rounds of MI355X's 256 CUs;
+//   down:    the same average, (H/256) * n >= 128 and at most one round,
+//            (H/256) * (T*K/256 + E) <= 256: its items carry the I-long
+//            contraction (3.5x a gate/up item for Mixtral), so a second,
+//            mostly idle round of them costs more than the re-reads saved.
+// Measured on MI355X (us, tile -> span): Mixtral-shaped T=1024 gate/up 750 ->
+// 708, down 439 -> 405; T=2048 gate/up 1130 -> 997 (against the 512-row
+// tile), down 631 -> 774 (two rounds: left tiled); Qwen2-shaped T=2048
+// gate/up 876 -> 849; T=256 (32 tokens an expert) 398 -> 520; one
+// Mixtral-shaped expert at 256 tokens (112 gate/up and 16 down items) 329 ->
+// 509 for the pair, hence the item floors.
 bool span_auto_gate_up(moe_dtype dt, int64_t T, int K, int E, int H, int I, int64_t cap) {
-  return T * K >= (int64_t)256 * E && span_shape_ok(dt, E, H, I, T, cap);
+  const int64_t n = (T * K + 255) / 256;
+  return T * K >= (int64_t)256 * E && (int64_t)(I / 128) * n >= 768 &&
+         span_shape_ok(dt, E, H, I, T, cap);
 }
 
 bool span_auto_down(moe_dtype dt, int64_t T, int K, int E, int H, int I, int64_t cap) {
-  return T * K >= (int64_t)256 * E && (int64_t)(H / 256) * (T * K / 256 + E) <= 256 &&
-         span_shape_ok(dt, E, H, I, T, cap);
+  const int64_t n = (T * K + 255) / 256;
+  return T * K >= (int64_t)256 * E && (int64_t)(H / 256) * n >= 128 &&
+         (int64_t)(H / 256) * (T * K / 256 + E) <= 256 && span_shape_ok(dt, E, H, I, T, cap);
 }
 
 moe_status span_unsupported(const char* what) {

@@ -132,11 +132,11 @@ FULL_CASES = [
     ("qwen2", 32, "zipf", True),
     ("deepseek_v3", 128, "uniform", True),
     ("deepseek_v3", 128, "zipf", True),
-    ("mixtral", 1024, "uniform", False),
-    ("mixtral", 2048, "uniform", False),   # 512 tokens per expert: the 512-row gate/up tile
+    ("mixtral", 1024, "uniform", False),   # span schedule on both halves (one or two spans an expert)
+    ("mixtral", 2048, "uniform", False),   # span gate/up (two or three spans an expert), tiled down
     ("qwen2", 256, "zipf", False),
-    ("qwen2", 2048, "zipf", False),
-    ("mixtral", 4096, "uniform", False),   # 1024 tokens per expert: wide gate/up tile, 8 blocks each
+    ("qwen2", 2048, "zipf", False),        # span gate/up with skewed spans, tiled down
+    ("mixtral", 4096, "uniform", False),   # 1024 tokens per expert: four spans each, 8 blocks
     ("deepseek_v3", 4096, "zipf", False),  # 32 768 pairs over 256 experts, skewed, tiled at block 128
 ]
 
