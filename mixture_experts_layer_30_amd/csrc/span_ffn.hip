@@ -23,7 +23,12 @@
 // rows x 64 tokens with 16x16x32 bf16 MFMAs (32 accumulators).  Wavefront wn
 // takes the span's 16-token tiles wn, wn+4, wn+8, wn+12, so a short span
 // still spreads its tiles over the 4 token columns; tiles past the span's
-// tokens skip their matrix ops.  The contraction goes in steps of 32 (64-byte
+// tokens skip their matrix ops, and the token rows of 16-row groups past the
+// span's end are not loaded.  An expert of 257 to 384 tokens gets two spans
+// of equal length instead of 256 and a short rest, so that its items weigh the
+// same (measured on MI355X, Mixtral-shaped T=1024 gate/up: 773 -> 729 us;
+// equal spans for every split expert made T=2048 3% slower and skewed loads
+// slower, as each wavefront's busiest token column sets an item's time).  The contraction goes in steps of 32 (64-byte
 // rows: 32 KB a stage) through a 4-stage LDS ring filled by direct
 // global->LDS loads, three stages ahead of the matrix ops; a step's fragments
 // are read from LDS while the previous step's ops issue.
@@ -50,7 +55,6 @@ constexpr int kPST = 4;                     // stages
 constexpr int kPWaves = 8;
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPMaxE = kPThreads;           // experts the in-kernel scan covers
-constexpr int kPLoads = (kPRows + kPTok) * kPRow / 1024 / kPWaves;   // direct loads per wave per stage
 
 struct SpanSmem {
   uint8_t a[kPST][kPRows * kPRow];
@@ -149,12 +153,16 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
     }
     const int e = lo;
     const int n = dense ? (int)rm.dense_rows : __builtin_amdgcn_readfirstlane(rm.counts[e]);
+    // spans of 256 rows and a shorter last one; an expert of 257..384 rows gets
+    // two spans of equal length (within one row) instead, so that its items
+    // weigh about the same rather than one full and one near-empty
     const int spans = (n + kPTok - 1) / kPTok;
     const int l = it - __builtin_amdgcn_readfirstlane(sm.pre[e]);
     const int tile = l / spans, span = l - tile * spans;
+    const int slen = (spans == 2 && n <= 3 * kPTok / 2) ? (n + 1) / 2 : kPTok;
     const int row0 =
-        (dense ? 0 : __builtin_amdgcn_readfirstlane(rm.offsets[e])) + span * kPTok;
-    const int nvalid = min(kPTok, n - span * kPTok);
+        (dense ? 0 : __builtin_amdgcn_readfirstlane(rm.offsets[e])) + span * slen;
+    const int nvalid = min(slen, n - span * slen);
 
     __syncthreads();   // the previous item's epilogue has read dst[]
     if (tid < kPTok) {
@@ -195,14 +203,32 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
       boff[j] = (uint32_t)sm.tok[r] * (uint32_t)Kdim * 2u + (seg << 4);
     }
     const int nk = Kdim / 32;
-    auto issue = [&](int ks) {
+    // token loads of this wavefront that hold tokens (16-row groups 2w, 2w+1
+    // below the span's end); the others are skipped, and the ring's waits
+    // count the wavefront's own loads per stage, 2 + lb
+    // (a full span, nvalid == 256, takes the unconditional path: lb == 2)
+    const int lb = min(2, max(0, (nvalid + 15) / 16 - 2 * wave));
+    auto issue = [&](int ks, auto skip) {
       const int st = ks % kPST;
       const uint32_t kb = (uint32_t)ks * kPRow;
 #pragma unroll
       for (int j = 0; j < 2; ++j) span_load16(wexp + (aoff[j] + kb), &sm.a[st][(2 * wave + j) * 1024]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) span_load16(xb + (boff[j] + kb), &sm.b[st][(2 * wave + j) * 1024]);
+      for (int j = 0; j < 2; ++j)
+        if (!decltype(skip)::value || j < lb)
+          span_load16(xb + (boff[j] + kb), &sm.b[st][(2 * wave + j) * 1024]);
     };
+    // wait until at most S stages' loads of this wavefront are in flight
+    auto wait_stages = [&](auto S, auto skip) {
+      constexpr int n = decltype(S)::value;
+      if (!decltype(skip)::value || lb == 2) span_wait_vm<4 * n>();
+      else if (lb == 1) span_wait_vm<3 * n>();
+      else span_wait_vm<2 * n>();
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
 
     // this wavefront's live 16-token tiles: wn, wn + 4, ... below the span's tiles
     const int nt = (nvalid + 15) / 16;
@@ -239,12 +265,12 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
     // stage t's slot is free for stage t+4.  The steady form (t + 4 < nk) has
     // no conditions, so it is one basic block.
     auto body = [&](int t, u32x4 (&ca)[TM], u32x4 (&cb)[TN], u32x4 (&na)[TM], u32x4 (&nb)[TN],
-                    auto steady, auto masked) {
+                    auto steady, auto skip, auto masked) {
       if constexpr (decltype(steady)::value) {
-        span_wait_vm<2 * kPLoads>();
+        wait_stages(S2{}, skip);
         span_wait_lgkm0();
         span_barrier();
-        issue(t + 4);
+        issue(t + 4, skip);
         read((t + 1) % kPST, na, nb, masked);   // completes while the ops issue
         ops(ca, cb, masked);
         if constexpr (!decltype(masked)::value) {
@@ -252,7 +278,8 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
           // between each of the first ops, then the remaining ops -- and none of
           // the ops moved past the next barrier, whose wait for the reads would
           // then find the matrix pipe empty
-          __builtin_amdgcn_sched_group_barrier(0x020, kPLoads, 0);   // VMEM
+          if constexpr (!decltype(skip)::value)
+            __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);       // VMEM
 #pragma unroll
           for (int i = 0; i < TM + TN; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
@@ -262,43 +289,47 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        if (t + 3 < nk) span_wait_vm<2 * kPLoads>();
-        else if (t + 2 < nk) span_wait_vm<kPLoads>();
-        else span_wait_vm<0>();
+        if (t + 3 < nk) wait_stages(S2{}, skip);
+        else if (t + 2 < nk) wait_stages(S1{}, skip);
+        else wait_stages(S0{}, skip);
         span_wait_lgkm0();
         span_barrier();
-        if (t + 4 < nk) issue(t + 4);
+        if (t + 4 < nk) issue(t + 4, skip);
         if (t + 1 < nk) read((t + 1) % kPST, na, nb, masked);
         ops(ca, cb, masked);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    auto run = [&](auto masked) {
+    // skip: a partial span (its token loads limited to the groups holding
+    // tokens); masked: this wavefront has token tiles past the span's end
+    auto run = [&](auto skip, auto masked) {
       u32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 #pragma unroll
       for (int s0 = 0; s0 < kPST; ++s0)
-        if (s0 < nk) issue(s0);
+        if (s0 < nk) issue(s0, skip);
       // stage 0 landed (the stages issued after it may stay in flight)
-      if (nk >= 4) span_wait_vm<3 * kPLoads>();
-      else if (nk == 3) span_wait_vm<2 * kPLoads>();
-      else if (nk == 2) span_wait_vm<kPLoads>();
-      else span_wait_vm<0>();
+      if (nk >= 4) wait_stages(S3{}, skip);
+      else if (nk == 3) wait_stages(S2{}, skip);
+      else if (nk == 2) wait_stages(S1{}, skip);
+      else wait_stages(S0{}, skip);
       span_barrier();
       read(0, fa0, fb0, masked);
       int t = 0;
       for (; t + 5 < nk; t += 2) {
-        body(t, fa0, fb0, fa1, fb1, std::true_type{}, masked);
-        body(t + 1, fa1, fb1, fa0, fb0, std::true_type{}, masked);
+        body(t, fa0, fb0, fa1, fb1, std::true_type{}, skip, masked);
+        body(t + 1, fa1, fb1, fa0, fb0, std::true_type{}, skip, masked);
       }
       for (; t < nk; t += 2) {
-        body(t, fa0, fb0, fa1, fb1, std::false_type{}, masked);
-        if (t + 1 < nk) body(t + 1, fa1, fb1, fa0, fb0, std::false_type{}, masked);
+        body(t, fa0, fb0, fa1, fb1, std::false_type{}, skip, masked);
+        if (t + 1 < nk) body(t + 1, fa1, fb1, fa0, fb0, std::false_type{}, skip, masked);
       }
     };
-    if (tn_live == TN)
-      run(std::false_type{});
+    if (nt == kPTok / 16)   // every 16-row group holds tokens: nothing to skip
+      run(std::false_type{}, std::false_type{});
+    else if (tn_live == TN)
+      run(std::true_type{}, std::false_type{});
     else
-      run(std::true_type{});
+      run(std::true_type{}, std::true_type{});
 
     // epilogue: lane holds rows 4g..4g+3 of each 16-row tile for token column
     // m of each of its token tiles
