@@ -2,6 +2,7 @@
 // What each call computes is documented in include/moe_layer.h.
 #include "moe_layer.h"
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -200,6 +201,35 @@ int tile_splits(int64_t tiles, int64_t nb, int kdim, int64_t T) {
   return best;
 }
 
+// Contraction split of the grouped 256-row tile's down projection (bf16, block
+// 64 or 128): the rounds model above over the token blocks the experts hold,
+// estimated for even routing with a margin for its spread -- E_act =
+// min(E, T*K) experts of lambda + 2 sqrt(lambda) pairs each, lambda = T*K /
+// E_act -- with fp32 partial sums per pair (T*K rows) added by the finish
+// kernel.  Measured on MI355X (Mixtral-shaped, us): at T=128 (8 experts of
+// one 64-token block: 128 down items for 256 CUs) the down projection split
+// in 2 runs 177 against 210; the same split of gate/up ran 391 against 344
+// (its partial sums are 2I wide) and is not taken; at T=512 an estimate
+// without the margin split a down projection whose experts mostly hold two
+// blocks (301 against 283).
+struct TileSplit {
+  int gu, dn;
+  int64_t part_bytes;
+};
+
+TileSplit grouped_tile_split(int64_t T, int K, int E, int H, int I, int block_m) {
+  TileSplit t{1, 1, 0};
+  if ((block_m != 64 && block_m != 128) || H % 256 || I % 128 || T <= 0) return t;
+  const int64_t pairs = T * K;
+  const int64_t eact = pairs < E ? pairs : E;
+  const double lambda = (double)pairs / (double)eact;
+  const int64_t per = (int64_t)ceil(lambda + 2.0 * sqrt(lambda));
+  const int64_t nb = eact * ((per + block_m - 1) / block_m);
+  t.dn = tile_splits(H / 256, nb, I, pairs);
+  t.part_bytes = t.dn > 1 ? t.dn * pairs * H * 4 : 0;
+  return t;
+}
+
 DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   DensePlan p;
   p.tok_blocks = stream_tok_blocks(T);
@@ -372,7 +402,12 @@ int64_t moe_ffn_workspace_bytes(int64_t cap, int I) {
 int64_t moe_ffn_workspace_bytes_ex(int64_t cap, int64_t T, int K, int E, int H, int I) {
   if (cap < 0 || T < 0 || K < 1 || E < 1 || H < 1 || I < 1) return -1;
   const GroupedSplit g = grouped_split(T, K, E, H, I, 128);
-  return grouped_part_offset(cap, I) + g.part_bytes;
+  int64_t part = g.part_bytes;
+  for (int b : {64, 128}) {   // the tile's splits at either block the tiles take
+    const TileSplit t = grouped_tile_split(T, K, E, H, I, b);
+    part = t.part_bytes > part ? t.part_bytes : part;
+  }
+  return grouped_part_offset(cap, I) + part;
 }
 
 int64_t dense_ffn_workspace_bytes(int64_t T, int H, int I_fa) {
@@ -447,6 +482,16 @@ static moe_status check_grouped(const void* x, moe_dtype dt, int64_t T, int H, i
   return MOE_OK;
 }
 
+// The grouped tile's split for this call: bf16 only, and none when the
+// caller's workspace has no room for the partial sums.
+static TileSplit grouped_tile_split_for(moe_dtype dt, int64_t T, int K, int E, int H, int I,
+                                        const moe_plan* plan, int64_t workspace_bytes) {
+  TileSplit t = grouped_tile_split(T, K, E, H, I, plan->block_m);
+  if (dt != MOE_BF16 || workspace_bytes < grouped_part_offset(plan->cap, I) + t.part_bytes)
+    return TileSplit{1, 1, 0};
+  return t;
+}
+
 static moe::RowMap grouped_rows(const moe_plan* plan, int K) {
   moe::RowMap rm;
   rm.counts = plan->expert_counts;
@@ -493,9 +538,12 @@ moe_status moe_grouped_gate_up(const void* x, moe_dtype dt, int64_t T, int H, in
   } else if (use == MOE_SCHED_TILE && wide_gate_up(dt, T, K, E, plan->block_m, H, I))
     e = moe::launch_tile_gate_up_wide(x, w13, rm, plan->cap / plan->block_m, H, I,
                                       (uint16_t*)workspace, s);
-  else if (use == MOE_SCHED_TILE)
+  else if (use == MOE_SCHED_TILE) {
+    const TileSplit ts = grouped_tile_split_for(dt, T, K, E, H, I, plan, workspace_bytes);
+    float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
     e = moe::launch_tile_gate_up(x, dt, w13, rm, plan->cap / plan->block_m, H, I,
-                                 (uint16_t*)workspace, s);
+                                 (uint16_t*)workspace, s, ts.gu, part, T * K);
+  }
   else if (use == MOE_SCHED_RING) {
     // experts whose tokens fit one ring pass go to the ring kernel, busier ones
     // (possible only when T exceeds a pass) to the register-streaming kernel
@@ -545,9 +593,12 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
     if (!span_shape_ok(dt, E, H, I, T, plan->cap)) return span_unsupported("moe_grouped_down");
     e = moe::launch_span_down(w2, (const uint16_t*)workspace, rm, E, H, I, plan->cap, T * K,
                               y_pairs, dt, s);
-  } else if (use == MOE_SCHED_TILE)
+  } else if (use == MOE_SCHED_TILE) {
+    const TileSplit ts = grouped_tile_split_for(dt, T, K, E, H, I, plan, workspace_bytes);
+    float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
     e = moe::launch_tile_down(w2, dt, (const uint16_t*)workspace, rm, plan->cap / plan->block_m,
-                              H, I, y_pairs, dt, 1, nullptr, s);
+                              H, I, y_pairs, dt, ts.dn, part, s, T * K);
+  }
   else if (use == MOE_SCHED_RING) {
     const int nb = ring_tok_blocks(T, K, E);
     moe::RowMap cold = rm, hot = rm;

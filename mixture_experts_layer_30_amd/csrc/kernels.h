@@ -59,23 +59,25 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
                               float* part, hipStream_t s);
 
 // LDS-tiled MFMA schedule: one workgroup per (block_m-row token block, 128 weight rows).
-// ksplit > 1 (dense rows, bf16, I % 128 == 0 only): the contraction in slices whose
-// fp32 gate and up sums go to part [ksplit][rows][2I], the SwiGLU applied by the
-// finish kernel after adding them in slice order.
+// ksplit > 1 (bf16, I % 128 == 0 only): the contraction in slices whose fp32 gate and
+// up sums go to part [ksplit][rows][2I] -- rows the dense rows, or for grouped rows
+// the `pairs` (T*K) pairs, indexed by pair -- the SwiGLU applied by the finish kernel
+// after adding them in slice order (grouped: into each pair's alignment row).
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
                                int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s,
-                               int ksplit = 1, float* part = nullptr);
+                               int ksplit = 1, float* part = nullptr, int64_t pairs = 0);
 // The gate/up tile of 512 weight rows x 128 tokens for bf16 experts that hold
 // several 128-token blocks: block_m 128, I % 256 == 0, H % 32 == 0 and an
 // expert's gate/up matrix below 4 GB (tile_wide_ok); hipErrorInvalidValue else.
 bool tile_wide_ok(int block_m, int H, int I);
 hipError_t launch_tile_gate_up_wide(const void* x, const void* w13, const RowMap& rm,
                                     int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s);
-// ksplit > 1 (dense rows, bf16, H % 256 == 0 only) splits the contraction into
-// slices whose fp32 sums go to part [ksplit][rows][H], added in order by a finish kernel.
+// ksplit > 1 (bf16, H % 256 == 0 only) splits the contraction into slices whose
+// fp32 sums go to part [ksplit][rows][H] (rows: the dense rows, or the `pairs` pairs
+// of grouped rows), added in order by a finish kernel.
 hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
                             int64_t nblocks, int H, int I, void* y, int ydt, int ksplit,
-                            float* part, hipStream_t s);
+                            float* part, hipStream_t s, int64_t pairs = 0);
 
 // The tiled schedule with FP8 E4M3 weights and fp32 row scales (w13_scale
 // [E][2I], w2_scale [E][H]) and bf16 tokens; needs H % 256 == 0, I % 128 == 0 and

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
     const typename SW::T* __restrict__ w, const float* __restrict__ wscale,
     const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
     uint16_t* __restrict__ act, typename SY::T* __restrict__ y, int ntiles, int nblocks,
-    int ksplit, float* __restrict__ part) {
+    int ksplit, float* __restrict__ part, int64_t prows) {
   constexpr bool kF8 = SW::kBytes == 1;
   constexpr int AROW = kF8 ? 64 : kRowBytes;               // weight row bytes per step
   constexpr int ASEG = AROW / 16;                          // lanes per weight row in a direct load
@@ -330,6 +330,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
     if (kGateUp) {
       // (a block of padding rows only, as max padding makes, reads token 0)
       sm.tok[j] = dense ? row : (nvalid > 0 ? rm.sorted_ids[row] / rm.K : 0);
+      // partial sums of a split contraction go to the row's pair (grouped rows)
+      if (part) sm.dst[j] = dense ? row : rm.sorted_ids[row];
     } else {
       sm.tok[j] = row;
       sm.dst[j] = dense ? row : rm.sorted_ids[row];
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
             us = us * *reinterpret_cast<const f32x4*>(se + I + i);
           }
           if (part) {  // split contraction: this slice's fp32 sums, SwiGLU in the finish kernel
-            float* pr = part + ((size_t)zk * rm.dense_rows + row0 + j) * (2 * (size_t)I);
+            float* pr = part + ((size_t)zk * prows + sm.dst[j]) * (2 * (size_t)I);
             *reinterpret_cast<f32x4*>(pr + i) = gs;
             *reinterpret_cast<f32x4*>(pr + I + i) = us;
             continue;
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
           f32x4 v = acc[tm][tn];
           if constexpr (kF8) v = v * *reinterpret_cast<const f32x4*>(wscale + (size_t)e * H + h);
           if (part) {  // split contraction: fp32 slice, summed in slice order by the finish kernel
-            *reinterpret_cast<f32x4*>(part + ((size_t)zk * rm.dense_rows + sm.dst[j]) * H + h) = v;
+            *reinterpret_cast<f32x4*>(part + ((size_t)zk * prows + sm.dst[j]) * H + h) = v;
           } else {
             typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
             store_out4<SY>(o, v);
@@ -765,39 +767,60 @@ hipError_t launch_tile_gate_up_wide(const void* x, const void* w13, const RowMap
   return hipGetLastError();
 }
 
+// Rows of one slice of partial sums: the dense rows, or the pairs (T*K) of
+// grouped rows, whose partial sums are indexed by pair.
+static int64_t part_rows(const RowMap& rm, int64_t pairs) {
+  return rm.counts == nullptr ? rm.dense_rows : pairs;
+}
+
 template <int BN, class SW = BF16>
 static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
                        int I, uint16_t* act, hipStream_t s, const float* wscale = nullptr,
-                       int ksplit = 1, float* part = nullptr) {
+                       int ksplit = 1, float* part = nullptr, int64_t prows = 0) {
   const int ntiles = I / (kT2BM / 2);
   hipLaunchKernelGGL((tile2_ffn_kernel<SW, BF16, BN, true, MOE_TILE_WAVES>),
                      dim3(xcd_grid((int64_t)ksplit * ntiles * nblocks)),
                      dim3(MOE_TILE_WAVES * kWave), 0, s,
                      static_cast<const typename SW::T*>(w13), wscale,
                      static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr, ntiles,
-                     (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr);
+                     (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr, prows);
 }
 
 template <class SY, int BN, class SW = BF16>
 static void dn2_launch(const void* w2, const uint16_t* act, const RowMap& rm, int64_t nblocks,
                        int H, int I, void* y, int ksplit, float* part, hipStream_t s,
-                       const float* wscale = nullptr) {
+                       const float* wscale = nullptr, int64_t prows = 0) {
   const int ntiles = H / kT2BM;
   hipLaunchKernelGGL((tile2_ffn_kernel<SW, SY, BN, false, MOE_TILE_WAVES>),
                      dim3(xcd_grid((int64_t)ksplit * ntiles * nblocks)),
                      dim3(MOE_TILE_WAVES * kWave), 0, s, static_cast<const typename SW::T*>(w2),
                      wscale, act, rm, H, I, (uint16_t*)nullptr, static_cast<typename SY::T*>(y),
-                     ntiles, (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr);
+                     ntiles, (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr, prows);
+}
+
+// the finish of a split launch: slices added in order; grouped partial sums
+// (per pair) go to the pair's alignment row (gate/up) or pair row (down)
+static hipError_t finish_gu(const float* part, int ksplit, const RowMap& rm, int64_t prows, int I,
+                            uint16_t* act, hipStream_t s) {
+  return rm.counts == nullptr ? launch_finish_gate_up(part, ksplit, prows, I, act, s)
+                              : launch_finish_gate_up(part, ksplit, prows, I, act, s, rm.inv_pos);
+}
+
+static hipError_t finish_dn(const float* part, int ksplit, const RowMap& rm, int64_t prows, int H,
+                            void* y, int ydt, hipStream_t s) {
+  return rm.counts == nullptr ? launch_finish_down(part, ksplit, prows, H, y, ydt, s)
+                              : launch_finish_down(part, ksplit, prows, H, y, ydt, s, rm.inv_pos);
 }
 
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
                                int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s,
-                               int ksplit, float* part) {
+                               int ksplit, float* part, int64_t pairs) {
   if (xdt == kDtBF16 && I % (kT2BM / 2) == 0) {
-    if (rm.block_m == 256) gu2_launch<256>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part);
-    else if (rm.block_m == 128) gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part);
-    else gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part);
-    if (ksplit > 1) return launch_finish_gate_up(part, ksplit, rm.dense_rows, I, act, s);
+    const int64_t prows = part_rows(rm, pairs);
+    if (rm.block_m == 256) gu2_launch<256>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
+    else if (rm.block_m == 128) gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
+    else gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
+    if (ksplit > 1) return finish_gu(part, ksplit, rm, prows, I, act, s);
     return hipGetLastError();
   }
   if (rm.block_m == 64) {
@@ -819,19 +842,20 @@ static void dn_by_out(const void* w2, const uint16_t* act, const RowMap& rm, int
 
 hipError_t launch_tile_down(const void* w2, int wdt, const uint16_t* act, const RowMap& rm,
                             int64_t nblocks, int H, int I, void* y, int ydt, int ksplit,
-                            float* part, hipStream_t s) {
+                            float* part, hipStream_t s, int64_t pairs) {
   if (wdt == kDtBF16 && H % kT2BM == 0) {
+    const int64_t pr = part_rows(rm, pairs);
     if (rm.block_m == 256) {
-      if (ydt == kDtF32) dn2_launch<F32, 256>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
-      else dn2_launch<BF16, 256>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
+      if (ydt == kDtF32) dn2_launch<F32, 256>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, nullptr, pr);
+      else dn2_launch<BF16, 256>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, nullptr, pr);
     } else if (rm.block_m == 128) {
-      if (ydt == kDtF32) dn2_launch<F32, 128>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
-      else dn2_launch<BF16, 128>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
+      if (ydt == kDtF32) dn2_launch<F32, 128>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, nullptr, pr);
+      else dn2_launch<BF16, 128>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, nullptr, pr);
     } else {
-      if (ydt == kDtF32) dn2_launch<F32, 64>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
-      else dn2_launch<BF16, 64>(w2, act, rm, nblocks, H, I, y, ksplit, part, s);
+      if (ydt == kDtF32) dn2_launch<F32, 64>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, nullptr, pr);
+      else dn2_launch<BF16, 64>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, nullptr, pr);
     }
-    if (ksplit > 1) return launch_finish_down(part, ksplit, rm.dense_rows, H, y, ydt, s);
+    if (ksplit > 1) return finish_dn(part, ksplit, rm, pr, H, y, ydt, s);
     return hipGetLastError();
   }
   if (rm.block_m == 64) {
@@ -853,11 +877,11 @@ hipError_t launch_tile_gate_up_fp8(const void* x, const void* w13, const float* 
                                    const RowMap& rm, int64_t nblocks, int H, int I, uint16_t* act,
                                    hipStream_t s, int ksplit, float* part) {
   if (rm.block_m == 256)
-    gu2_launch<256, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part);
+    gu2_launch<256, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part, rm.dense_rows);
   else if (rm.block_m == 128)
-    gu2_launch<128, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part);
+    gu2_launch<128, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part, rm.dense_rows);
   else
-    gu2_launch<64, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part);
+    gu2_launch<64, FP8>(x, w13, rm, nblocks, H, I, act, s, w13_scale, ksplit, part, rm.dense_rows);
   if (ksplit > 1) return launch_finish_gate_up(part, ksplit, rm.dense_rows, I, act, s);
   return hipGetLastError();
 }
@@ -868,9 +892,11 @@ hipError_t launch_tile_down_fp8(const void* w2, const float* w2_scale, const uin
   auto go = [&](auto bn) {
     constexpr int BN = decltype(bn)::value;
     if (ydt == kDtF32)
-      dn2_launch<F32, BN, FP8>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, w2_scale);
+      dn2_launch<F32, BN, FP8>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, w2_scale,
+                               rm.dense_rows);
     else
-      dn2_launch<BF16, BN, FP8>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, w2_scale);
+      dn2_launch<BF16, BN, FP8>(w2, act, rm, nblocks, H, I, y, ksplit, part, s, w2_scale,
+                                rm.dense_rows);
   };
   if (rm.block_m == 256) go(std::integral_constant<int, 256>{});
   else if (rm.block_m == 128) go(std::integral_constant<int, 128>{});

@@ -140,6 +140,9 @@ VAR_K_CASES = [
     # few experts: the ring launches split their contraction, the finish kernels skip unused pairs
     (LayerShape("vark_split", 2048, 1024, 4, 2, 0, "bf16", (5,), ("uniform",)), 5, [0, 1, 2],
      B.SCHED_AUTO, None),
+    # the grouped tile's contraction split with unused slots
+    (LayerShape("vark_tile_split", 1024, 1024, 8, 4, 0, "bf16", (60,), ("uniform",)), 60,
+     [0, 1, 2, 4], B.SCHED_TILE, 64),
 ]
 
 
@@ -421,6 +424,10 @@ TILE_SHAPES = [
     # experts averaging >= 512 tokens: the 512-row gate/up tile (two column tiles), ragged blocks
     (LayerShape("tile_wide", 256, 512, 4, 2, 0, "bf16", (1100,), ("zipf",)), 1100, "zipf", 128),
     (LayerShape("tile_wide_u", 512, 256, 4, 1, 256, "bf16", (2100,), ("uniform",)), 2100, "uniform", 128),
+    # few token blocks for the CUs: the grouped tile splits its contraction (fp32 partial
+    # sums per pair, added in slice order by the finish kernels)
+    (LayerShape("tile_split", 1024, 1024, 8, 2, 0, "bf16", (100,), ("uniform",)), 100, "uniform", 64),
+    (LayerShape("tile_split_zipf", 1024, 1024, 16, 4, 512, "bf16", (90,), ("zipf",)), 90, "zipf", 128),
 ]
 
 
