@@ -403,9 +403,13 @@ int64_t moe_ffn_workspace_bytes_ex(int64_t cap, int64_t T, int K, int E, int H, 
   if (cap < 0 || T < 0 || K < 1 || E < 1 || H < 1 || I < 1) return -1;
   const GroupedSplit g = grouped_split(T, K, E, H, I, 128);
   int64_t part = g.part_bytes;
-  for (int b : {64, 128}) {   // the tile's splits at either block the tiles take
-    const TileSplit t = grouped_tile_split(T, K, E, H, I, b);
-    part = t.part_bytes > part ? t.part_bytes : part;
+  // the tiled down projection's split where AUTO tiles (at either block the
+  // tiles take); a call with a smaller workspace runs unsplit
+  if (T > 32 && T * K >= kTileFrom * (int64_t)E) {
+    for (int b : {64, 128}) {
+      const TileSplit t = grouped_tile_split(T, K, E, H, I, b);
+      part = t.part_bytes > part ? t.part_bytes : part;
+    }
   }
   return grouped_part_offset(cap, I) + part;
 }

@@ -427,7 +427,7 @@ TILE_SHAPES = [
     # few token blocks for the CUs: the grouped tile splits its contraction (fp32 partial
     # sums per pair, added in slice order by the finish kernels)
     (LayerShape("tile_split", 1024, 1024, 8, 2, 0, "bf16", (100,), ("uniform",)), 100, "uniform", 64),
-    (LayerShape("tile_split_zipf", 1024, 1024, 16, 4, 512, "bf16", (90,), ("zipf",)), 90, "zipf", 128),
+    (LayerShape("tile_split_zipf", 1024, 1024, 16, 4, 512, "bf16", (100,), ("zipf",)), 100, "zipf", 128),
 ]
 
 
