@@ -132,6 +132,7 @@ FULL_CASES = [
     ("qwen2", 32, "zipf", True),
     ("deepseek_v3", 128, "uniform", True),
     ("deepseek_v3", 128, "zipf", True),
+    ("mixtral", 128, "uniform", True),     # 64-token tiles, the down projection's contraction split
     ("mixtral", 1024, "uniform", False),   # span schedule on both halves (one or two spans an expert)
     ("mixtral", 2048, "uniform", False),   # span gate/up (two or three spans an expert), tiled down
     ("qwen2", 256, "zipf", False),
