@@ -825,12 +825,15 @@ hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const Ro
     const int64_t prows = part_rows(rm, pairs);
     if (rm.block_m == 256) gu2_launch<256>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
     else if (rm.block_m == 128) gu2_launch<128>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
-    // grouped 64-token blocks (mid-size batches, HBM-bound): 128-row tiles, whose
-    // 24 KB stages keep five in flight where the 256-row tile's 40 KB keep two.
-    // Measured on MI355X (us, 256 -> 128 rows): Mixtral-shaped T=96 gate/up
-    // 369 -> 356, T=128 346 -> 340, DeepSeek-V3 T=128 Zipf busy experts' launch
-    // within the gate/up 644 -> 634; as the down projection 1-4.5% slower
-    else if (rm.counts) gu2_launch<64, BF16, 128>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
+    // grouped 64-token blocks of every expert (mid-size batches, HBM-bound):
+    // 128-row tiles, whose 24 KB stages keep five in flight where the 256-row
+    // tile's 40 KB keep two.  Measured on MI355X (us, 256 -> 128 rows):
+    // Mixtral-shaped T=96 gate/up 369 -> 356, T=128 346 -> 340; as the down
+    // projection 1-4.5% slower.  Not for the launch of the busy experts only
+    // (min_rows > 1), which is empty under even routing and then costs its
+    // grid's dispatch: twice the workgroups measured 18.8 against 11.1 us
+    else if (rm.counts && rm.min_rows <= 1)
+      gu2_launch<64, BF16, 128>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
     else gu2_launch<64>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);
     if (ksplit > 1) return finish_gu(part, ksplit, rm, prows, I, act, s);
     return hipGetLastError();
