@@ -158,6 +158,7 @@ struct DensePlan {
   int tok_blocks, split_gu, split_dn;  // streaming schedule
   int tile_block, tile_split;          // tiled schedule: token block and down-projection split
   int tile_split_gu;                   // and gate/up split
+  int tile_full_gu, tile_tail_gu;      // gate/up in 128-row tiles: whole tiles, tail split
   bool ring_gu, ring_dn;               // LDS-ring streaming applies to the half
   int ring_split_gu, ring_split_dn;    // and the contraction split it uses
   int64_t act_bytes, part_bytes;
@@ -230,6 +231,49 @@ TileSplit grouped_tile_split(int64_t T, int K, int E, int H, int I, int block_m)
   return t;
 }
 
+// Modelled time of tile_splits' choice s for `tiles` output tiles (one token
+// block), in units of one unsplit 256-row tile
+double tile_split_cost(int64_t tiles, int s, int kdim, int64_t T) {
+  double c = (double)((tiles * s + 255) / 256) * (1.0 / s + 192.0 / kdim);
+  if (s > 1) c += 4.0 * s * (double)T / kdim * (double)tiles / 256.0;
+  return c;
+}
+
+// Gate/up of dense rows in one 128-token block in 128-row tiles (n = I/64 of
+// them): the first nfull = 256 floor(n/256) whole, in full rounds of the CUs,
+// and the remaining r tiles' contraction split s ways to fill the last round,
+// their fp32 partial sums (s x T x 128 columns each) added by the finish
+// kernel.  In the units above a 128-row tile weighs 1/2:
+//   0.5 [nfull/256 (1 + f) + rounds(r s) (1/s + f)] + [s > 1] 0.5 * 4 s T/H * r/256,
+// f = 192/H the pipeline fill; s in 1..H/512.  Taken where it beats the uniform
+// split of 256-row tiles.  Measured on MI355X (DeepSeek-V3-shaped DenseFA, 128
+// tokens: 288 tiles = 256 whole + 32 split 8 ways, in place of 144 tiles of 256
+// rows split 3 ways into 432 workgroups).
+struct TailPlan {
+  int nfull, s;
+  double cost;
+};
+
+TailPlan dense_tail_split(int64_t T, int H, int I) {
+  TailPlan t{0, 1, 1e30};
+  if (T > 128 || I % 64 || H % 64) return t;
+  const int64_t n = I / 64;
+  const int64_t nfull = n / 256 * 256, r = n - nfull;
+  if (nfull == 0 || r == 0) return t;
+  const double f = 192.0 / H;
+  const int most = H / 64 / 8 > 1 ? H / 64 / 8 : 1;
+  for (int s = 1; s <= most; ++s) {
+    double c = 0.5 * ((double)nfull / 256 * (1 + f) + (double)((r * s + 255) / 256) * (1.0 / s + f));
+    if (s > 1) c += 0.5 * 4.0 * s * (double)T / H * (double)r / 256.0;
+    if (c < t.cost) {
+      t.nfull = (int)nfull;
+      t.s = s;
+      t.cost = c;
+    }
+  }
+  return t;
+}
+
 DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   DensePlan p;
   p.tok_blocks = stream_tok_blocks(T);
@@ -243,10 +287,17 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   p.tile_block = (tile2 && T > 128) ? 256 : 128;
   p.tile_split = 1;
   p.tile_split_gu = 1;
+  p.tile_full_gu = 0;
+  p.tile_tail_gu = 1;
   if (tile2) {
     const int64_t nb = (T + p.tile_block - 1) / p.tile_block;
     p.tile_split = tile_splits(H / 256, nb, I, T);
     p.tile_split_gu = tile_splits(I / 128, nb, H, T);
+    const TailPlan tp = dense_tail_split(T, H, I);
+    if (nb == 1 && tp.nfull > 0 && tp.cost < tile_split_cost(I / 128, p.tile_split_gu, H, T)) {
+      p.tile_full_gu = tp.nfull;
+      p.tile_tail_gu = tp.s;
+    }
   }
   p.ring_gu = moe::ring_gate_up_ok(dt, dt, H, I);
   p.ring_dn = moe::ring_down_ok(dt, H, I);
@@ -254,12 +305,15 @@ DensePlan dense_plan(int64_t T, int H, int I, int dt) {
   p.ring_split_dn = p.ring_dn ? moe::ring_down_splits(T, H, I) : 1;
   p.act_bytes = round_up(round_up(T, 128) * (int64_t)I * 2, 256);
   // partial sums of whichever split schedule runs: the largest of them
-  const int64_t cand[6] = {p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0,
+  const int64_t cand[7] = {p.split_gu > 1 ? (int64_t)p.split_gu * T * 2 * I * 4 : 0,
                            p.split_dn > 1 ? (int64_t)p.split_dn * T * H * 4 : 0,
                            p.tile_split > 1 ? (int64_t)p.tile_split * T * H * 4 : 0,
                            p.tile_split_gu > 1 ? (int64_t)p.tile_split_gu * T * 2 * I * 4 : 0,
                            p.ring_split_gu > 1 ? (int64_t)p.ring_split_gu * T * 2 * I * 4 : 0,
-                           p.ring_split_dn > 1 ? (int64_t)p.ring_split_dn * T * H * 4 : 0};
+                           p.ring_split_dn > 1 ? (int64_t)p.ring_split_dn * T * H * 4 : 0,
+                           p.tile_full_gu > 0 && p.tile_tail_gu > 1
+                               ? (int64_t)p.tile_tail_gu * T * 2 * (I - 64 * (int64_t)p.tile_full_gu) * 4
+                               : 0};
   p.part_bytes = 0;
   for (int64_t c : cand) p.part_bytes = c > p.part_bytes ? c : p.part_bytes;
   return p;
@@ -697,8 +751,11 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
     float* part = (float*)((char*)workspace + dp.act_bytes);
     rm.block_m = dp.tile_block;
     const int64_t nblocks = (T + rm.block_m - 1) / rm.block_m;
-    hipError_t e = moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s,
-                                            dp.tile_split_gu, part);
+    hipError_t e = dp.tile_full_gu > 0
+                       ? moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s,
+                                                  dp.tile_tail_gu, part, 0, dp.tile_full_gu)
+                       : moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s,
+                                                  dp.tile_split_gu, part);
     if (e != hipSuccess) return hip_status(e, "dense_ffn_fa gate/up");
     e = moe::launch_tile_down(w2, dt, act, rm, nblocks, H, I_fa, out, odt, dp.tile_split, part, s);
     return hip_status(e, "dense_ffn_fa down");

@@ -63,9 +63,14 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
 // up sums go to part [ksplit][rows][2I] -- rows the dense rows, or for grouped rows
 // the `pairs` (T*K) pairs, indexed by pair -- the SwiGLU applied by the finish kernel
 // after adding them in slice order (grouped: into each pair's alignment row).
+// nfull > 0 (bf16 dense rows in one 128-token block, I % 64 == 0, nfull < I/64):
+// 128-row tiles, tiles 0..nfull-1 whole and each later tile's contraction in ksplit
+// slices, whose sums go to part [ksplit][rows][2 (I - 64 nfull)] (columns from
+// 64 nfull: gate, then up); hipErrorInvalidValue for other shapes.
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
                                int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s,
-                               int ksplit = 1, float* part = nullptr, int64_t pairs = 0);
+                               int ksplit = 1, float* part = nullptr, int64_t pairs = 0,
+                               int nfull = 0);
 // The gate/up tile of 512 weight rows x 128 tokens for bf16 experts that hold
 // several 128-token blocks: block_m 128, I % 256 == 0, H % 32 == 0 and an
 // expert's gate/up matrix below 4 GB (tile_wide_ok); hipErrorInvalidValue else.
@@ -106,11 +111,12 @@ hipError_t launch_span_down(const void* w2, const uint16_t* act, const RowMap& r
                             int I, int64_t act_rows, int64_t rows_bound, void* y, int ydt,
                             hipStream_t s);
 
-// act[o][i] = silu(g) * u with g, u the in-order sums over z < splits of
-// part[z][r][i] and part[z][r][I + i], o = out_row[r] (r when out_row is null;
-// rows with out_row[r] < 0 are skipped).
+// act[o][col0 + i] = silu(g) * u for i < W = I - col0, with g, u the in-order sums
+// over z < splits of part[z][r][i] and part[z][r][W + i], o = out_row[r] (r when
+// out_row is null; rows with out_row[r] < 0 are skipped).
 hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, int I,
-                                 uint16_t* act, hipStream_t s, const int32_t* out_row = nullptr);
+                                 uint16_t* act, hipStream_t s, const int32_t* out_row = nullptr,
+                                 int col0 = 0);
 
 // y[r][h] = sum over z < splits (in order) of part[z][r][h], rounded to ydt
 // (rows with skip[r] < 0 left untouched when skip is not null).

@@ -312,23 +312,26 @@ __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void str
 }
 
 // Split-K finish (dense rows only): sums the gridDim.z slices in slice order.
+// (gate/up: the partial sums cover columns col0.. of I, W = I - col0 of each)
 __global__ __launch_bounds__(256) void finish_gate_up_kernel(const float* __restrict__ part,
                                                              int splits, int64_t rows, int I,
+                                                             int col0,
                                                              uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ out_row) {
+  const int W = I - col0;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * I) return;
-  const int64_t r = idx / I;
-  const int i = (int)(idx % I);
+  if (idx >= rows * W) return;
+  const int64_t r = idx / W;
+  const int i = (int)(idx % W);
   const int64_t o = out_row ? out_row[r] : r;
   if (o < 0) return;
   float g = 0.f, u = 0.f;
   for (int z = 0; z < splits; ++z) {
-    const float* pr = part + ((size_t)z * rows + r) * (2 * (size_t)I);
+    const float* pr = part + ((size_t)z * rows + r) * (2 * (size_t)W);
     g += pr[i];
-    u += pr[I + i];
+    u += pr[W + i];
   }
-  act[o * I + i] = f32_to_bf16(silu(g) * u);
+  act[o * I + col0 + i] = f32_to_bf16(silu(g) * u);
 }
 
 template <class SY>
@@ -412,11 +415,11 @@ hipError_t launch_stream_down(const void* w2, int wdt, const uint16_t* act, cons
 }
 
 hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, int I,
-                                 uint16_t* act, hipStream_t s, const int32_t* out_row) {
-  const int64_t n = rows * I;
+                                 uint16_t* act, hipStream_t s, const int32_t* out_row, int col0) {
+  const int64_t n = rows * (I - col0);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(finish_gate_up_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     part, splits, rows, I, act, out_row);
+                     part, splits, rows, I, col0, act, out_row);
   return hipGetLastError();
 }
 

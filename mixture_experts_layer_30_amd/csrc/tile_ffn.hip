@@ -286,7 +286,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
     const typename SW::T* __restrict__ w, const float* __restrict__ wscale,
     const uint16_t* __restrict__ xs, RowMap rm, int H, int I,
     uint16_t* __restrict__ act, typename SY::T* __restrict__ y, int ntiles, int nblocks,
-    int ksplit, float* __restrict__ part, int64_t prows) {
+    int ksplit, float* __restrict__ part, int64_t prows, int nfull) {
   constexpr bool kF8 = SW::kBytes == 1;
   constexpr int AROW = kF8 ? 64 : kRowBytes;               // weight row bytes per step
   constexpr int ASEG = AROW / 16;                          // lanes per weight row in a direct load
@@ -301,14 +301,39 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   static_assert(BInst >= 1 && kLoads * (ST - 1) < 64, "load counts");
   static_assert(AInst >= 1 && TM >= 2 && TM % 2 == 0, "tile rows");
   __shared__ Tile2Smem<BN, ST, AROW, BM> sm;
-  // XCD-aware work item: XCD b % 8 takes items [xcd * per, (xcd + 1) * per)
-  const int per = (int)(gridDim.x / 8);
-  const int item0 = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-  if (item0 >= ksplit * ntiles * nblocks) return;
-  const int zk = item0 / (ntiles * nblocks);   // slice of a split contraction (dense rows only)
-  const int item = item0 % (ntiles * nblocks);
-  const int tile = item / nblocks;
-  const int blk = item % nblocks;
+  int zk, tile, blk, slices;
+  if (nfull > 0) {
+    // one block of dense rows: tiles 0..nfull-1 whole (the first workgroups,
+    // dispatched first: full rounds of the CUs), then each later tile's
+    // contraction in ksplit slices, which fill the last round
+    const int item0 = (int)blockIdx.x;
+    blk = 0;
+    if (item0 < nfull) {
+      tile = item0;
+      zk = 0;
+      slices = 1;
+    } else {
+      const int r = item0 - nfull;
+      if (r >= (ntiles - nfull) * ksplit) return;
+      tile = nfull + r / ksplit;
+      zk = r % ksplit;
+      slices = ksplit;
+    }
+  } else {
+    // XCD-aware work item: XCD b % 8 takes items [xcd * per, (xcd + 1) * per)
+    const int per = (int)(gridDim.x / 8);
+    const int item0 = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (item0 >= ksplit * ntiles * nblocks) return;
+    zk = item0 / (ntiles * nblocks);   // slice of a split contraction (dense rows only)
+    const int item = item0 % (ntiles * nblocks);
+    tile = item / nblocks;
+    blk = item % nblocks;
+    slices = ksplit;
+  }
+  // split items write fp32 partial sums of the tiles past the whole ones: the
+  // gate/up columns from c0 = nfull * BM / 2 (2 (I - c0) a row: gate, then up),
+  // the down features from h0 = nfull * BM (H - h0 a row)
+  float* const psum = slices > 1 ? part : nullptr;
   const bool dense = rm.counts == nullptr;
   int e, row0, nvalid;
   if (dense) {
@@ -377,8 +402,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
 
   // this workgroup's steps [k0, k0 + nk) of the contraction
   const int nk_all = Kdim / kBK;
-  const int k0 = zk * nk_all / ksplit;
-  const int nk = (zk + 1) * nk_all / ksplit - k0;
+  const int k0 = zk * nk_all / slices;
+  const int nk = (zk + 1) * nk_all / slices - k0;
   auto issue = [&](int ks) {
     const int st = ks % ST;
     const size_t kb = (size_t)(k0 + ks) * kRowBytes;
@@ -494,10 +519,11 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
             gs = gs * *reinterpret_cast<const f32x4*>(se + i);
             us = us * *reinterpret_cast<const f32x4*>(se + I + i);
           }
-          if (part) {  // split contraction: this slice's fp32 sums, SwiGLU in the finish kernel
-            float* pr = part + ((size_t)zk * prows + sm.dst[j]) * (2 * (size_t)I);
-            *reinterpret_cast<f32x4*>(pr + i) = gs;
-            *reinterpret_cast<f32x4*>(pr + I + i) = us;
+          if (psum) {  // split contraction: this slice's fp32 sums, SwiGLU in the finish kernel
+            const int c0 = nfull * (BM / 2), wt = I - c0;
+            float* pr = psum + ((size_t)zk * prows + sm.dst[j]) * (2 * (size_t)wt);
+            *reinterpret_cast<f32x4*>(pr + (i - c0)) = gs;
+            *reinterpret_cast<f32x4*>(pr + wt + (i - c0)) = us;
             continue;
           }
           uint2 v;
@@ -516,8 +542,10 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
           const int h = i0 + wm * (TM * 16) + tm * 16 + 4 * g;
           f32x4 v = acc[tm][tn];
           if constexpr (kF8) v = v * *reinterpret_cast<const f32x4*>(wscale + (size_t)e * H + h);
-          if (part) {  // split contraction: fp32 slice, summed in slice order by the finish kernel
-            *reinterpret_cast<f32x4*>(part + ((size_t)zk * prows + sm.dst[j]) * H + h) = v;
+          if (psum) {  // split contraction: fp32 slice, summed in slice order by the finish kernel
+            const int h0 = nfull * BM;
+            *reinterpret_cast<f32x4*>(psum + ((size_t)zk * prows + sm.dst[j]) * (H - h0) +
+                                      (h - h0)) = v;
           } else {
             typename SY::T* o = y + (size_t)sm.dst[j] * H + h;
             store_out4<SY>(o, v);
@@ -779,17 +807,24 @@ static int64_t part_rows(const RowMap& rm, int64_t pairs) {
   return rm.counts == nullptr ? rm.dense_rows : pairs;
 }
 
+// Workgroups of a launch: with nfull whole tiles (one block of dense rows),
+// nfull + (ntiles - nfull) * ksplit in order; else the XCD-aware grid
+static unsigned tile2_grid(int ntiles, int64_t nblocks, int ksplit, int nfull) {
+  if (nfull > 0) return (unsigned)(nfull + (int64_t)(ntiles - nfull) * ksplit);
+  return xcd_grid((int64_t)ksplit * ntiles * nblocks);
+}
+
 template <int BN, class SW = BF16, int BM = kT2BM>
 static void gu2_launch(const void* x, const void* w13, const RowMap& rm, int64_t nblocks, int H,
                        int I, uint16_t* act, hipStream_t s, const float* wscale = nullptr,
-                       int ksplit = 1, float* part = nullptr, int64_t prows = 0) {
+                       int ksplit = 1, float* part = nullptr, int64_t prows = 0, int nfull = 0) {
   const int ntiles = I / (BM / 2);
   hipLaunchKernelGGL((tile2_ffn_kernel<SW, BF16, BN, true, MOE_TILE_WAVES, BM>),
-                     dim3(xcd_grid((int64_t)ksplit * ntiles * nblocks)),
+                     dim3(tile2_grid(ntiles, nblocks, ksplit, nfull)),
                      dim3(MOE_TILE_WAVES * kWave), 0, s,
                      static_cast<const typename SW::T*>(w13), wscale,
                      static_cast<const uint16_t*>(x), rm, H, I, act, (uint16_t*)nullptr, ntiles,
-                     (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr, prows);
+                     (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr, prows, nfull);
 }
 
 template <class SY, int BN, class SW = BF16, int BM = kT2BM>
@@ -798,10 +833,10 @@ static void dn2_launch(const void* w2, const uint16_t* act, const RowMap& rm, in
                        const float* wscale = nullptr, int64_t prows = 0) {
   const int ntiles = H / BM;
   hipLaunchKernelGGL((tile2_ffn_kernel<SW, SY, BN, false, MOE_TILE_WAVES, BM>),
-                     dim3(xcd_grid((int64_t)ksplit * ntiles * nblocks)),
+                     dim3(tile2_grid(ntiles, nblocks, ksplit, 0)),
                      dim3(MOE_TILE_WAVES * kWave), 0, s, static_cast<const typename SW::T*>(w2),
                      wscale, act, rm, H, I, (uint16_t*)nullptr, static_cast<typename SY::T*>(y),
-                     ntiles, (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr, prows);
+                     ntiles, (int)nblocks, ksplit, ksplit > 1 ? part : (float*)nullptr, prows, 0);
 }
 
 // the finish of a split launch: slices added in order; grouped partial sums
@@ -820,7 +855,17 @@ static hipError_t finish_dn(const float* part, int ksplit, const RowMap& rm, int
 
 hipError_t launch_tile_gate_up(const void* x, int xdt, const void* w13, const RowMap& rm,
                                int64_t nblocks, int H, int I, uint16_t* act, hipStream_t s,
-                               int ksplit, float* part, int64_t pairs) {
+                               int ksplit, float* part, int64_t pairs, int nfull) {
+  if (nfull > 0) {   // one block of dense rows, 128-row tiles, the last round split
+    if (xdt != kDtBF16 || rm.counts != nullptr || rm.block_m != 128 || nblocks != 1 ||
+        I % 64 != 0 || nfull >= I / 64 || (ksplit > 1 && part == nullptr))
+      return hipErrorInvalidValue;
+    gu2_launch<128, BF16, 128>(x, w13, rm, 1, H, I, act, s, nullptr, ksplit, part,
+                               rm.dense_rows, nfull);
+    if (ksplit > 1) return launch_finish_gate_up(part, ksplit, rm.dense_rows, I, act, s, nullptr,
+                                                 nfull * 64);
+    return hipGetLastError();
+  }
   if (xdt == kDtBF16 && I % (kT2BM / 2) == 0) {
     const int64_t prows = part_rows(rm, pairs);
     if (rm.block_m == 256) gu2_launch<256>(x, w13, rm, nblocks, H, I, act, s, nullptr, ksplit, part, prows);

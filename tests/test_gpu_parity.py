@@ -323,6 +323,10 @@ DENSE_TILE_CASES = [
     (70, 2816, 256),
     (128, 7168, 2048),
     (40, 2048, 18432),
+    # gate/up in 128-row tiles, 256 whole and the rest split: 16 tiles in 2 slices (a
+    # ragged 100-token block), 8 tiles in 8 slices
+    (100, 1024, 17408),
+    (40, 4096, 16896),
 ]
 
 

@@ -176,6 +176,27 @@ def test_layer_parity_full_size(name, T, routing, decode):
     torch.cuda.empty_cache()
 
 
+# DenseFA (I_fa = K*I + I_s) on its own, every token: the DeepSeek-V3 shape at 128 tokens
+# (tiled, both contractions split), the Mixtral sweep's 8 tokens and Qwen2's 32 tokens
+# (LDS ring, contractions split by the ring's rounds model)
+@pytest.mark.parametrize("name,T", [("deepseek_v3", 128), ("mixtral_sweep", 8), ("qwen2", 32)])
+def test_dense_fa_full_size(name, T):
+    shape = configs.CONFIGS[name]
+    print(f"\n[full-size DenseFA parity] {name} T={T}", flush=True)
+    x = synth.tokens(T, shape.hidden, "bf16", seed=T + 5, device=DEV)
+    w13, w2 = synth.swiglu_weights(shape.dense_fa_inter, shape.hidden, "bf16", seed=6,
+                                   device=DEV)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(T, shape.hidden, shape.dense_fa_inter),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, shape.hidden, dtype=torch.bfloat16, device=DEV)
+    B.dense_ffn_fa(x, w13, w2, ws, out)
+    torch.cuda.synchronize()
+    ref = oracle.dense_ffn(x.cpu(), w13.cpu(), w2.cpu())
+    assert rel_err(out, ref) <= TOL
+    del w13, w2, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,T,routing,levels", [("qwen2", 32, "zipf", [0, 2, 4, 8]),
                                                    ("deepseek_v3", 128, "uniform", [2, 4, 6, 8])])
 def test_layer_parity_var_k_full_size(name, T, routing, levels):
