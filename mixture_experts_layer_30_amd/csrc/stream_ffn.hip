@@ -311,40 +311,62 @@ __global__ __launch_bounds__(kStreamThreads, MOE_STREAM_WAVES_PER_SIMD) void str
   }
 }
 
-// Split-K finish (dense rows only): sums the gridDim.z slices in slice order.
+// Split-K finish: sums the slices in slice order, V consecutive elements a
+// thread (4 where the row length allows: 16-byte loads of the partial sums).
 // (gate/up: the partial sums cover columns col0.. of I, W = I - col0 of each)
+template <int V>
 __global__ __launch_bounds__(256) void finish_gate_up_kernel(const float* __restrict__ part,
                                                              int splits, int64_t rows, int I,
                                                              int col0,
                                                              uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ out_row) {
   const int W = I - col0;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (idx >= rows * W) return;
   const int64_t r = idx / W;
   const int i = (int)(idx % W);
   const int64_t o = out_row ? out_row[r] : r;
   if (o < 0) return;
-  float g = 0.f, u = 0.f;
-  for (int z = 0; z < splits; ++z) {
-    const float* pr = part + ((size_t)z * rows + r) * (2 * (size_t)W);
-    g += pr[i];
-    u += pr[W + i];
+  if constexpr (V == 4) {
+    f32x4 g = f32x4{0.f, 0.f, 0.f, 0.f}, u = g;
+    for (int z = 0; z < splits; ++z) {
+      const float* pr = part + ((size_t)z * rows + r) * (2 * (size_t)W);
+      g += *reinterpret_cast<const f32x4*>(pr + i);
+      u += *reinterpret_cast<const f32x4*>(pr + W + i);
+    }
+    uint2 v;
+    v.x = pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y);
+    v.y = pack_bf16x2(silu(g.z) * u.z, silu(g.w) * u.w);
+    *reinterpret_cast<uint2*>(act + o * I + col0 + i) = v;
+  } else {
+    float g = 0.f, u = 0.f;
+    for (int z = 0; z < splits; ++z) {
+      const float* pr = part + ((size_t)z * rows + r) * (2 * (size_t)W);
+      g += pr[i];
+      u += pr[W + i];
+    }
+    act[o * I + col0 + i] = f32_to_bf16(silu(g) * u);
   }
-  act[o * I + col0 + i] = f32_to_bf16(silu(g) * u);
 }
 
-template <class SY>
+template <class SY, int V>
 __global__ __launch_bounds__(256) void finish_down_kernel(const float* __restrict__ part,
                                                           int splits, int64_t rows, int H,
                                                           typename SY::T* __restrict__ y,
                                                           const int32_t* __restrict__ skip) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (idx >= rows * H) return;
   if (skip && skip[idx / H] < 0) return;
-  float s = 0.f;
-  for (int z = 0; z < splits; ++z) s += part[(size_t)z * rows * H + idx];
-  store_out<SY>(y + idx, s);
+  if constexpr (V == 4) {
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < splits; ++z)
+      s += *reinterpret_cast<const f32x4*>(part + (size_t)z * rows * H + idx);
+    store_out4<SY>(y + idx, s);
+  } else {
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += part[(size_t)z * rows * H + idx];
+    store_out<SY>(y + idx, s);
+  }
 }
 
 template <class S, int TB>
@@ -418,8 +440,12 @@ hipError_t launch_finish_gate_up(const float* part, int splits, int64_t rows, in
                                  uint16_t* act, hipStream_t s, const int32_t* out_row, int col0) {
   const int64_t n = rows * (I - col0);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(finish_gate_up_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     part, splits, rows, I, col0, act, out_row);
+  if ((I - col0) % 4 == 0 && I % 4 == 0 && col0 % 4 == 0)
+    hipLaunchKernelGGL(finish_gate_up_kernel<4>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256),
+                       0, s, part, splits, rows, I, col0, act, out_row);
+  else
+    hipLaunchKernelGGL(finish_gate_up_kernel<1>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       s, part, splits, rows, I, col0, act, out_row);
   return hipGetLastError();
 }
 
@@ -427,13 +453,18 @@ hipError_t launch_finish_down(const float* part, int splits, int64_t rows, int H
                               int ydt, hipStream_t s, const int32_t* skip) {
   const int64_t n = rows * H;
   if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (ydt == kDtF32)
-    hipLaunchKernelGGL(finish_down_kernel<F32>, dim3(blocks), dim3(256), 0, s, part, splits, rows,
-                       H, static_cast<float*>(y), skip);
-  else
-    hipLaunchKernelGGL(finish_down_kernel<BF16>, dim3(blocks), dim3(256), 0, s, part, splits,
-                       rows, H, static_cast<uint16_t*>(y), skip);
+  auto go = [&](auto v) {
+    constexpr int V = decltype(v)::value;
+    const unsigned blocks = (unsigned)((n / V + 255) / 256);
+    if (ydt == kDtF32)
+      hipLaunchKernelGGL((finish_down_kernel<F32, V>), dim3(blocks), dim3(256), 0, s, part,
+                         splits, rows, H, static_cast<float*>(y), skip);
+    else
+      hipLaunchKernelGGL((finish_down_kernel<BF16, V>), dim3(blocks), dim3(256), 0, s, part,
+                         splits, rows, H, static_cast<uint16_t*>(y), skip);
+  };
+  if (H % 4 == 0) go(std::integral_constant<int, 4>{});
+  else go(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 
