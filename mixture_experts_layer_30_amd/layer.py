@@ -19,6 +19,7 @@ the Serving-tax notes (section "定義", Eq. 1) is tau = T(MoE, b) / T(DenseFA, 
 import torch
 
 from . import binding as B
+from .debug import check_plan, debug_enabled
 
 
 def default_block_m(T, K, E):
@@ -37,12 +38,15 @@ def default_block_m(T, K, E):
 
 class MoELayer:
     def __init__(self, shape, inputs, block_m=None, sched=B.SCHED_AUTO, out_dtype=None,
-                 pad=B.PAD_BLOCK, fp8=False, k_tok=None):
+                 pad=B.PAD_BLOCK, fp8=False, k_tok=None, debug=None):
         """fp8: run the experts, shared experts and DenseFA on the FP8 E4M3 codes
         and row scales of the inputs (keys q13/s13, q2/s2, qs13/ss13, qs2/ss2,
         qfa13/sfa13, qfa2/sfa2; see synth.add_fp8_weights).  k_tok: per-token
         routing budgets [T] int32 on the device (moe_route_var; K is then the
-        largest budget allowed)."""
+        largest budget allowed).  debug (default: the MOE_DEBUG environment
+        variable): check every alignment's invariants on the host
+        (debug.check_plan), raising debug.PlanError on a violation."""
+        self.debug = debug_enabled(debug)
         x = inputs["x"]
         if fp8 and x.dtype != torch.bfloat16:
             raise B.MoEError(B.MOE_EUNSUPPORTED, f"FP8 weights need bf16 tokens, got {x.dtype}")
@@ -90,6 +94,9 @@ class MoELayer:
             B.moe_align(self.topk_ids, self.shape.experts, self.plan)
         else:
             B.moe_align_ex(self.topk_ids, self.shape.experts, self.plan, self.pad)
+        if self.debug:
+            check_plan(self.plan.arrays(), self.topk_ids, self.shape.experts, self.block_m,
+                       self.plan.cap, "block" if self.pad == B.PAD_BLOCK else "max")
 
     def gate_up(self):
         d = self.inputs

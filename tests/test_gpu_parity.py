@@ -673,6 +673,22 @@ def test_layer_parity_max_padding(shape, T, routing, block_m, sched):
     assert rel_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("pad", [B.PAD_BLOCK, B.PAD_MAX])
+def test_debug_mode_checks_device_plans(pad, monkeypatch):
+    """MOE_DEBUG=1: every alignment the layer makes is read back and checked
+    (debug.check_plan); the device's plans pass, block and max padding alike,
+    and the output is unchanged."""
+    shape, T, routing = SMALL_SHAPES[1]
+    d, dev = layer_case(shape, T, routing, seed=21)
+    ref = MoELayer(shape, dev, pad=pad).forward().clone()
+    monkeypatch.setenv("MOE_DEBUG", "1")
+    layer = MoELayer(shape, dev, pad=pad)
+    assert layer.debug
+    out = layer.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 def test_tile_schedule_rejects_unsupported_block():
     shape = TILE_SHAPES[1][0]
     d, dev = layer_case(shape, 40, "zipf")
