@@ -359,6 +359,24 @@ def run_only(name, T, routing, what, steps, fp8=False):
                           "steps": steps}))
         return
     shape = configs.CONFIGS[name]
+    if what == "vendor_gemm":
+        # the vendor library's GEMM (torch.mm: hipBLASLt) on one expert's gate/up at
+        # the batch's average load, T*K/E tokens x 2I outputs x H: a reference for
+        # the grouped prefill kernels' counters, not a step of the pass
+        H, I = shape.hidden, shape.inter
+        m = T * shape.topk // shape.experts
+        x = synth.tokens(m, H, "bf16", seed=1, device="cuda")
+        w = synth.swiglu_weights(I, H, "bf16", seed=2, device="cuda")[0]
+        out = torch.empty(m, 2 * I, dtype=torch.bfloat16, device="cuda")
+        wt = w.t()
+        torch.mm(x, wt, out=out)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            torch.mm(x, wt, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": what, "workload": f"{name} T={T}: one expert's gate/up, {m} tokens",
+                          "steps": steps, "flops_per_launch": 2 * m * H * 2 * I}))
+        return
     d = synth.layer_inputs(shape, T, routing, seed=0, device="cuda", dense=(what == "dense_fa"))
     if fp8:
         synth.add_fp8_weights(d, drop_bf16=True)
@@ -654,7 +672,7 @@ def main():
     ap.add_argument("--routing", default=None)
     ap.add_argument("--all", action="store_true", help="one line per workload of every config")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gate_up", "down", "dense_fa", "layer", "copy"],
+    ap.add_argument("--only", choices=["gate_up", "down", "dense_fa", "layer", "copy", "vendor_gemm"],
                     help="run one piece `--steps` times, untimed (for counter runs)")
     ap.add_argument("--fp8", action="store_true",
                     help="also time the decode workloads with FP8 E4M3 weights (one line each)")
