@@ -221,6 +221,21 @@ moe_status moe_align_ex(const int32_t *topk_ids, int64_t T, int K, int E, const 
                         moe_padding pad, void *stream);
 
 /*
+ * moe_route (k_tok NULL) or moe_route_var (k_tok [T] int32 budgets), then
+ * moe_align_ex, with the same arguments and the same results bit for bit: the
+ * Table 1 auxiliary kernels of the Serving-tax notes at decode, where each is a
+ * few microseconds of work.  While T*K <= 4096 and one workgroup routes the
+ * batch in one pass (T <= 128, 64, 32 or 16 for E <= 8, 16, 32, or more) both
+ * run in one launch of one workgroup (the ids it routes stay in LDS for the
+ * alignment); otherwise the two launches.  topk_ids / topk_w are written as by moe_route; the plan as by
+ * moe_align_ex.
+ * Errors: those of moe_route and moe_align_ex.
+ */
+moe_status moe_route_align(const float *logits, int64_t T, int E, int K, const int32_t *k_tok,
+                           int32_t *topk_ids, float *topk_w, const moe_plan *plan,
+                           moe_padding pad, void *stream);
+
+/*
  * Grouped expert FFN (Serving-tax notes, Table 1 row "GroupGEMM": the batch
  * is split per expert; Table 2 gives the MoE intermediate size).  The expert
  * body is a bias-free SwiGLU.  For each valid row r of the plan (pair

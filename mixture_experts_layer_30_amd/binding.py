@@ -20,7 +20,7 @@ PAD_BLOCK, PAD_MAX = 0, 1
 # every function the C header declares
 EXPORTS = ["moe_last_error", "moe_status_string", "moe_align_capacity", "moe_align_capacity_ex",
            "moe_ffn_workspace_bytes", "moe_ffn_workspace_bytes_ex", "dense_ffn_workspace_bytes",
-           "moe_route", "moe_route_var", "moe_align", "moe_align_ex", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
+           "moe_route", "moe_route_var", "moe_align", "moe_align_ex", "moe_route_align", "moe_grouped_ffn", "moe_grouped_gate_up", "moe_grouped_down",
            "moe_combine", "dense_ffn_fa", "moe_grouped_gate_up_fp8", "moe_grouped_down_fp8",
            "dense_ffn_fp8", "moe_grouped_ffn_noalloc"]
 
@@ -73,6 +73,8 @@ def lib():
         L.moe_align.argtypes = [vp, i64, i32, i32, P, vp]
         L.moe_align_ex.restype = i32
         L.moe_align_ex.argtypes = [vp, i64, i32, i32, P, i32, vp]
+        L.moe_route_align.restype = i32
+        L.moe_route_align.argtypes = [vp, i64, i32, i32, vp, vp, vp, P, i32, vp]
         L.moe_grouped_ffn.restype = i32
         L.moe_grouped_ffn.argtypes = [vp, i32, i64, i32, i32, i32, i32, vp, vp, P, vp, i64, vp, vp]
         L.moe_grouped_ffn_noalloc.restype = i32
@@ -180,6 +182,15 @@ def moe_align(topk_ids, E, plan, stream=None):
 def moe_align_ex(topk_ids, E, plan, pad, stream=None):
     T, K = topk_ids.shape
     _check(lib().moe_align_ex(_ptr(topk_ids), T, K, E, ctypes.byref(plan.c), pad, _stream(stream)))
+
+
+def moe_route_align(logits, K, topk_ids, topk_w, plan, pad=None, k_tok=None, stream=None):
+    """moe_route (or moe_route_var with budgets k_tok) then moe_align_ex, in one
+    launch for small batches."""
+    T, E = logits.shape
+    _check(lib().moe_route_align(_ptr(logits), T, E, K, _ptr(k_tok) if k_tok is not None else None,
+                                 _ptr(topk_ids), _ptr(topk_w), ctypes.byref(plan.c),
+                                 PAD_BLOCK if pad is None else pad, _stream(stream)))
 
 
 def moe_grouped_ffn(x, w13, w2, K, plan, workspace, y_pairs, stream=None):

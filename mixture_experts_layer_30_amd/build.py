@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "route.hip", "align.hip", "combine.hip", "stream_ffn.hip", "ring_ffn.hip", "tile_ffn.hip",
-           "span_ffn.hip", "noalloc.hip"]
+           "span_ffn.hip", "route_align.hip", "noalloc.hip"]
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           # no packed-fp32 instructions in device code

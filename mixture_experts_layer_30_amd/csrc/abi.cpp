@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include "kernels.h"
+#include "route_align.h"
 
 namespace {
 
@@ -522,6 +523,28 @@ moe_status moe_align_ex(const int32_t* topk_ids, int64_t T, int K, int E, const 
 moe_status moe_align(const int32_t* topk_ids, int64_t T, int K, int E, const moe_plan* plan,
                      void* stream) {
   return moe_align_ex(topk_ids, T, K, E, plan, MOE_PAD_BLOCK, stream);
+}
+
+moe_status moe_route_align(const float* logits, int64_t T, int E, int K, const int32_t* k_tok,
+                           int32_t* topk_ids, float* topk_w, const moe_plan* plan,
+                           moe_padding pad, void* stream) {
+  moe_status st = check_route_shape(T, E, K);
+  if (st) return st;
+  if (pad != MOE_PAD_BLOCK && pad != MOE_PAD_MAX)
+    return fail(MOE_EINVAL, "moe_route_align: padding scheme %d", (int)pad);
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+                !aligned(topk_w, 4) || (k_tok && !aligned(k_tok, 4))))
+    return fail(MOE_EINVAL, "moe_route_align: NULL or misaligned pointer");
+  st = check_plan(plan, T, K, E, pad);
+  if (st) return st;
+  if (T == 0)   // the plan of an empty batch: the alignment alone
+    return moe_align_ex(topk_ids, T, K, E, plan, pad, stream);
+  return hip_status(moe::launch_route_align(logits, T, E, K, k_tok, topk_ids, topk_w,
+                                            plan->block_m, plan->cap, pad == MOE_PAD_MAX ? 1 : 0,
+                                            plan->expert_counts, plan->expert_offsets,
+                                            plan->sorted_ids, plan->block_expert, plan->inv_pos,
+                                            (hipStream_t)stream),
+                    "moe_route_align");
 }
 
 static moe_status check_grouped(const void* x, moe_dtype dt, int64_t T, int H, int I, int E, int K,

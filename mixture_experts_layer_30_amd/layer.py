@@ -94,6 +94,15 @@ class MoELayer:
             B.moe_align(self.topk_ids, self.shape.experts, self.plan)
         else:
             B.moe_align_ex(self.topk_ids, self.shape.experts, self.plan, self.pad)
+        self._debug_plan()
+
+    def route_align(self):
+        """route() then align() in one call (one launch for small batches)."""
+        B.moe_route_align(self.inputs["logits"], self.shape.topk, self.topk_ids, self.topk_w,
+                          self.plan, self.pad, self.k_tok)
+        self._debug_plan()
+
+    def _debug_plan(self):
         if self.debug:
             check_plan(self.plan.arrays(), self.topk_ids, self.shape.experts, self.block_m,
                        self.plan.cap, "block" if self.pad == B.PAD_BLOCK else "max")
@@ -143,8 +152,16 @@ class MoELayer:
                 self.shared()
             join = torch.cuda.Event()
             join.record(self.side)
-        self.route()
-        self.align()
+        if self.has_shared:
+            # the shared experts' ring, forked first, holds every CU's LDS while it
+            # streams; the routing kernel (no LDS) still runs beside it, a fused
+            # routing + alignment launch would wait (measured on MI355X: Qwen2-shaped
+            # T = 1 pass 190 -> 192-206 us fused; Mixtral-shaped T = 1, no shared
+            # experts, 142 -> 135)
+            self.route()
+            self.align()
+        else:
+            self.route_align()
         if gate_up_events:
             gate_up_events[0].record(cur)
         self.gate_up()

@@ -119,6 +119,79 @@ def test_route_var_parity(T, E, K):
     assert (got[rids < 0] == 0).all()
 
 
+# ------------------------------------------------- routing and alignment in one launch
+
+ROUTE_ALIGN_CASES = [
+    # (T, E, K, routing, block_m, pad, budgets): one-launch sizes (T*K <= 4096 and one
+    # routing pass: T <= 128, 64, 32, 16 for E <= 8, 16, 32, more) for each route
+    # instantiation (E <= 8, 16, 32, 64, and 4 logits a lane), ties, max padding and
+    # per-token budgets, 128 tokens of 8 experts (one pass, the largest); two launches past
+    # a pass (T = 32 of 64 experts, 128 of 256) and past 4096 pairs (4104)
+    (1, 8, 2, "uniform", 16, B.PAD_BLOCK, False),
+    (32, 8, 2, "uniform", 16, B.PAD_BLOCK, False),
+    (1, 64, 8, "zipf", 16, B.PAD_BLOCK, False),
+    (32, 64, 8, "zipf", 64, B.PAD_MAX, False),
+    (19, 37, 5, "uniform", 32, B.PAD_BLOCK, False),
+    (40, 16, 16, "ties", 16, B.PAD_BLOCK, False),
+    (33, 10, 10, "ties", 128, B.PAD_BLOCK, True),
+    (128, 256, 8, "uniform", 64, B.PAD_BLOCK, False),
+    (128, 256, 8, "zipf", 64, B.PAD_BLOCK, True),
+    (300, 3, 2, "uniform", 1, B.PAD_MAX, False),
+    (128, 8, 2, "uniform", 16, B.PAD_BLOCK, True),
+    (16, 200, 8, "zipf", 16, B.PAD_MAX, False),
+    (9, 20, 3, "ties", 32, B.PAD_BLOCK, False),
+    (512, 256, 8, "zipf", 128, B.PAD_BLOCK, False),
+    (513, 256, 8, "zipf", 128, B.PAD_BLOCK, True),
+]
+
+
+@pytest.mark.parametrize("T,E,K,routing,block_m,pad,budgets", ROUTE_ALIGN_CASES)
+def test_route_align_parity(T, E, K, routing, block_m, pad, budgets):
+    """moe_route_align gives what moe_route(_var) then moe_align_ex give, bit for bit,
+    and both match the oracle."""
+    logits = (tie_logits(T, E, seed=T + E) if routing == "ties"
+              else synth.router_logits(T, E, routing, seed=T + E))
+    k_tok = synth.budgets(T, list(range(0, K + 1)), seed=T) if budgets else None
+    ld = logits.to(DEV)
+    kd = k_tok.to(DEV) if budgets else None
+    plan = B.Plan(T, K, E, block_m, DEV, pad=pad)
+    for t in plan.arrays().values():
+        t.fill_(-12345)
+    ids = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), -7.0, dtype=torch.float32, device=DEV)
+    B.moe_route_align(ld, K, ids, w, plan, pad, kd)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in plan.arrays().items()}
+    rids, rw = oracle.route_var(logits, K, k_tok) if budgets else oracle.route(logits, K)
+    assert (ids.cpu().numpy() == rids).all()
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-5
+    ref = oracle.align(rids, E, block_m, plan.cap, mode="max" if pad == B.PAD_MAX else "block")
+    for k in ref:
+        assert (got[k] == ref[k]).all(), k
+    # the separate launches: identical
+    ids2, w2 = torch.empty_like(ids), torch.empty_like(w)
+    plan2 = B.Plan(T, K, E, block_m, DEV, pad=pad)
+    if budgets:
+        B.moe_route_var(ld, K, kd, ids2, w2)
+    else:
+        B.moe_route(ld, K, ids2, w2)
+    B.moe_align_ex(ids2, E, plan2, pad)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    for k, v in plan2.arrays().items():
+        assert (v.cpu().numpy() == got[k]).all(), k
+
+
+def test_route_align_empty_batch():
+    plan = B.Plan(0, 2, 8, 16, DEV)
+    ids = torch.empty(0, 2, dtype=torch.int32, device=DEV)
+    w = torch.empty(0, 2, dtype=torch.float32, device=DEV)
+    B.moe_route_align(torch.zeros(0, 8, device=DEV), 2, ids, w, plan)
+    torch.cuda.synchronize()
+    a = plan.arrays()
+    assert (a["expert_counts"].cpu() == 0).all() and (a["expert_offsets"].cpu() == 0).all()
+
+
 @pytest.mark.parametrize("block_m", [1, 16, 64, 128])
 def test_align_with_unused_slots(block_m):
     for T, E, K, levels in [(200, 8, 2, [0, 1, 2]), (500, 64, 8, [2, 4, 8]), (3, 4, 4, [0])]:
