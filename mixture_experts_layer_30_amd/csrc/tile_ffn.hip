@@ -400,16 +400,31 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
               (((lane & 7) ^ swz(r)) << 4);
   }
 
-  // this workgroup's steps [k0, k0 + nk) of the contraction
+  // this workgroup's steps [k0, k0 + nk) of the contraction.  Workgroups that
+  // start together read the same offset of their weight rows at the same
+  // time, and where a row is a whole number of 4 KB those reads pile onto the
+  // same HBM channels; there each (expert, weight tile) starts 3 steps further
+  // round its steps, taking k0 + rot .. k0 + nk - 1 and then k0 .. k0 + rot - 1
+  // (one start per weight tile, so token blocks sharing a tile through L2 stay
+  // in step).  Elsewhere the tiles stay in step: they share the token rows,
+  // which they then read from L2 together.  Measured on MI355X (us, bf16):
+  // Mixtral-shaped (8 KB gate/up rows, 28 KB down rows) DenseFA at 128 tokens
+  // 176 -> 163, grouped down at 512 / 2048 tokens 283 -> 277 / 617 -> 604;
+  // DeepSeek-V3-shaped grouped down (4 KB rows, Zipf routing) 344 -> 335; its
+  // 14 KB gate/up rows rotated measured no gain.  Costs: Mixtral-shaped DenseFA
+  // at 512 tokens 392 -> 399 and the grouped down at 128 tokens 176 -> 179.
   const int nk_all = Kdim / kBK;
   const int k0 = zk * nk_all / slices;
   const int nk = (zk + 1) * nk_all / slices - k0;
+  const bool rotate = !kF8 && ((int64_t)Kdim * SW::kBytes) % 4096 == 0 && nk > 0;
+  const int rot = rotate ? 3 * (tile + e * ntiles) % nk : 0;
   auto issue = [&](int ks) {
     const int st = ks % ST;
-    const size_t kb = (size_t)(k0 + ks) * kRowBytes;
+    const int kp = ks + rot < nk ? ks + rot : ks + rot - nk;
+    const size_t kb = (size_t)(k0 + kp) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < AInst; ++j)
-      lds_direct16(asrc[j] + (size_t)(k0 + ks) * AROW, &sm.a[st][(wave * AInst + j) * 1024]);
+      lds_direct16(asrc[j] + (size_t)(k0 + kp) * AROW, &sm.a[st][(wave * AInst + j) * 1024]);
 #pragma unroll
     for (int j = 0; j < BInst; ++j)
       lds_direct16(bsrc[j] + kb, &sm.b[st][(wave * BInst + j) * 1024]);
