@@ -505,6 +505,10 @@ TILE_SHAPES = [
     # sums per pair, added in slice order by the finish kernels)
     (LayerShape("tile_split", 1024, 1024, 8, 2, 0, "bf16", (100,), ("uniform",)), 100, "uniform", 64),
     (LayerShape("tile_split_zipf", 1024, 1024, 16, 4, 512, "bf16", (100,), ("zipf",)), 100, "zipf", 128),
+    # weight rows of a whole number of 4 KB (H = I = 2048 bf16): each weight tile starts
+    # its contraction further round its steps; ragged blocks, and a split down projection
+    (LayerShape("tile2_rot", 2048, 2048, 8, 2, 0, "bf16", (300,), ("zipf",)), 300, "zipf", 128),
+    (LayerShape("tile2_rot_split", 2048, 2048, 16, 4, 0, "bf16", (70,), ("uniform",)), 70, "uniform", 64),
 ]
 
 
