@@ -264,6 +264,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void lds_direct16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
 }
+// The same with the non-temporal hint, for data read by one workgroup only
+__device__ __forceinline__ void lds_direct16_nt(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 2);
+}
 
 // Workgroup barrier without the memory fence __syncthreads() adds (which would
 // wait for every load in flight, draining the LDS ring).  The "memory" clobber
@@ -418,13 +422,16 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   const int nk = (zk + 1) * nk_all / slices - k0;
   const bool rotate = !kF8 && ((int64_t)Kdim * SW::kBytes) % 4096 == 0 && nk > 0;
   const int rot = rotate ? 3 * (tile + e * ntiles) % nk : 0;
-  auto issue = [&](int ks) {
+  auto issue = [&](int ks, auto nt) {
     const int st = ks % ST;
     const int kp = ks + rot < nk ? ks + rot : ks + rot - nk;
     const size_t kb = (size_t)(k0 + kp) * kRowBytes;
 #pragma unroll
-    for (int j = 0; j < AInst; ++j)
-      lds_direct16(asrc[j] + (size_t)(k0 + kp) * AROW, &sm.a[st][(wave * AInst + j) * 1024]);
+    for (int j = 0; j < AInst; ++j) {
+      const uint8_t* src = asrc[j] + (size_t)(k0 + kp) * AROW;
+      if constexpr (decltype(nt)::value) lds_direct16_nt(src, &sm.a[st][(wave * AInst + j) * 1024]);
+      else lds_direct16(src, &sm.a[st][(wave * AInst + j) * 1024]);
+    }
 #pragma unroll
     for (int j = 0; j < BInst; ++j)
       lds_direct16(bsrc[j] + kb, &sm.b[st][(wave * BInst + j) * 1024]);
@@ -496,16 +503,16 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
   // The k loop, in a copy per path so that the steady-state body (wait for
   // stage ks, barrier, issue stage ks + ST - 1, the step) is one basic block
   // and the waits inside it count only the reads an op needs.
-  auto run = [&](auto masked) {
+  auto run = [&](auto masked, auto nt) {
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
-      if (s0 < nk) issue(s0);
+      if (s0 < nk) issue(s0, nt);
     int ks = 0;
     for (; ks + ST - 1 < nk; ++ks) {
       // stage ks must be in LDS: the ST-2 stages issued after it may stay in flight
       wait_vmcnt<(ST - 2) * kLoads>();
       barrier_no_fence();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
-      issue(ks + ST - 1);
+      issue(ks + ST - 1, nt);
       step(ks % ST, masked);
     }
     for (; ks < nk; ++ks) {   // the last ST - 1 steps: nothing left to issue
@@ -514,10 +521,29 @@ __global__ __launch_bounds__(NW * kWave, 1) void tile2_ffn_kernel(
       step(ks % ST, masked);
     }
   };
-  if (NB2 == 2 && tn_live == TN)
-    run(std::false_type{});
-  else
-    run(std::true_type{});
+  // The weight tile's loads carry the non-temporal hint where no other
+  // workgroup reads the same rows: dense rows in one token block, or an expert
+  // whose bucket is one block.  Where several token blocks share a weight tile
+  // they run side by side and meet in L2, which the hint would defeat.  bf16
+  // only (FP8 rows are 64-byte pieces a step, which the hint slows).  Measured
+  // on MI355X (us): Mixtral-shaped layer at 128 tokens 535 -> 485 (its DenseFA
+  // 166 -> 145), DeepSeek-V3-shaped DenseFA at 128 tokens 192 -> 173, Qwen2-
+  // shaped gate/up at 256 tokens 409 -> 395; with the hint on every tile the
+  // shared tiles lost up to 14% (Mixtral-shaped gate/up at 512 tokens 446 -> 510).
+  const bool single = dense ? nblocks == 1 : rm.offsets[e + 1] - rm.offsets[e] <= BN;
+  const bool live = NB2 == 2 && tn_live == TN;
+  if constexpr (!kF8) {
+    if (single) {
+      if (live) run(std::false_type{}, std::true_type{});
+      else run(std::true_type{}, std::true_type{});
+    } else {
+      if (live) run(std::false_type{}, std::false_type{});
+      else run(std::true_type{}, std::false_type{});
+    }
+  } else {
+    if (live) run(std::false_type{}, std::false_type{});
+    else run(std::true_type{}, std::false_type{});
+  }
 
   // epilogue: lane holds rows 4g..4g+3 of each 16-row tile, for token column m of each tile
   if (kGateUp) {
