@@ -216,6 +216,10 @@ VAR_K_CASES = [
     # the grouped tile's contraction split with unused slots
     (LayerShape("vark_tile_split", 1024, 1024, 8, 4, 0, "bf16", (60,), ("uniform",)), 60,
      [0, 1, 2, 4], B.SCHED_TILE, 64),
+    # the span down projection split in two (loads 276 / 265 / 265 in equal halves, 243 split)
+    # with 351 unused slots, which its finish kernel skips
+    (LayerShape("vark_span_split", 256, 8192, 4, 2, 0, "bf16", (700,), ("uniform",)), 700,
+     [1, 2], B.SCHED_AUTO, 64),
 ]
 
 
