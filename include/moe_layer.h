@@ -151,12 +151,9 @@ int64_t moe_ffn_workspace_bytes(int64_t cap, int I);
  * Workspace bytes with which moe_grouped_ffn (and its halves, bf16 and FP8)
  * may also split the contraction of a launch across workgroups: a
  * weight-streaming launch when few experts can be active (T*K or E small:
- * their weight slabs alone would leave compute units idle), the tiled bf16
- * down projection when its token blocks would (sized where MOE_SCHED_AUTO
- * tiles: T > 32 and T*K >= 24*E), and the span schedule's down projection
- * where experts average 192..384 tokens (about one span each, whose
- * contraction is then cut in two; the partial sums 2*T*K*H*4 bytes at most
- * 35% of the weights' E*H*I*2).  The workspace holds the activations, then
+ * their weight slabs alone would leave compute units idle), and the tiled
+ * bf16 down projection when its token blocks would (sized where MOE_SCHED_AUTO
+ * tiles: T > 32 and T*K >= 24*E).  The workspace holds the activations, then
  * fp32 partial sums per pair added in a fixed order by a second kernel.  A
  * workspace of at least this size selects the split wherever it applies; one
  * of moe_ffn_workspace_bytes never splits.  The two give results that differ

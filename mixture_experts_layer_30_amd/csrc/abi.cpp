@@ -369,27 +369,6 @@ bool span_auto_down(moe_dtype dt, int64_t T, int K, int E, int H, int I, int64_t
          (int64_t)(H / 256) * (T * K / 256 + E) <= 256 && span_shape_ok(dt, E, H, I, T, cap);
 }
 
-// Contraction split of the span schedule's down projection: 2 where experts
-// average 192..384 tokens (T*K/E, about one span each, so that most spans hold
-// more than 192 rows and the launch splits them in two; launch_span_down), and
-// where the fp32 partial sums, 2 x T*K x H x 4 bytes written and read back,
-// stay below 35% of the weight bytes E*H*I*2; else 1.  Measured on MI355X
-// (Mixtral-shaped experts, us): at T=1024, one span per expert and 128 down
-// items for 256 CUs, the down projection runs 405 unsplit against 376 split
-// (finish included); the split spans then fill LDS at ~5.2 TB/s over all CUs
-// where 128 CUs reached ~4.7, so the items share a load bound rather than
-// halving.  At T=2048 (two spans an expert) the split span launch took 696
-// against 631 for the 128-token tiles, which keep that shape.
-int span_down_split(int64_t T, int K, int E, int H, int I) {
-  const int64_t pairs = T * K;
-  if (pairs < (int64_t)192 * E || pairs > (int64_t)384 * E || H % 4) return 1;
-  return 16.0 * (double)pairs <= 0.7 * (double)E * (double)I ? 2 : 1;
-}
-
-int64_t span_down_part_bytes(int64_t T, int K, int E, int H, int I) {
-  return span_down_split(T, K, E, H, I) > 1 ? (int64_t)2 * T * K * H * 4 : 0;
-}
-
 moe_status span_unsupported(const char* what) {
   return fail(MOE_EUNSUPPORTED, "%s: span schedule needs bf16, E <= 512, H %% 256 == 0, "
               "I %% 128 == 0 and an expert's gate/up matrix, x and the activations each "
@@ -487,9 +466,6 @@ int64_t moe_ffn_workspace_bytes_ex(int64_t cap, int64_t T, int K, int E, int H, 
       part = t.part_bytes > part ? t.part_bytes : part;
     }
   }
-  // and the span schedule's split down projection
-  const int64_t sp = span_down_part_bytes(T, K, E, H, I);
-  part = sp > part ? sp : part;
   return grouped_part_offset(cap, I) + part;
 }
 
@@ -687,15 +663,8 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   const bool ring = moe::ring_down_ok(dt, H, I);
   st = pick_stream(sched, ring, ring, "moe_grouped_down", &use);
   if (st) return st;
-  // the span schedule's split down projection where the workspace holds its
-  // partial sums (a smaller workspace: unsplit)
-  const int span_split =
-      workspace_bytes >= grouped_part_offset(plan->cap, I) + span_down_part_bytes(T, K, E, H, I)
-          ? span_down_split(T, K, E, H, I)
-          : 1;
   if (sched == MOE_SCHED_AUTO && use == MOE_SCHED_TILE &&
-      (span_auto_down(dt, T, K, E, H, I, plan->cap) ||
-       (span_split > 1 && span_shape_ok(dt, E, H, I, T, plan->cap))))
+      span_auto_down(dt, T, K, E, H, I, plan->cap))
     use = MOE_SCHED_SPAN;
   const bool hot_tiled = sched == MOE_SCHED_AUTO && tile_ok(plan->block_m, H);
   const moe::RowMap rm = grouped_rows(plan, K);
@@ -703,9 +672,8 @@ moe_status moe_grouped_down(const void* w2, moe_dtype dt, int64_t T, int H, int 
   hipError_t e;
   if (use == MOE_SCHED_SPAN) {
     if (!span_shape_ok(dt, E, H, I, T, plan->cap)) return span_unsupported("moe_grouped_down");
-    float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));
     e = moe::launch_span_down(w2, (const uint16_t*)workspace, rm, E, H, I, plan->cap, T * K,
-                              y_pairs, dt, s, span_split, part, T * K);
+                              y_pairs, dt, s);
   } else if (use == MOE_SCHED_TILE) {
     const TileSplit ts = grouped_tile_split_for(dt, T, K, E, H, I, plan, workspace_bytes);
     float* part = (float*)((char*)workspace + grouped_part_offset(plan->cap, I));

@@ -107,13 +107,9 @@ bool span_ok(int E, int H, int I, int64_t x_rows, int64_t act_rows);
 hipError_t launch_span_gate_up(const void* x, const void* w13, const RowMap& rm, int E, int H,
                                int I, int64_t x_rows, int64_t rows_bound, uint16_t* act,
                                hipStream_t s);
-// ksplit = 2 splits the contraction of the spans above 192 rows in two, their
-// fp32 sums going to part [2][prows][H] (prows: the T*K pairs, or the dense
-// rows) and added by a finish launch on the same stream; ksplit = 1: no split.
 hipError_t launch_span_down(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H,
                             int I, int64_t act_rows, int64_t rows_bound, void* y, int ydt,
-                            hipStream_t s, int ksplit = 1, float* part = nullptr,
-                            int64_t prows = 0);
+                            hipStream_t s);
 
 // act[o][col0 + i] = silu(g) * u for i < W = I - col0, with g, u the in-order sums
 // over z < splits of part[z][r][i] and part[z][r][W + i], o = out_row[r] (r when

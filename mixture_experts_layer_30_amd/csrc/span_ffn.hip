@@ -38,15 +38,16 @@
 //            matching gate and up sums and applies the SwiGLU in registers;
 //            act rows are the alignment rows.
 //   down:    tile rows are 256 output features; each token's sums go to its
-//            pair's output row.
-//
-// The down projection's items carry the I-long contraction, so a few hundred
-// of them can leave CUs idle (one span per expert at ~256 tokens: 128 items
-// for Mixtral's 8 experts on 256 CUs).  A launch with ksplit = 2 splits the
-// contraction of every span above 192 rows in two halves, whose fp32 sums go
-// to part [2][rows][H] and are added by finish_span_down_kernel; shorter spans
-// (the two equal spans of 257..384 rows, a short last span) stay whole and
-// write their rows directly, so the items weigh about the same.
+//            pair's output row.  An expert of 193 to 256 tokens gets two
+//            spans of equal length here too: the down items carry the I-long
+//            contraction, and an expert's H/256 tiles each read its
+//            activation rows again, so one span an expert (Mixtral T=1024:
+//            128 items for 256 CUs) leaves CUs idle while the launch is
+//            bound by those re-reads from HBM.  The two spans of a tile run
+//            side by side on one XCD and read its weights through L2
+//            (measured on MI355X: Mixtral-shaped T=1024 down 400 -> 339-343
+//            us; a two-way contraction split of the long spans instead,
+//            with fp32 partial sums and a finish launch, 352-358).
 #include <type_traits>
 
 #include "common.h"
@@ -81,23 +82,12 @@ __device__ __forceinline__ int span_off(int row, int seg) {
   return row * kPRow + ((seg ^ ((row >> 1) & 3)) << 4);
 }
 
-// Spans of an expert's n rows: runs of 256 and a shorter last one, or two of
-// equal length (within one row) for 257..384 rows.
-struct SpanGeo {
-  int spans, slen;
-};
-__device__ __forceinline__ SpanGeo span_geo(int n) {
-  SpanGeo g;
-  g.spans = (n + kPTok - 1) / kPTok;
-  g.slen = (g.spans == 2 && n <= 3 * kPTok / 2) ? (n + 1) / 2 : kPTok;
-  return g;
-}
-
-constexpr int kPSplitMin = 3 * kPTok / 4;   // spans above this many rows are split
-
-// contraction slices of a span of len rows in a launch split ksplit ways
-__device__ __forceinline__ int span_slices(int len, int ksplit) {
-  return (ksplit > 1 && len > kPSplitMin) ? ksplit : 1;
+// Spans of an expert's n rows: runs of 256 and a shorter last one; the down
+// projection halves an expert of 193..256 rows (its length rule below)
+template <bool kGateUp>
+__device__ __forceinline__ int span_count(int n) {
+  const int s = (n + kPTok - 1) / kPTok;
+  return (!kGateUp && s == 1 && n > 3 * kPTok / 4) ? 2 : s;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -120,14 +110,11 @@ __device__ __forceinline__ void span_wait_lgkm0() {
 
 // w: w13 [E][2I][H] (gate/up) or w2 [E][H][I] (down); xs: x [T][H] (gate/up)
 // or act [rows][I] (down).  Writes act [rows][I] (gate/up) or y [pairs][H] at
-// each row's pair (down; dense rows: y [T][H]); a down launch with ksplit = 2
-// writes the split spans' sums to part [2][prows][H] instead (prows: T*K
-// pairs, or the dense rows).
+// each row's pair (down; dense rows: y [T][H]).
 template <class SY, bool kGateUp>
 __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ xs, RowMap rm, int E, int H,
-    int I, uint16_t* __restrict__ act, typename SY::T* __restrict__ y, int ksplit,
-    float* __restrict__ part, int64_t prows) {
+    int I, uint16_t* __restrict__ act, typename SY::T* __restrict__ y) {
   __shared__ __attribute__((aligned(1024))) SpanSmem sm;
   constexpr int TM = 8, TN = 4;
   const bool dense = rm.counts == nullptr;
@@ -141,18 +128,13 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
   const int ntiles = kGateUp ? I / (kPRows / 2) : H / kPRows;
   const int nexp = dense ? 1 : E;
 
-  // items per expert (tiles x the slices of its spans, of the experts within
-  // min_rows..max_rows), scanned across the workgroup into pre[]
+  // items per expert (tiles x spans of the experts within min_rows..max_rows),
+  // scanned across the workgroup into pre[]
   {
     int u = 0;
     if (tid < nexp) {
       const int n = dense ? (int)rm.dense_rows : rm.counts[tid];
-      if (n > 0 && (dense || (n >= rm.min_rows && n <= rm.max_rows))) {
-        const SpanGeo sg = span_geo(n);
-        const int full = sg.spans - 1;
-        u = ntiles * (full * span_slices(sg.slen, ksplit) +
-                      span_slices(n - full * sg.slen, ksplit));
-      }
+      if (dense || (n >= rm.min_rows && n <= rm.max_rows)) u = ntiles * span_count<kGateUp>(n);
     }
     int incl = u;
 #pragma unroll
@@ -190,25 +172,12 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
     const int n = dense ? (int)rm.dense_rows : __builtin_amdgcn_readfirstlane(rm.counts[e]);
     // spans of 256 rows and a shorter last one; an expert of 257..384 rows gets
     // two spans of equal length (within one row) instead, so that its items
-    // weigh about the same rather than one full and one near-empty.  Within a
-    // tile the items of the full spans come slice-major (the spans that share
-    // a weight slice side by side), then the last span's slices.
-    const SpanGeo sg = span_geo(n);
-    const int full = sg.spans - 1, slen = sg.slen;
-    const int slf = span_slices(slen, ksplit), sll = span_slices(n - full * slen, ksplit);
-    const int per_tile = full * slf + sll;
+    // weigh about the same rather than one full and one near-empty (the down
+    // projection: from 193 rows)
+    const int spans = span_count<kGateUp>(n);
     const int l = it - __builtin_amdgcn_readfirstlane(sm.pre[e]);
-    const int tile = l / per_tile, li = l - tile * per_tile;
-    int span, z, nsl;
-    if (li < full * slf) {
-      z = li / full;
-      span = li - z * full;
-      nsl = slf;
-    } else {
-      span = full;
-      z = li - full * slf;
-      nsl = sll;
-    }
+    const int tile = l / spans, span = l - tile * spans;
+    const int slen = (spans == 2 && n <= 3 * kPTok / 2) ? (n + 1) / 2 : kPTok;
     const int row0 =
         (dense ? 0 : __builtin_amdgcn_readfirstlane(rm.offsets[e])) + span * slen;
     const int nvalid = min(slen, n - span * slen);
@@ -251,14 +220,7 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
       aoff[j] = wr * (uint32_t)Kdim * 2u + (seg << 4);
       boff[j] = (uint32_t)sm.tok[r] * (uint32_t)Kdim * 2u + (seg << 4);
     }
-    // slice z of nsl: contraction steps [ks0, ks1) of the Kdim / 32
-    const int ks0 = z * (Kdim / 32) / nsl, ks1 = (z + 1) * (Kdim / 32) / nsl;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      aoff[j] += (uint32_t)ks0 * kPRow;
-      boff[j] += (uint32_t)ks0 * kPRow;
-    }
-    const int nk = ks1 - ks0;
+    const int nk = Kdim / 32;
     // token loads of this wavefront that hold tokens (16-row groups 2w, 2w+1
     // below the span's end); the others are skipped, and the ring's waits
     // count the wavefront's own loads per stage, 2 + lb
@@ -412,46 +374,11 @@ __global__ __launch_bounds__(kPThreads, 1) void span_ffn_kernel(
           const int j = (wn + 4 * tn) * 16 + m;
           if (j < nvalid) {
             const int h = i0 + wm * 128 + tm * 16 + 4 * g;
-            if (nsl > 1)
-              *reinterpret_cast<f32x4*>(part + ((size_t)z * prows + sm.dst[j]) * H + h) =
-                  acc[tm][tn];
-            else
-              store_out4<SY>(y + (size_t)sm.dst[j] * H + h, acc[tm][tn]);
+            store_out4<SY>(y + (size_t)sm.dst[j] * H + h, acc[tm][tn]);
           }
         }
     }
   }
-}
-
-// y[p][h] = part[0][p][h] + part[1][p][h] for the pairs p (dense rows: rows)
-// whose span the split launch cut in two; the other rows were written by the
-// span kernel itself.  Four elements a thread.
-template <class SY>
-__global__ __launch_bounds__(256) void finish_span_down_kernel(const float* __restrict__ part,
-                                                               int ksplit, int64_t prows, int H,
-                                                               RowMap rm,
-                                                               typename SY::T* __restrict__ y) {
-  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (idx >= prows * H) return;
-  const int64_t p = idx / H;
-  int j, n;
-  if (rm.counts == nullptr) {
-    j = (int)p;
-    n = (int)rm.dense_rows;
-  } else {
-    const int r = rm.inv_pos[p];
-    if (r < 0) return;   // an unused slot: no row
-    const int e = rm.block_expert[r / rm.block_m];
-    j = r - rm.offsets[e];
-    n = rm.counts[e];
-  }
-  const SpanGeo sg = span_geo(n);
-  const int span = j / sg.slen;
-  if (span_slices(min(sg.slen, n - span * sg.slen), ksplit) == 1) return;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < ksplit; ++z)
-    acc += *reinterpret_cast<const f32x4*>(part + (size_t)z * prows * H + idx);
-  store_out4<SY>(y + idx, acc);
 }
 
 // compute units of the device current at the first call, as a multiple of the
@@ -498,38 +425,25 @@ hipError_t launch_span_gate_up(const void* x, const void* w13, const RowMap& rm,
   if (items <= 0) return hipSuccess;
   hipLaunchKernelGGL((span_ffn_kernel<BF16, true>), dim3(span_grid(items)), dim3(kPThreads), 0, s,
                      static_cast<const uint16_t*>(w13), static_cast<const uint16_t*>(x), rm, E, H,
-                     I, act, (uint16_t*)nullptr, 1, (float*)nullptr, (int64_t)0);
+                     I, act, (uint16_t*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_span_down(const void* w2, const uint16_t* act, const RowMap& rm, int E, int H,
                             int I, int64_t act_rows, int64_t rows_bound, void* y, int ydt,
-                            hipStream_t s, int ksplit, float* part, int64_t prows) {
+                            hipStream_t s) {
   if (!span_ok(rm.counts == nullptr ? 1 : E, H, I, 0, act_rows)) return hipErrorInvalidValue;
-  if (ksplit != 1 && (ksplit != 2 || part == nullptr || prows <= 0 || H % 4))
-    return hipErrorInvalidValue;
   const int ntiles = H / kPRows;
-  const int64_t items = span_items(rm, E, rows_bound, ntiles) * ksplit;
+  const int64_t items = span_items(rm, E, rows_bound, ntiles);
   if (items <= 0) return hipSuccess;
-  float* ps = ksplit > 1 ? part : nullptr;
   if (ydt == kDtF32)
     hipLaunchKernelGGL((span_ffn_kernel<F32, false>), dim3(span_grid(items)), dim3(kPThreads), 0,
                        s, static_cast<const uint16_t*>(w2), act, rm, E, H, I, (uint16_t*)nullptr,
-                       static_cast<float*>(y), ksplit, ps, prows);
+                       static_cast<float*>(y));
   else
     hipLaunchKernelGGL((span_ffn_kernel<BF16, false>), dim3(span_grid(items)), dim3(kPThreads), 0,
                        s, static_cast<const uint16_t*>(w2), act, rm, E, H, I, (uint16_t*)nullptr,
-                       static_cast<uint16_t*>(y), ksplit, ps, prows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ksplit == 1) return e;
-  const int64_t threads = prows * H / 4;
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  if (ydt == kDtF32)
-    hipLaunchKernelGGL((finish_span_down_kernel<F32>), grid, dim3(256), 0, s, part, ksplit, prows,
-                       H, rm, static_cast<float*>(y));
-  else
-    hipLaunchKernelGGL((finish_span_down_kernel<BF16>), grid, dim3(256), 0, s, part, ksplit,
-                       prows, H, rm, static_cast<uint16_t*>(y));
+                       static_cast<uint16_t*>(y));
   return hipGetLastError();
 }
 

@@ -216,10 +216,10 @@ VAR_K_CASES = [
     # the grouped tile's contraction split with unused slots
     (LayerShape("vark_tile_split", 1024, 1024, 8, 4, 0, "bf16", (60,), ("uniform",)), 60,
      [0, 1, 2, 4], B.SCHED_TILE, 64),
-    # the span down projection split in two (loads 276 / 265 / 265 in equal halves, 243 split)
-    # with 351 unused slots, which its finish kernel skips
-    (LayerShape("vark_span_split", 256, 8192, 4, 2, 0, "bf16", (700,), ("uniform",)), 700,
-     [1, 2], B.SCHED_AUTO, 64),
+    # the span schedule (loads 276 / 265 / 265 in equal spans, 243 halved by the down
+    # projection) with 351 unused slots
+    (LayerShape("vark_span", 256, 8192, 4, 2, 0, "bf16", (700,), ("uniform",)), 700,
+     [1, 2], B.SCHED_SPAN, 64),
 ]
 
 
@@ -597,49 +597,39 @@ def test_span_schedule_rejects_unsupported_shape():
         layer.down()
 
 
-SPAN_SPLIT_SHAPES = [
-    # (shape, T, routing, block_m, pad): experts averaging 192..384 tokens with
-    # few partial sums next to the weights (16 T K <= 0.7 E I): the span
-    # schedule's down projection splits every span above 192 rows in two.
-    # Zipf loads 540 / 361 / 234 / 145: three spans (256 and 256 split, 28
-    # whole), two equal spans of 181 / 180 (whole), one split span, one whole;
-    # uniform K = 1 loads 245 / 240 / 266 / 249 (split, split, two equal halves,
-    # split); the Zipf case again with max padding and 64-token blocks
-    (LayerShape("span_split_zipf", 256, 8192, 4, 2, 0, "bf16", (640,), ("zipf",)), 640, "zipf", 128, "block"),
-    (LayerShape("span_split_unif", 256, 8192, 4, 1, 0, "bf16", (1000,), ("uniform",)), 1000, "uniform", 64, "block"),
-    (LayerShape("span_split_max", 256, 8192, 4, 2, 0, "bf16", (640,), ("zipf",)), 640, "zipf", 64, "max"),
+SPAN_HALF_SHAPES = [
+    # (shape, T, routing, block_m, pad): the span schedule's down projection gives an
+    # expert of 193..256 tokens two spans of equal length.  Zipf loads 540 / 361 / 234
+    # / 145: three spans (256, 256, 28), two equal spans of 181 / 180, two halves of
+    # 117, one span; uniform K = 1 loads 245 / 240 / 266 / 249 (halves of 123 / 120,
+    # equal spans of 133, halves of 125); the Zipf case again with max padding and
+    # 64-token blocks
+    (LayerShape("span_half_zipf", 256, 8192, 4, 2, 0, "bf16", (640,), ("zipf",)), 640, "zipf", 128, "block"),
+    (LayerShape("span_half_unif", 256, 8192, 4, 1, 0, "bf16", (1000,), ("uniform",)), 1000, "uniform", 64, "block"),
+    (LayerShape("span_half_max", 256, 8192, 4, 2, 0, "bf16", (640,), ("zipf",)), 640, "zipf", 64, "max"),
 ]
 
 
-@pytest.mark.parametrize("shape,T,routing,block_m,pad", SPAN_SPLIT_SHAPES,
-                         ids=[s[0].name for s in SPAN_SPLIT_SHAPES])
-@pytest.mark.parametrize("sched", ["auto", "span"])
-def test_span_down_split_parity(shape, T, routing, block_m, pad, sched):
-    """The span down projection with its contraction split (fp32 halves of the
-    long spans added by the finish kernel, short spans written directly), under
-    AUTO (tiled gate/up) and forced SPAN; with the minimal workspace the same
-    launch runs unsplit.  All match the oracle; the split pass repeats bit for
+@pytest.mark.parametrize("shape,T,routing,block_m,pad", SPAN_HALF_SHAPES,
+                         ids=[s[0].name for s in SPAN_HALF_SHAPES])
+def test_span_down_halves_parity(shape, T, routing, block_m, pad):
+    """The span schedule forced on experts of 145..540 tokens: the down projection
+    halves those of 193..256 tokens, splits 257..384 into equal spans and cuts
+    longer ones into 256-row spans; the pass matches the oracle and repeats bit for
     bit."""
     d, dev = layer_case(shape, T, routing, seed=17)
-    layer = MoELayer(shape, dev, block_m=block_m,
-                     sched=B.SCHED_SPAN if sched == "span" else B.SCHED_AUTO,
+    layer = MoELayer(shape, dev, block_m=block_m, sched=B.SCHED_SPAN,
                      pad=B.PAD_MAX if pad == "max" else B.PAD_BLOCK)
-    K, H = shape.topk, shape.hidden
-    ws_min = B.moe_ffn_workspace_bytes(layer.plan.cap, shape.inter)
-    assert layer.workspace.numel() >= ws_min + 2 * T * K * H * 4   # the split is planned
+    K = shape.topk
     out = layer.forward().clone()
     out_rep = layer.forward().clone()
     torch.cuda.synchronize()
     ref, rids, _ = oracle.moe_layer(d["x"], d["logits"], d["w13"], d["w2"], K)
     assert (layer.topk_ids.cpu().numpy() == rids).all()
     counts = np.bincount(rids.reshape(-1), minlength=shape.experts)
-    assert (counts > 192).any()   # some span is split
+    assert ((counts > 192) & (counts <= 256)).any()   # some expert is halved
     assert rel_err(out, ref) <= TOL
     assert torch.equal(out, out_rep)
-    layer.workspace = torch.empty(ws_min, dtype=torch.uint8, device=DEV)
-    out_min = layer.forward().clone()
-    torch.cuda.synchronize()
-    assert rel_err(out_min, ref) <= TOL
 
 
 RING_SHAPES = [
