@@ -317,6 +317,9 @@ moe_status moe_combine(const void *y_pairs, moe_dtype ydt, const float *topk_w, 
  * workspace >= dense_ffn_workspace_bytes(T, H, I_fa); out [T][H] odt.
  * Deterministic: when the contraction is split across workgroups the partial
  * sums are added in a fixed order by a second kernel, never with atomics.
+ * MOE_SCHED_AUTO streams up to 32 tokens and tiles above; its gate/up half
+ * takes the span schedule (bf16, span shape conditions) where that gives
+ * (I_fa/128) * ceil(T/256) >= 768 work items.
  */
 moe_status dense_ffn_fa(const void *x, moe_dtype dt, int64_t T, int H, int I_fa, const void *w13,
                         const void *w2, void *workspace, int64_t workspace_bytes, void *out,

@@ -584,6 +584,25 @@ def test_dense_ffn_span_parity(T, H, I, odt):
     assert rel_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_dense_ffn_auto_span_gate_up_parity(odt):
+    """AUTO on dense rows with (I/128) x ceil(T/256) >= 768 gate/up items: the gate/up
+    half on the span schedule (spans of 256 rows, the last of 232), the down half on
+    256-token tiles (the last ragged) reading its activation rows."""
+    T, H, I = 1000, 256, 24576
+    x = synth.tokens(T, H, "bf16", seed=3)
+    w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=4)
+    ref = oracle.swiglu(x, w13, w2)
+    ws = torch.empty(B.dense_ffn_workspace_bytes(T, H, I), dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, H, dtype=odt, device=DEV)
+    B.dense_ffn_fa(x.to(DEV), w13.to(DEV), w2.to(DEV), ws, out)
+    out2 = torch.empty_like(out)
+    B.dense_ffn_fa(x.to(DEV), w13.to(DEV), w2.to(DEV), ws, out2, sched=B.SCHED_TILE)
+    torch.cuda.synchronize()
+    assert rel_err(out, ref) <= TOL
+    assert rel_err(out2, ref) <= TOL
+
+
 def test_span_schedule_rejects_unsupported_shape():
     # H % 256 != 0
     shape = LayerShape("span_bad", 384, 256, 8, 2, 0, "bf16", (300,), ("uniform",))
