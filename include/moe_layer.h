@@ -319,7 +319,7 @@ moe_status moe_combine(const void *y_pairs, moe_dtype ydt, const float *topk_w, 
  * sums are added in a fixed order by a second kernel, never with atomics.
  * MOE_SCHED_AUTO streams up to 32 tokens and tiles above; its gate/up half
  * takes the span schedule (bf16, span shape conditions) where that gives
- * (I_fa/128) * ceil(T/256) >= 768 work items.
+ * (I_fa/128) * ceil(T/256) >= 384 work items.
  */
 moe_status dense_ffn_fa(const void *x, moe_dtype dt, int64_t T, int H, int I_fa, const void *w13,
                         const void *w2, void *workspace, int64_t workspace_bytes, void *out,

@@ -775,14 +775,15 @@ moe_status dense_ffn_fa(const void* x, moe_dtype dt, int64_t T, int H, int I_fa,
     rm.block_m = dp.tile_block;
     const int64_t nblocks = (T + rm.block_m - 1) / rm.block_m;
     // AUTO: the gate/up half on the span schedule where its (I/128) x ceil(T/256)
-    // items fill the CUs three times over, the down half tiled (its H/256 tiles a
+    // items fill the CUs 1.5 times over, the down half tiled (its H/256 tiles a
     // span are too few items).  Measured on MI355X (us, tiled -> span gate/up):
-    // DenseFA Mixtral-shaped at T=1024 778-788 -> 721-726, T=2048 1359-1369 ->
-    // 1248-1254, T=4096 2635-2645 -> 2472-2480; Qwen2's shared experts at T=2048
-    // 915-934 -> 841-846.  The span writes act rows 0..T-1; the tiles' rows past
-    // T feed only outputs that are never stored.
+    // DenseFA Mixtral-shaped at T=512 (448 items) 417-418 -> 380-385, T=1024
+    // 778-788 -> 721-726, T=2048 1359-1369 -> 1248-1254, T=4096 2635-2645 ->
+    // 2472-2480; Qwen2's shared experts at T=2048 915-934 -> 841-846.  The span
+    // writes act rows 0..T-1; the tiles' rows past T feed only outputs that are
+    // never stored.
     const bool span_gu = sched == MOE_SCHED_AUTO && span_shape_ok(dt, 1, H, I_fa, T, T) &&
-                         (int64_t)(I_fa / 128) * ((T + 255) / 256) >= 768;
+                         (int64_t)(I_fa / 128) * ((T + 255) / 256) >= 384;
     hipError_t e = span_gu ? moe::launch_span_gate_up(x, w13, rm, 1, H, I_fa, T, T, act, s)
                  : dp.tile_full_gu > 0
                        ? moe::launch_tile_gate_up(x, dt, w13, rm, nblocks, H, I_fa, act, s,

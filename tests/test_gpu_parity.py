@@ -586,7 +586,7 @@ def test_dense_ffn_span_parity(T, H, I, odt):
 
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
 def test_dense_ffn_auto_span_gate_up_parity(odt):
-    """AUTO on dense rows with (I/128) x ceil(T/256) >= 768 gate/up items: the gate/up
+    """AUTO on dense rows with (I/128) x ceil(T/256) >= 384 gate/up items: the gate/up
     half on the span schedule (spans of 256 rows, the last of 232), the down half on
     256-token tiles (the last ragged) reading its activation rows."""
     T, H, I = 1000, 256, 24576
