@@ -584,12 +584,13 @@ def test_dense_ffn_span_parity(T, H, I, odt):
     assert rel_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("T", [500, 1000])
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
-def test_dense_ffn_auto_span_gate_up_parity(odt):
-    """AUTO on dense rows with (I/128) x ceil(T/256) >= 384 gate/up items: the gate/up
-    half on the span schedule (spans of 256 rows, the last of 232), the down half on
-    256-token tiles (the last ragged) reading its activation rows."""
-    T, H, I = 1000, 256, 24576
+def test_dense_ffn_auto_span_gate_up_parity(T, odt):
+    """AUTO on dense rows with (I/128) x ceil(T/256) >= 384 gate/up items (384 and 768):
+    the gate/up half on the span schedule (spans of 256 rows, the last of 244 or 232),
+    the down half on 256-token tiles (the last ragged) reading its activation rows."""
+    H, I = 256, 24576
     x = synth.tokens(T, H, "bf16", seed=3)
     w13, w2 = synth.swiglu_weights(I, H, "bf16", seed=4)
     ref = oracle.swiglu(x, w13, w2)
