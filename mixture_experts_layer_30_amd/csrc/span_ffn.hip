@@ -401,10 +401,12 @@ unsigned span_grid(int64_t items) {
   return (unsigned)(g < span_workgroups() ? (g < 8 ? 8 : g) : span_workgroups());
 }
 
-// items of a launch: tiles x the spans of the rows (at most rows/256 + one per expert)
-int64_t span_items(const RowMap& rm, int E, int64_t rows_bound, int ntiles) {
-  const int64_t spans = rm.counts == nullptr ? (rm.dense_rows + kPTok - 1) / kPTok
-                                             : rows_bound / kPTok + E;
+// items of a launch: tiles x the spans of the rows, at most rows/256 + one per
+// expert (gate/up) or rows/192 + one per expert (down, whose experts of 193..256
+// rows take two spans)
+int64_t span_items(const RowMap& rm, int E, int64_t rows_bound, int ntiles, bool gate_up) {
+  const int64_t per = gate_up ? kPTok : 3 * kPTok / 4;
+  const int64_t spans = rm.counts == nullptr ? rm.dense_rows / per + 1 : rows_bound / per + E;
   return spans * ntiles;
 }
 
@@ -421,7 +423,7 @@ hipError_t launch_span_gate_up(const void* x, const void* w13, const RowMap& rm,
                                hipStream_t s) {
   if (!span_ok(rm.counts == nullptr ? 1 : E, H, I, x_rows, rows_bound)) return hipErrorInvalidValue;
   const int ntiles = I / (kPRows / 2);
-  const int64_t items = span_items(rm, E, rows_bound, ntiles);
+  const int64_t items = span_items(rm, E, rows_bound, ntiles, true);
   if (items <= 0) return hipSuccess;
   hipLaunchKernelGGL((span_ffn_kernel<BF16, true>), dim3(span_grid(items)), dim3(kPThreads), 0, s,
                      static_cast<const uint16_t*>(w13), static_cast<const uint16_t*>(x), rm, E, H,
@@ -434,7 +436,7 @@ hipError_t launch_span_down(const void* w2, const uint16_t* act, const RowMap& r
                             hipStream_t s) {
   if (!span_ok(rm.counts == nullptr ? 1 : E, H, I, 0, act_rows)) return hipErrorInvalidValue;
   const int ntiles = H / kPRows;
-  const int64_t items = span_items(rm, E, rows_bound, ntiles);
+  const int64_t items = span_items(rm, E, rows_bound, ntiles, false);
   if (items <= 0) return hipSuccess;
   if (ydt == kDtF32)
     hipLaunchKernelGGL((span_ffn_kernel<F32, false>), dim3(span_grid(items)), dim3(kPThreads), 0,
